@@ -1,0 +1,232 @@
+/*
+ * pa.h -- C ABI of libpa: paged GQA attention at head_dim 512 for MI355X (gfx950).
+ *
+ * Operations (each cites the page that defines it):
+ *
+ *  - Paged decode: one query token per request attends the request's KV, read through a
+ *    page table from the combined HND cache [num_pages, 2, num_kv_heads, page_size,
+ *    head_dim] ("[None][feat] Run Gemma4 head_dim 512 attention on Triton", TensorRT-LLM
+ *    pull request 17772, section "Approach"), split along the key axis and merged by
+ *    log-sum-exp (same page, section "Not covered": split-K workspaces), with sliding
+ *    windows and FP8 KV cast on load (same page, sections "Approach" and "Test Coverage").
+ *  - Paged prefill: causal attention of the new tokens over the cached prefix and
+ *    themselves (same page, section "Approach"; section "Not covered" for the current
+ *    tokens versus the prefix), including head_dim_qk = 512 with head_dim_vo = 256 over
+ *    separately allocated K and V pools ("feat(attention): asymmetric VO-split NVFP4 paged
+ *    prefill (qk=512/vo=256) for Gemma-4 on SM120/121", FlashInfer pull request 3684,
+ *    sections "Summary" and "What's in it").
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless the parameter name ends in _host.  The library
+ *    never allocates memory and never frees what it is given; every pointer is borrowed
+ *    for the duration of the call (for enqueuing calls: until the stream reaches the
+ *    enqueued work).
+ *  - Every call returns a pa_status.  On an error nothing is enqueued and no output is
+ *    written; pa_last_error() then returns a message naming the argument at fault
+ *    (thread-local, valid until the next failing call on the same thread).  An input the
+ *    library does not implement is refused with an error instead of being computed
+ *    wrongly (the rule both pages follow: the Triton page's section "Not covered", and the
+ *    FlashInfer page's commit on unequal K/V strides).
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.  Enqueuing
+ *    calls do not synchronise.
+ *  - Element strides are in elements of the stored type; the innermost (head_dim) stride
+ *    is 1.  Base pointers and strides must keep every 16-byte vector load aligned.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,          /* malformed metadata, mismatched sizes, null pointers */
+  PA_ERR_UNSUPPORTED = 2,          /* a valid request this library does not implement   */
+  PA_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace or plan buffer below the planned size     */
+  PA_ERR_HIP = 4                   /* a HIP runtime call failed                           */
+} pa_status;
+
+typedef enum {
+  PA_DTYPE_BF16 = 0,
+  PA_DTYPE_FP32 = 1,
+  PA_DTYPE_FP8_E4M3FN = 2          /* OCP E4M3FN: bias 7, max 448, NaN only at S.1111.111 */
+} pa_dtype;
+
+/* One paged KV cache.  K and V may be two halves of the combined HND cache or two
+ * separate pools with their own strides and widths (the FlashInfer page's commit that
+ * tests the asymmetric prefill over separately allocated K and V pools whose strides
+ * differ).  Element (page, head, slot, d) of K is at
+ *   k + page*k_stride_page + head*k_stride_head + slot*k_stride_token + d
+ * and likewise for V.  For FP8 the stored code c stands for e4m3fn(c) * k_scale (or
+ * v_scale); bf16 caches use scales of 1. */
+typedef struct pa_kv_cache {
+  const void* k;
+  const void* v;
+  int32_t kv_dtype;                /* PA_DTYPE_BF16 or PA_DTYPE_FP8_E4M3FN */
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t page_size;               /* tokens per page, >= 1 */
+  int32_t head_dim_qk;
+  int32_t head_dim_vo;
+  int64_t k_stride_page, k_stride_head, k_stride_token;
+  int64_t v_stride_page, v_stride_head, v_stride_token;
+  float k_scale;
+  float v_scale;
+} pa_kv_cache;
+
+/* Page table, as the FlashInfer decode plan slices it (Triton page, section "Approach"):
+ * request b owns pages kv_indices[kv_indptr[b] .. kv_indptr[b+1]) in logical order; all
+ * are full except the last, which holds kv_last_page_len[b] tokens (1..page_size; an
+ * exact multiple of the page size has a last page length of page_size).  Logical token t
+ * of request b is slot t % page_size of page kv_indices[kv_indptr[b] + t / page_size].
+ * All three arrays are device int32. */
+typedef struct pa_page_table {
+  const int32_t* kv_indptr;        /* [batch + 1], kv_indptr[0] == 0, non-decreasing */
+  const int32_t* kv_indices;       /* [kv_indptr[batch]], each in [0, num_pages)      */
+  const int32_t* kv_last_page_len; /* [batch]                                         */
+  int32_t batch;
+} pa_page_table;
+
+typedef struct pa_attn_params {
+  int32_t num_qo_heads;            /* multiple of num_kv_heads; query head h reads KV head
+                                      h / (num_qo_heads / num_kv_heads)                  */
+  float sm_scale;                  /* scores are sm_scale * q.k (e.g. 1/sqrt(head_dim_qk)) */
+  int32_t window;                  /* > 0: a query at position p sees keys t > p - window;
+                                      <= 0: no window                                      */
+  int32_t causal;                  /* prefill: nonzero = causal; decode ignores it (the one
+                                      query is the last position, so it is causal anyway) */
+  int32_t q_dtype;                 /* PA_DTYPE_BF16 */
+  int32_t out_dtype;               /* PA_DTYPE_FP32 or PA_DTYPE_BF16 (round to nearest even) */
+} pa_attn_params;
+
+/* Host-side plan: the partition of the work into items.  Plain data, owned by the
+ * caller; filled by pa_decode_plan / pa_prefill_plan and read by the run calls, which
+ * check that the sizes in it match their own arguments. */
+typedef struct pa_plan {
+  int32_t kind;                    /* 1 = decode, 2 = prefill                          */
+  int32_t batch;
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t head_dim_qk;
+  int32_t head_dim_vo;
+  int32_t kv_dtype;
+  int32_t window;
+  int32_t causal;
+  int32_t num_items;               /* work items; one workgroup per (item, kv head)     */
+  int32_t num_slots;               /* decode: partial-result slots in the workspace     */
+  int32_t num_merges;              /* decode: requests whose partials are merged        */
+  int32_t block_tokens;            /* decode: key block of the partition (16)           */
+  int32_t chunk_blocks;            /* decode: adaptive chunk length in blocks, or 0     */
+  int32_t num_splits;              /* decode: requested splits (0 = adaptive)           */
+  int32_t tile_rows;               /* prefill: query rows (token, head) per tile        */
+  int32_t total_q;                 /* prefill: number of query tokens                   */
+  int32_t max_kv_len;
+  int32_t reserved0;
+  int64_t plan_bytes;              /* bytes of the host plan buffer in use              */
+  int64_t items_offset;            /* byte offset of the item array in the plan buffer  */
+  int64_t merges_offset;           /* byte offset of the merge array in the plan buffer */
+  int64_t partial_o_offset;        /* byte offset of partial outputs in the workspace   */
+  int64_t partial_lse_offset;      /* byte offset of partial lse in the workspace       */
+  int64_t workspace_bytes;         /* device workspace the run call needs               */
+} pa_plan;
+
+/* Fills *out for the combined HND cache [num_pages, 2, num_kv_heads, page_size, head_dim]
+ * at `base` (K = index 0 of the "2" axis, V = index 1), contiguous, both widths equal to
+ * head_dim.  Pure host arithmetic; `base` is not dereferenced. */
+pa_status pa_kv_cache_hnd(const void* base, int32_t kv_dtype, int32_t num_pages,
+                          int32_t num_kv_heads, int32_t page_size, int32_t head_dim,
+                          float k_scale, float v_scale, pa_kv_cache* out);
+
+/* Fills *out for two contiguous pools K [num_pages, num_kv_heads, page_size, head_dim_qk]
+ * and V [num_pages, num_kv_heads, page_size, head_dim_vo] sharing one page table. */
+pa_status pa_kv_cache_separate(const void* k, const void* v, int32_t kv_dtype,
+                               int32_t num_pages, int32_t num_kv_heads, int32_t page_size,
+                               int32_t head_dim_qk, int32_t head_dim_vo, float k_scale,
+                               float v_scale, pa_kv_cache* out);
+
+/* Checks host copies of a page table: kv_indptr[0] == 0 and non-decreasing, every index
+ * in [0, num_pages), every last page length in [1, page_size] for a non-empty request.
+ * kv_indices_host may be NULL to skip the index range check.  Never calls HIP. */
+pa_status pa_validate_page_table_host(const int32_t* kv_indptr_host,
+                                      const int32_t* kv_indices_host,
+                                      const int32_t* kv_last_page_len_host, int32_t batch,
+                                      int32_t num_pages, int32_t page_size);
+
+/* Plans a decode batch from host copies of kv_indptr and kv_last_page_len (the device
+ * copies passed to pa_paged_decode must hold the same values).  num_splits > 0 cuts each
+ * request's visible keys into min(num_splits, blocks) near-equal chunks of 16-token
+ * blocks; num_splits == 0 picks the chunk length so that the batch makes about 2048
+ * workgroups (at least 8 blocks per chunk, at most 64 chunks per request).  Items run
+ * longest first.  Call with plan_buf_host == NULL to learn plan->plan_bytes (and
+ * plan->workspace_bytes); then call again with a buffer of at least that size.
+ * Supported: head dims (512,512), (256,256), (512,256); kv bf16 or FP8 E4M3FN;
+ * q bf16; out fp32 or bf16; 1 <= num_qo_heads / num_kv_heads <= 8; num_splits <= 64.
+ * Never calls HIP. */
+pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
+                         const int32_t* kv_indptr_host, const int32_t* kv_last_page_len_host,
+                         int32_t batch, int32_t num_splits, void* plan_buf_host,
+                         size_t plan_buf_bytes, pa_plan* plan);
+
+/* Plans a prefill batch.  qo_indptr_host [batch + 1] gives each request's new tokens,
+ * which must not outnumber its KV tokens; row i of request b sits at key position
+ * L_b - q_len_b + i.  Query rows of one (request, KV head) are the (token, head) pairs of
+ * its head group, tiled in plan->tile_rows; tiles run longest first.  Same two-call
+ * sizing as pa_decode_plan.  Supported: head dims (512,512), (256,256), (512,256); kv
+ * bf16; q bf16; out fp32 or bf16; num_qo_heads / num_kv_heads <= 16.  Never calls HIP. */
+pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache,
+                          const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+                          const int32_t* kv_last_page_len_host, int32_t batch,
+                          void* plan_buf_host, size_t plan_buf_bytes, pa_plan* plan);
+
+/* Copies plan->plan_bytes from plan_buf_host to the start of the device workspace
+ * (stream-ordered hipMemcpyAsync).  The host buffer must stay unchanged until the copy
+ * has run.  The run calls read the work items from there, so upload once per plan. */
+pa_status pa_plan_upload(const pa_plan* plan, const void* plan_buf_host, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Enqueues one decode step: q [batch, num_qo_heads, head_dim_qk] bf16 (contiguous) ->
+ * out [batch, num_qo_heads, head_dim_vo] in params->out_dtype, and, if lse != NULL,
+ * lse [batch, num_qo_heads] fp32 (natural log; -inf for a request with no keys, whose
+ * output row is zero).  workspace: device buffer of at least plan->workspace_bytes
+ * holding the uploaded plan; it also receives the split partials.  Launches the
+ * split-K partial kernel and, when a request was split, the log-sum-exp merge kernel.
+ * Concurrent calls sharing one workspace race. */
+pa_status pa_paged_decode(const pa_plan* plan, const void* q, const pa_kv_cache* cache,
+                          const pa_page_table* table, const pa_attn_params* params,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Enqueues one prefill: q [total_q, num_qo_heads, head_dim_qk] bf16 (contiguous, ragged
+ * by qo_indptr) -> out [total_q, num_qo_heads, head_dim_vo] in params->out_dtype and
+ * optional lse [total_q, num_qo_heads] fp32.  qo_indptr is the device copy of the array
+ * given to pa_prefill_plan. */
+pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const int32_t* qo_indptr,
+                           const pa_kv_cache* cache, const pa_page_table* table,
+                           const pa_attn_params* params, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Copies the stored K and V elements of (request, kv_head) in logical token order, through
+ * the same address path as the attention kernels: k_out [kv_len, head_dim_qk] and
+ * v_out [kv_len, head_dim_vo] in the cache's element type.  kv_len must equal the
+ * request's length.  For bit-exact checks of the page-table handling. */
+pa_status pa_debug_gather_kv(const pa_kv_cache* cache, const pa_page_table* table,
+                             int32_t request, int32_t kv_len, int32_t kv_head, void* k_out,
+                             void* v_out, void* stream);
+
+/* Converts n FP8 E4M3FN codes to fp32 with the same conversion the kernels use. */
+pa_status pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int32_t n, void* stream);
+
+const char* pa_last_error(void);   /* thread-local message of the last failing call */
+uint64_t pa_launch_count(void);    /* kernels launched by this process so far         */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

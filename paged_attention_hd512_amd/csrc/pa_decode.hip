@@ -1,0 +1,605 @@
+// Paged decode for gfx950: split-K partial kernel, log-sum-exp merge kernel, and the
+// C entry points that plan-check and enqueue them.
+//
+// What is computed ("[None][feat] Run Gemma4 head_dim 512 attention on Triton",
+// TensorRT-LLM pull request 17772, sections "Approach" and "Not covered"): for every
+// request b and query head h, softmax(sm_scale * q . K^T) V over the request's visible
+// keys, read through the page table from the combined HND cache, with the key axis cut
+// into chunks whose partial results are merged by log-sum-exp weights (flash-decoding).
+//
+// Work decomposition.  The host planner cuts every request's visible keys into chunks of
+// 16-token blocks; one workgroup (4 waves) runs one (chunk, KV head).  The G query heads
+// that share the KV head are computed together, so each K/V byte is read from HBM once
+// for the whole group:
+//   * S = K Q^T for a 16-key block is one 16x16 tile of v_mfma_f32_16x16x32_bf16 (keys
+//     on M, the G heads padded to 16 on N, head_dim on K).  Each lane loads its K operand
+//     straight from the page as 16-byte vectors (4 lanes cover 64 contiguous bytes of a key
+//     row); Q sits in LDS with the same head_dim order.
+//   * The online softmax keeps a running max and sum per head; the block max is a
+//     cross-lane reduction over the 4 lanes that share a head.
+//   * P V runs on the vector ALU: each V load instruction covers whole key rows (lane l
+//     holds 8 consecutive head_dim elements of one row), each lane keeps G x 8 fp32
+//     accumulators, and the block's probabilities come from LDS as broadcast reads.
+//   * The 4 waves take interleaved blocks and merge their states through LDS in a fixed
+//     order at the end, so results are deterministic.
+// FP8 E4M3FN keys are widened to bf16 in registers (exact); k_scale is folded into the
+// score scale and v_scale into the output.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "pa_device.hpp"
+#include "pa_internal.hpp"
+
+namespace pa {
+
+constexpr int kDecodeWaves = 4;
+
+struct DecodeArgs {
+  const uint16_t* q;           // [B, Hq, DQK] bf16 bits
+  const char* k;               // byte base of the K pool
+  const char* v;               // byte base of the V pool
+  int64_t k_sp, k_sh, k_st;    // element strides
+  int64_t v_sp, v_sh, v_st;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const DecodeItem* items;
+  void* out;                   // [B, Hq, DVO] fp32 or bf16
+  float* lse;                  // [B, Hq] or null
+  float* part_o;               // [slots, Hq, DVO] fp32
+  float* part_lse;             // [slots, Hq], log2 domain
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t page_size;
+  int32_t out_fp32;
+  float scale_log2;            // sm_scale * k_scale * log2(e)
+  float v_scale;
+};
+
+// head_dim offset of the 8 bf16 operand elements that lane group g4 holds at MFMA step j.
+// bf16 keys: one 16-byte load per step.  FP8 keys: one 16-byte load covers two steps.
+template <int KVB>
+__device__ __forceinline__ int q_dim_of_step(int j, int g4) {
+  if constexpr (KVB == 2) return 32 * j + 8 * g4;
+  else return 64 * (j >> 1) + 16 * g4 + 8 * (j & 1);
+}
+
+template <int DQK, int DVO, int KVB, int GMAX>
+__global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
+  constexpr int NW = kDecodeWaves;
+  constexpr int NSTEP = DQK / 32;                 // MFMA steps over head_dim
+  constexpr int NKL = 16 * DQK * KVB / (64 * 16); // 16-byte K loads per lane per block
+  constexpr int LPR = DVO / 8;                    // lanes per V row (8 elements per lane)
+  constexpr int RPI = 64 / LPR;                   // V rows per load instruction (1 or 2)
+  constexpr int NVL = 16 / RPI;                   // V load instructions per block
+  constexpr int QPITCH = DQK + 8;                 // LDS row pitch of Q (bf16), padded
+  using vload_t = typename std::conditional<KVB == 2, u32x4_t, u32x2_t>::type;
+
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[16 * QPITCH];
+  __shared__ __attribute__((aligned(16))) float p_lds[NW][16][16];
+  __shared__ __attribute__((aligned(16))) float alpha_lds[NW][16];
+  __shared__ __attribute__((aligned(16))) float ml_lds[2][NW][16];
+  __shared__ __attribute__((aligned(16))) float merge_lds[2][GMAX][DVO];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g4 = lane >> 4;
+  const int n = lane & 15;
+  const int hkv = a.num_kv_heads;
+  const int kvh = blockIdx.x % hkv;
+  const DecodeItem it = a.items[blockIdx.x / hkv];
+  const int G = a.group;
+  const int t0 = it.t_begin, t1 = it.t_end;
+  const int32_t* __restrict__ pages = a.kv_indices + a.kv_indptr[it.b];
+
+  // Q of the head group -> LDS rows 0..G-1; rows G..15 are zero.
+  {
+    const uint16_t* qsrc = a.q + ((int64_t)it.b * a.num_qo_heads + (int64_t)kvh * G) * DQK;
+    for (int idx = tid; idx < 16 * (DQK / 8); idx += 256) {
+      const int row = idx / (DQK / 8), c8 = idx % (DQK / 8);
+      u32x4_t val = {0u, 0u, 0u, 0u};
+      if (row < G) val = *(const u32x4_t*)(qsrc + row * DQK + c8 * 8);
+      *(u32x4_t*)(q_lds + row * QPITCH + c8 * 8) = val;
+    }
+  }
+  __syncthreads();
+
+  float m_run = -INFINITY;  // per head n, log2 domain
+  float l_run = 0.f;        // this lane's share of the sum for head n
+  float acc[GMAX][8];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+  const int blk_first = t0 / 16;
+  const int blk_end = (t1 + 15) / 16;
+  const int64_t k_head = (int64_t)kvh * a.k_sh;
+  const int64_t v_head = (int64_t)kvh * a.v_sh;
+
+  u32x4_t kbuf[NKL];
+  vload_t vbuf[NVL];
+
+  // Page and slot of key n of a block (clamped into the chunk, so that every load is of a
+  // key this chunk owns; clamped lanes are masked out of the softmax).
+  auto block_page = [&](int blk, int32_t& page, int32_t& slot) {
+    int t = blk * 16 + n;
+    t = t < t0 ? t0 : (t >= t1 ? t1 - 1 : t);
+    token_page_slot(pages, t, a.page_size, page, slot);
+  };
+  auto issue_k = [&](int32_t page, int32_t slot) {
+    const char* base = a.k + (row_elem_offset(page, 0, slot, a.k_sp, 0, a.k_st) + k_head) * KVB + 16 * g4;
+#pragma unroll
+    for (int l = 0; l < NKL; ++l) kbuf[l] = *(const u32x4_t*)(base + 64 * l);
+  };
+  auto issue_v = [&](int32_t page, int32_t slot) {
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int src = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
+      int32_t pv, sv;
+      if constexpr (RPI == 1) {
+        pv = __builtin_amdgcn_readlane(page, src);
+        sv = __builtin_amdgcn_readlane(slot, src);
+      } else {
+        pv = shfl_i(page, src);
+        sv = shfl_i(slot, src);
+      }
+      const char* base = a.v + (row_elem_offset(pv, 0, sv, a.v_sp, 0, a.v_st) + v_head) * KVB +
+                         (lane % LPR) * 8 * KVB;
+      vbuf[i] = *(const vload_t*)base;
+    }
+  };
+
+  int blk = blk_first + w;
+  int32_t page_c = 0, slot_c = 0, page_n = 0, slot_n = 0;
+  if (blk < blk_end) {
+    block_page(blk, page_c, slot_c);
+    issue_k(page_c, slot_c);
+    if (blk + NW < blk_end) block_page(blk + NW, page_n, slot_n);
+    issue_v(page_c, slot_c);
+  }
+
+  for (; blk < blk_end; blk += NW) {
+    const bool has_next = blk + NW < blk_end;
+    // ---- S^T = K Q^T for the 16 keys of this block (keys on rows, heads on columns).
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NSTEP; ++j) {
+      bf16x8_t kf;
+      if constexpr (KVB == 2) {
+        kf = __builtin_bit_cast(bf16x8_t, kbuf[j]);
+      } else {
+        const u32x4_t raw = kbuf[j >> 1];
+        const u32x2_t lo = fp8x4_to_bf16x4(raw[(j & 1) * 2 + 0]);
+        const u32x2_t hi = fp8x4_to_bf16x4(raw[(j & 1) * 2 + 1]);
+        const u32x4_t packed = {lo[0], lo[1], hi[0], hi[1]};
+        kf = __builtin_bit_cast(bf16x8_t, packed);
+      }
+      const u32x4_t qv = *(const u32x4_t*)(q_lds + n * QPITCH + q_dim_of_step<KVB>(j, g4));
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, __builtin_bit_cast(bf16x8_t, qv), s, 0, 0, 0);
+    }
+    // ---- prefetch: next block's keys (its page index was loaded one iteration ago) and
+    // the page index of the block after it.
+    if (has_next) issue_k(page_n, slot_n);
+    int32_t page_nn = 0, slot_nn = 0;
+    if (blk + 2 * NW < blk_end) block_page(blk + 2 * NW, page_nn, slot_nn);
+
+    // ---- online softmax over the block; lane (g4, n) holds keys 4*g4 + i of head n.
+    float sc[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = blk * 16 + 4 * g4 + i;
+      sc[i] = (t >= t0 && t < t1) ? s[i] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sc[i]);
+    }
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = exp2f(sc[i] - m_use);
+      psum += p;
+      p_lds[w][4 * g4 + i][n] = p;
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (g4 == 0) alpha_lds[w][n] = alpha;
+    wave_lds_sync();
+
+    // ---- rescale the accumulators, then O += P V.
+    {
+      float al[GMAX];
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) al[h] = alpha_lds[w][h];
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+    }
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int tk = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
+      float p[GMAX];
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) p[h] = p_lds[w][tk][h];
+      float vf[8];
+      if constexpr (KVB == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf[2 * e] = bf16_lo(vbuf[i][e]);
+          vf[2 * e + 1] = bf16_hi(vbuf[i][e]);
+        }
+      } else {
+        fp8x4_to_f32(vbuf[i][0], vf);
+        fp8x4_to_f32(vbuf[i][1], vf + 4);
+      }
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        if (GMAX == 1 || h < G) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p[h], vf[e], acc[h][e]);
+        }
+      }
+    }
+    wave_lds_sync();  // p_lds / alpha_lds are rewritten next iteration
+    if (has_next) issue_v(page_n, slot_n);
+    page_n = page_nn;
+    slot_n = slot_nn;
+  }
+
+  // ---- per-wave totals: the sum over the 4 lanes of a head, and (two rows per V load)
+  // the accumulator halves.
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+  if constexpr (RPI == 2) {
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += shfl_xor_f(acc[h][e], 32);
+  }
+  if (g4 == 0) {
+    ml_lds[0][w][n] = m_run;
+    ml_lds[1][w][n] = l_run;
+  }
+  __syncthreads();
+
+  // ---- merge the 4 waves: common max per head, rescale, then a fixed-order tree sum.
+  float mtot[GMAX], ltot[GMAX];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    float mm = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) mm = fmaxf(mm, ml_lds[0][x][h]);
+    const float mu = mm == -INFINITY ? 0.f : mm;
+    float ll = 0.f;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) ll += ml_lds[1][x][h] * exp2f(ml_lds[0][x][h] - mu);
+    const float f = exp2f(ml_lds[0][w][h] - mu);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] *= f;
+    mtot[h] = mm;
+    ltot[h] = ll;
+  }
+  const bool writer = lane < LPR;
+  auto publish = [&](int slot) {
+    if (writer) {
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        *(f32x4_t*)&merge_lds[slot][h][lane * 8] = f32x4_t{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+        *(f32x4_t*)&merge_lds[slot][h][lane * 8 + 4] = f32x4_t{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+      }
+    }
+  };
+  auto absorb = [&](int slot) {
+    if (writer) {
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        const f32x4_t x0 = *(const f32x4_t*)&merge_lds[slot][h][lane * 8];
+        const f32x4_t x1 = *(const f32x4_t*)&merge_lds[slot][h][lane * 8 + 4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[h][e] += x0[e];
+          acc[h][e + 4] += x1[e];
+        }
+      }
+    }
+  };
+  if (w >= 2) publish(w - 2);
+  __syncthreads();
+  if (w < 2) absorb(w);
+  __syncthreads();
+  if (w == 1) publish(0);
+  __syncthreads();
+  if (w != 0) return;
+  absorb(0);
+
+  // ---- wave 0 writes the chunk result: final output, or a partial for the merge.
+  const int h0 = kvh * G;
+  if (it.slot < 0) {
+    if (writer) {
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        if (h >= G) continue;
+        const float inv = ltot[h] > 0.f ? a.v_scale / ltot[h] : 0.f;
+        const int64_t off = ((int64_t)it.b * a.num_qo_heads + h0 + h) * DVO + lane * 8;
+        if (a.out_fp32) {
+          float* o = (float*)a.out + off;
+          *(f32x4_t*)o = f32x4_t{acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv};
+          *(f32x4_t*)(o + 4) = f32x4_t{acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv};
+        } else {
+          u32x4_t pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[e] = pack_bf16(acc[h][2 * e] * inv, acc[h][2 * e + 1] * inv);
+          *(u32x4_t*)((uint16_t*)a.out + off) = pk;
+        }
+      }
+    }
+    if (a.lse && lane < G) {
+      float lv = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h)
+        if (h == lane && ltot[h] > 0.f) lv = (mtot[h] + log2f(ltot[h])) * kLn2;
+      a.lse[(int64_t)it.b * a.num_qo_heads + h0 + lane] = lv;
+    }
+  } else {
+    if (writer) {
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        if (h >= G) continue;
+        const float inv = ltot[h] > 0.f ? a.v_scale / ltot[h] : 0.f;
+        float* o = a.part_o + ((int64_t)it.slot * a.num_qo_heads + h0 + h) * DVO + lane * 8;
+        *(f32x4_t*)o = f32x4_t{acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv};
+        *(f32x4_t*)(o + 4) = f32x4_t{acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv};
+      }
+    }
+    if (lane < G) {
+      float lv = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h)
+        if (h == lane && ltot[h] > 0.f) lv = mtot[h] + log2f(ltot[h]);
+      a.part_lse[(int64_t)it.slot * a.num_qo_heads + h0 + lane] = lv;
+    }
+  }
+}
+
+struct MergeArgs {
+  const MergeItem* merges;
+  const float* part_o;
+  const float* part_lse;   // log2 domain
+  void* out;
+  float* lse;
+  int32_t num_qo_heads;
+  int32_t out_fp32;
+};
+
+// One wave per (split request, query head): log-sum-exp weights over the chunks, in chunk
+// order, then the weighted sum of the chunk outputs.
+template <int DVO>
+__global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a) {
+  constexpr int EPT = DVO / 64;
+  const MergeItem mi = a.merges[blockIdx.x];
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int hq = a.num_qo_heads;
+  float mx = -INFINITY;
+  for (int c = 0; c < mi.num_chunks; ++c)
+    mx = fmaxf(mx, a.part_lse[(int64_t)(mi.slot_begin + c) * hq + h]);
+  const float mu = mx == -INFINITY ? 0.f : mx;
+  float o[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) o[e] = 0.f;
+  float wsum = 0.f;
+  for (int c = 0; c < mi.num_chunks; ++c) {
+    const int64_t row = (int64_t)(mi.slot_begin + c) * hq + h;
+    const float lc = a.part_lse[row];
+    if (lc == -INFINITY) continue;
+    const float wgt = exp2f(lc - mu);
+    wsum += wgt;
+    const float* src = a.part_o + row * DVO + lane * EPT;
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4) {
+      const f32x4_t x = *(const f32x4_t*)(src + e);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[e + u] = fmaf(wgt, x[u], o[e + u]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t off = ((int64_t)mi.b * hq + h) * DVO + lane * EPT;
+  if (a.out_fp32) {
+    float* dst = (float*)a.out + off;
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4)
+      *(f32x4_t*)(dst + e) = f32x4_t{o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv};
+  } else {
+    uint32_t* dst = (uint32_t*)((uint16_t*)a.out + off);
+#pragma unroll
+    for (int e = 0; e < EPT; e += 2) dst[e / 2] = pack_bf16(o[e] * inv, o[e + 1] * inv);
+  }
+  if (a.lse && lane == 0)
+    a.lse[(int64_t)mi.b * hq + h] = wsum > 0.f ? (mx + log2f(wsum)) * kLn2 : -INFINITY;
+}
+
+// Copies the rows of one (request, KV head) in logical order, through the same address
+// path as the attention kernels.  One workgroup per key.
+__global__ __launch_bounds__(64) void gather_kv_kernel(const char* k, const char* v, int64_t k_sp,
+                                                       int64_t k_sh, int64_t k_st, int64_t v_sp,
+                                                       int64_t v_sh, int64_t v_st,
+                                                       const int32_t* kv_indptr,
+                                                       const int32_t* kv_indices, int32_t b,
+                                                       int32_t head, int32_t page_size,
+                                                       int32_t k_row_bytes, int32_t v_row_bytes,
+                                                       int32_t esz, char* k_out, char* v_out) {
+  const int t = blockIdx.x;
+  int32_t page, slot;
+  token_page_slot(kv_indices + kv_indptr[b], t, page_size, page, slot);
+  const char* ks = k + row_elem_offset(page, head, slot, k_sp, k_sh, k_st) * esz;
+  const char* vs = v + row_elem_offset(page, head, slot, v_sp, v_sh, v_st) * esz;
+  for (int c = threadIdx.x; c < k_row_bytes / 16; c += 64)
+    *(u32x4_t*)(k_out + (int64_t)t * k_row_bytes + 16 * c) = *(const u32x4_t*)(ks + 16 * c);
+  for (int c = threadIdx.x; c < v_row_bytes / 16; c += 64)
+    *(u32x4_t*)(v_out + (int64_t)t * v_row_bytes + 16 * c) = *(const u32x4_t*)(vs + 16 * c);
+}
+
+__global__ void fp8_to_f32_kernel(const uint8_t* codes, float* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (4 * i >= n) return;
+  uint32_t w = 0;
+  for (int u = 0; u < 4 && 4 * i + u < n; ++u) w |= (uint32_t)codes[4 * i + u] << (8 * u);
+  float f[4];
+  fp8x4_to_f32(w, f);
+  for (int u = 0; u < 4 && 4 * i + u < n; ++u) out[4 * i + u] = f[u];
+}
+
+template <int DQK, int DVO, int KVB>
+static hipError_t launch_decode_dims(const DecodeArgs& a, int gmax, int grid, hipStream_t s) {
+  switch (gmax) {
+    case 1: decode_partial_kernel<DQK, DVO, KVB, 1><<<grid, 256, 0, s>>>(a); break;
+    case 2: decode_partial_kernel<DQK, DVO, KVB, 2><<<grid, 256, 0, s>>>(a); break;
+    case 4: decode_partial_kernel<DQK, DVO, KVB, 4><<<grid, 256, 0, s>>>(a); break;
+    default: decode_partial_kernel<DQK, DVO, KVB, 8><<<grid, 256, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+static hipError_t launch_decode(const DecodeArgs& a, int dqk, int dvo, int kvb, int gmax,
+                                int grid, hipStream_t s) {
+  if (kvb == 2) {
+    if (dqk == 512 && dvo == 512) return launch_decode_dims<512, 512, 2>(a, gmax, grid, s);
+    if (dqk == 256 && dvo == 256) return launch_decode_dims<256, 256, 2>(a, gmax, grid, s);
+    return launch_decode_dims<512, 256, 2>(a, gmax, grid, s);
+  }
+  if (dqk == 512 && dvo == 512) return launch_decode_dims<512, 512, 1>(a, gmax, grid, s);
+  if (dqk == 256 && dvo == 256) return launch_decode_dims<256, 256, 1>(a, gmax, grid, s);
+  return launch_decode_dims<512, 256, 1>(a, gmax, grid, s);
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+pa_status pa_plan_upload(const pa_plan* plan, const void* plan_buf_host, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!plan || !plan_buf_host) return fail(PA_ERR_INVALID_ARG, "plan or plan buffer is NULL");
+  if (plan->plan_bytes == 0) return PA_OK;
+  if (!workspace) return fail(PA_ERR_INVALID_ARG, "workspace is NULL");
+  if ((int64_t)workspace_bytes < plan->workspace_bytes)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, plan needs %lld",
+                workspace_bytes, (long long)plan->workspace_bytes);
+  hipError_t e = hipMemcpyAsync(workspace, plan_buf_host, (size_t)plan->plan_bytes,
+                                hipMemcpyHostToDevice, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+pa_status pa_paged_decode(const pa_plan* plan, const void* q, const pa_kv_cache* cache,
+                          const pa_page_table* table, const pa_attn_params* params,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  pa_status st = check_cache(cache, true);
+  if (st != PA_OK) return st;
+  if ((st = check_params(params, cache, kMaxDecodeGroup)) != PA_OK) return st;
+  if ((st = check_plan_matches(plan, 1, params, cache, table, workspace_bytes)) != PA_OK) return st;
+  if (plan->num_items == 0) return PA_OK;
+  if (!q || !out) return fail(PA_ERR_INVALID_ARG, "q or out is NULL");
+  if (!workspace) return fail(PA_ERR_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)workspace) & 15)
+    return fail(PA_ERR_UNSUPPORTED, "q, out and workspace must be 16-byte aligned");
+  if ((uintptr_t)lse & 3) return fail(PA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+
+  const int group = params->num_qo_heads / cache->num_kv_heads;
+  const int gmax = group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8;
+  char* ws = (char*)workspace;
+  DecodeArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const char*)cache->k;
+  a.v = (const char*)cache->v;
+  a.k_sp = cache->k_stride_page; a.k_sh = cache->k_stride_head; a.k_st = cache->k_stride_token;
+  a.v_sp = cache->v_stride_page; a.v_sh = cache->v_stride_head; a.v_st = cache->v_stride_token;
+  a.kv_indptr = table->kv_indptr;
+  a.kv_indices = table->kv_indices;
+  a.items = (const DecodeItem*)(ws + plan->items_offset);
+  a.out = out;
+  a.lse = lse;
+  a.part_o = (float*)(ws + plan->partial_o_offset);
+  a.part_lse = (float*)(ws + plan->partial_lse_offset);
+  a.num_qo_heads = params->num_qo_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = group;
+  a.page_size = cache->page_size;
+  a.out_fp32 = params->out_dtype == PA_DTYPE_FP32;
+  a.scale_log2 = params->sm_scale * cache->k_scale * kLog2e;
+  a.v_scale = cache->v_scale;
+  const int kvb = cache->kv_dtype == PA_DTYPE_FP8_E4M3FN ? 1 : 2;
+  const int grid = plan->num_items * cache->num_kv_heads;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_decode(a, cache->head_dim_qk, cache->head_dim_vo, kvb, gmax, grid, s);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
+  count_launches(1);
+  if (plan->num_merges > 0) {
+    MergeArgs m;
+    m.merges = (const MergeItem*)(ws + plan->merges_offset);
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.out = out;
+    m.lse = lse;
+    m.num_qo_heads = params->num_qo_heads;
+    m.out_fp32 = a.out_fp32;
+    dim3 mg(plan->num_merges, params->num_qo_heads);
+    if (cache->head_dim_vo == 512) decode_merge_kernel<512><<<mg, 64, 0, s>>>(m);
+    else decode_merge_kernel<256><<<mg, 64, 0, s>>>(m);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+    count_launches(1);
+  }
+  return PA_OK;
+}
+
+pa_status pa_debug_gather_kv(const pa_kv_cache* cache, const pa_page_table* table,
+                             int32_t request, int32_t kv_len, int32_t kv_head, void* k_out,
+                             void* v_out, void* stream) {
+  pa_status st = check_cache(cache, true);
+  if (st != PA_OK) return st;
+  if (!table || !table->kv_indptr || !table->kv_indices)
+    return fail(PA_ERR_INVALID_ARG, "page table is NULL");
+  if (request < 0 || request >= table->batch) return fail(PA_ERR_INVALID_ARG, "request out of range");
+  if (kv_head < 0 || kv_head >= cache->num_kv_heads) return fail(PA_ERR_INVALID_ARG, "kv_head out of range");
+  if (kv_len < 0) return fail(PA_ERR_INVALID_ARG, "kv_len is negative");
+  if (kv_len == 0) return PA_OK;
+  if (!k_out || !v_out || (((uintptr_t)k_out | (uintptr_t)v_out) & 15))
+    return fail(PA_ERR_INVALID_ARG, "k_out / v_out must be non-NULL and 16-byte aligned");
+  const int esz = dtype_bytes(cache->kv_dtype);
+  gather_kv_kernel<<<kv_len, 64, 0, (hipStream_t)stream>>>(
+      (const char*)cache->k, (const char*)cache->v, cache->k_stride_page, cache->k_stride_head,
+      cache->k_stride_token, cache->v_stride_page, cache->v_stride_head, cache->v_stride_token,
+      table->kv_indptr, table->kv_indices, request, kv_head, cache->page_size,
+      cache->head_dim_qk * esz, cache->head_dim_vo * esz, esz, (char*)k_out, (char*)v_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "gather kernel launch: %s", hipGetErrorString(e));
+  count_launches(1);
+  return PA_OK;
+}
+
+pa_status pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int32_t n, void* stream) {
+  if (n < 0) return fail(PA_ERR_INVALID_ARG, "n is negative");
+  if (n == 0) return PA_OK;
+  if (!codes || !out) return fail(PA_ERR_INVALID_ARG, "codes or out is NULL");
+  const int threads = (n + 3) / 4;
+  fp8_to_f32_kernel<<<(threads + 255) / 256, 256, 0, (hipStream_t)stream>>>(codes, out, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "fp8 kernel launch: %s", hipGetErrorString(e));
+  count_launches(1);
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Device-side helpers shared by every libpa kernel: vector types, element conversions,
+// the paged address path and wave-level primitives.  gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- element conversions
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite or +-inf).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Four FP8 E4M3FN codes (one dword) -> four fp32 values, exact.  gfx950's conversion
+// instructions read the OCP E4M3FN encoding.
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* out) {
+  auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  out[0] = lo[0];
+  out[1] = lo[1];
+  out[2] = hi[0];
+  out[3] = hi[1];
+}
+
+// Four FP8 codes -> four bf16 values packed in two dwords.  Exact: every E4M3FN value has
+// at most 4 significant bits and an exponent inside bf16's range, so the upper half of
+// its fp32 image is the bf16 value.
+__device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
+  auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  u32x2_t r;
+  r[0] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
+  r[1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
+  return r;
+}
+
+// ---------------------------------------------------------------- paged address path
+//
+// Logical token t of a request whose page list starts at `pages` is slot t % P of page
+// pages[t / P] (page table layout of the Triton page, section "Approach"); every kernel
+// and the debug gather resolve keys through these two functions.
+
+__device__ __forceinline__ void token_page_slot(const int32_t* __restrict__ pages, int32_t t,
+                                                int32_t page_size, int32_t& page,
+                                                int32_t& slot) {
+  const int32_t j = t / page_size;
+  page = pages[j];
+  slot = t - j * page_size;
+}
+
+__device__ __forceinline__ int64_t row_elem_offset(int32_t page, int32_t head, int32_t slot,
+                                                   int64_t stride_page, int64_t stride_head,
+                                                   int64_t stride_token) {
+  return (int64_t)page * stride_page + (int64_t)head * stride_head + (int64_t)slot * stride_token;
+}
+
+// ---------------------------------------------------------------- wave primitives
+
+// Orders this wave's LDS writes before its later LDS reads by other lanes of the same wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  const int lane = __lane_id();
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
+}
+
+__device__ __forceinline__ int shfl_i(int v, int src_lane) {
+  return __builtin_amdgcn_ds_bpermute(src_lane << 2, v);
+}
+
+}  // namespace pa

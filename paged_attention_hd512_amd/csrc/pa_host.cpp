@@ -1,0 +1,402 @@
+// Host half of libpa: error state, cache descriptors, validation and the work planners.
+// Nothing in this file calls HIP, so every function here runs on a machine without a GPU.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <string>
+#include <vector>
+
+#include "pa_internal.hpp"
+
+namespace pa {
+
+static thread_local std::string g_last_error;
+static std::atomic<uint64_t> g_launches{0};
+
+pa_status fail(pa_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+void count_launches(uint64_t n) { g_launches.fetch_add(n, std::memory_order_relaxed); }
+
+static bool supported_dims(int qk, int vo) {
+  return (qk == 512 && vo == 512) || (qk == 256 && vo == 256) || (qk == 512 && vo == 256);
+}
+
+pa_status check_cache(const pa_kv_cache* c, bool need_pointers) {
+  if (!c) return fail(PA_ERR_INVALID_ARG, "cache is NULL");
+  if (c->kv_dtype != PA_DTYPE_BF16 && c->kv_dtype != PA_DTYPE_FP8_E4M3FN)
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype %d: only bf16 and fp8 e4m3fn KV are supported",
+                c->kv_dtype);
+  if (c->num_pages < 1 || c->num_kv_heads < 1 || c->page_size < 1)
+    return fail(PA_ERR_INVALID_ARG, "num_pages (%d), num_kv_heads (%d) and page_size (%d) must be >= 1",
+                c->num_pages, c->num_kv_heads, c->page_size);
+  if (!supported_dims(c->head_dim_qk, c->head_dim_vo))
+    return fail(PA_ERR_UNSUPPORTED,
+                "head dims (qk=%d, vo=%d): supported are (512,512), (256,256), (512,256)",
+                c->head_dim_qk, c->head_dim_vo);
+  const int64_t vec = 16 / dtype_bytes(c->kv_dtype);  // elements per 16-byte vector
+  const int64_t s[6] = {c->k_stride_page, c->k_stride_head, c->k_stride_token,
+                        c->v_stride_page, c->v_stride_head, c->v_stride_token};
+  const char* names[6] = {"k_stride_page", "k_stride_head", "k_stride_token",
+                          "v_stride_page", "v_stride_head", "v_stride_token"};
+  for (int i = 0; i < 6; ++i) {
+    if (s[i] < 0) return fail(PA_ERR_INVALID_ARG, "%s is negative", names[i]);
+    if (s[i] % vec)
+      return fail(PA_ERR_UNSUPPORTED, "%s = %lld is not a multiple of 16 bytes", names[i],
+                  (long long)s[i]);
+  }
+  if (c->kv_dtype == PA_DTYPE_BF16 && (c->k_scale != 1.0f || c->v_scale != 1.0f))
+    return fail(PA_ERR_INVALID_ARG, "bf16 KV takes k_scale = v_scale = 1");
+  if (!(std::isfinite(c->k_scale) && c->k_scale > 0.f && std::isfinite(c->v_scale) &&
+        c->v_scale > 0.f))
+    return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+  if (need_pointers) {
+    if (!c->k || !c->v) return fail(PA_ERR_INVALID_ARG, "cache k/v pointer is NULL");
+    if (((uintptr_t)c->k | (uintptr_t)c->v) & 15)
+      return fail(PA_ERR_UNSUPPORTED, "cache k/v pointers must be 16-byte aligned");
+  }
+  return PA_OK;
+}
+
+pa_status check_params(const pa_attn_params* p, const pa_kv_cache* c, int max_group) {
+  if (!p) return fail(PA_ERR_INVALID_ARG, "params is NULL");
+  if (p->num_qo_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_qo_heads must be >= 1");
+  if (p->num_qo_heads % c->num_kv_heads)
+    return fail(PA_ERR_INVALID_ARG, "num_qo_heads (%d) is not a multiple of num_kv_heads (%d)",
+                p->num_qo_heads, c->num_kv_heads);
+  const int group = p->num_qo_heads / c->num_kv_heads;
+  if (group > max_group)
+    return fail(PA_ERR_UNSUPPORTED, "%d query heads per KV head; at most %d are supported",
+                group, max_group);
+  if (!std::isfinite(p->sm_scale)) return fail(PA_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (p->q_dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "q_dtype %d: only bf16 queries are supported", p->q_dtype);
+  if (p->out_dtype != PA_DTYPE_BF16 && p->out_dtype != PA_DTYPE_FP32)
+    return fail(PA_ERR_UNSUPPORTED, "out_dtype %d: only fp32 and bf16 outputs are supported",
+                p->out_dtype);
+  return PA_OK;
+}
+
+static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+static pa_status check_table_host(const int32_t* indptr, const int32_t* last, int32_t batch,
+                                  int32_t page_size) {
+  if (batch < 0) return fail(PA_ERR_INVALID_ARG, "batch is negative");
+  if (batch == 0) return PA_OK;
+  if (!indptr || !last) return fail(PA_ERR_INVALID_ARG, "host kv_indptr / kv_last_page_len is NULL");
+  if (indptr[0] != 0) return fail(PA_ERR_INVALID_ARG, "kv_indptr[0] = %d, must be 0", indptr[0]);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t n = indptr[b + 1] - indptr[b];
+    if (n < 0) return fail(PA_ERR_INVALID_ARG, "kv_indptr decreases at request %d", b);
+    if (n > 0 && (last[b] < 1 || last[b] > page_size))
+      return fail(PA_ERR_INVALID_ARG, "kv_last_page_len[%d] = %d is outside [1, %d]", b, last[b],
+                  page_size);
+    const int64_t len = n == 0 ? 0 : (int64_t)(n - 1) * page_size + last[b];
+    if (len > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "request %d is longer than 2^31 keys", b);
+  }
+  return PA_OK;
+}
+
+static int64_t kv_len_of(const int32_t* indptr, const int32_t* last, int32_t b, int32_t page_size) {
+  const int32_t n = indptr[b + 1] - indptr[b];
+  return n == 0 ? 0 : (int64_t)(n - 1) * page_size + last[b];
+}
+
+static void plan_header(pa_plan* plan, int kind, const pa_attn_params* p, const pa_kv_cache* c,
+                        int32_t batch) {
+  memset(plan, 0, sizeof(*plan));
+  plan->kind = kind;
+  plan->batch = batch;
+  plan->num_qo_heads = p->num_qo_heads;
+  plan->num_kv_heads = c->num_kv_heads;
+  plan->page_size = c->page_size;
+  plan->head_dim_qk = c->head_dim_qk;
+  plan->head_dim_vo = c->head_dim_vo;
+  plan->kv_dtype = c->kv_dtype;
+  plan->window = p->window > 0 ? p->window : 0;
+  plan->causal = p->causal ? 1 : 0;
+}
+
+pa_status check_plan_matches(const pa_plan* plan, int kind, const pa_attn_params* p,
+                             const pa_kv_cache* c, const pa_page_table* t,
+                             size_t workspace_bytes) {
+  if (!plan) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
+  if (!t) return fail(PA_ERR_INVALID_ARG, "page table is NULL");
+  if (plan->kind != kind) return fail(PA_ERR_INVALID_ARG, "plan kind %d does not match this call", plan->kind);
+  const int window = p->window > 0 ? p->window : 0;
+  if (plan->batch != t->batch || plan->num_qo_heads != p->num_qo_heads ||
+      plan->num_kv_heads != c->num_kv_heads || plan->page_size != c->page_size ||
+      plan->head_dim_qk != c->head_dim_qk || plan->head_dim_vo != c->head_dim_vo ||
+      plan->kv_dtype != c->kv_dtype || plan->window != window ||
+      (kind == 2 && plan->causal != (p->causal ? 1 : 0)))
+    return fail(PA_ERR_INVALID_ARG,
+                "plan was made for other sizes (batch, heads, page size, head dims, dtype, "
+                "window or causal differ)");
+  if ((int64_t)workspace_bytes < plan->workspace_bytes)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, plan needs %lld",
+                workspace_bytes, (long long)plan->workspace_bytes);
+  if (t->batch > 0 && (!t->kv_indptr || !t->kv_indices || !t->kv_last_page_len))
+    return fail(PA_ERR_INVALID_ARG, "device page table pointer is NULL");
+  return PA_OK;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+uint64_t pa_launch_count(void) { return g_launches.load(std::memory_order_relaxed); }
+const char* pa_version(void) { return "libpa 0.1.0 (gfx950)"; }
+
+pa_status pa_kv_cache_hnd(const void* base, int32_t kv_dtype, int32_t num_pages,
+                          int32_t num_kv_heads, int32_t page_size, int32_t head_dim,
+                          float k_scale, float v_scale, pa_kv_cache* out) {
+  if (!out) return fail(PA_ERR_INVALID_ARG, "out is NULL");
+  pa_kv_cache c;
+  memset(&c, 0, sizeof(c));
+  const int esz = dtype_bytes(kv_dtype);
+  c.k = base;
+  c.v = base ? (const void*)((const char*)base + (size_t)num_kv_heads * page_size * head_dim * esz)
+             : nullptr;
+  c.kv_dtype = kv_dtype;
+  c.num_pages = num_pages;
+  c.num_kv_heads = num_kv_heads;
+  c.page_size = page_size;
+  c.head_dim_qk = c.head_dim_vo = head_dim;
+  c.k_stride_token = c.v_stride_token = head_dim;
+  c.k_stride_head = c.v_stride_head = (int64_t)page_size * head_dim;
+  c.k_stride_page = c.v_stride_page = 2 * (int64_t)num_kv_heads * page_size * head_dim;
+  c.k_scale = k_scale;
+  c.v_scale = v_scale;
+  pa_status st = check_cache(&c, false);
+  if (st != PA_OK) return st;
+  *out = c;
+  return PA_OK;
+}
+
+pa_status pa_kv_cache_separate(const void* k, const void* v, int32_t kv_dtype,
+                               int32_t num_pages, int32_t num_kv_heads, int32_t page_size,
+                               int32_t head_dim_qk, int32_t head_dim_vo, float k_scale,
+                               float v_scale, pa_kv_cache* out) {
+  if (!out) return fail(PA_ERR_INVALID_ARG, "out is NULL");
+  pa_kv_cache c;
+  memset(&c, 0, sizeof(c));
+  c.k = k;
+  c.v = v;
+  c.kv_dtype = kv_dtype;
+  c.num_pages = num_pages;
+  c.num_kv_heads = num_kv_heads;
+  c.page_size = page_size;
+  c.head_dim_qk = head_dim_qk;
+  c.head_dim_vo = head_dim_vo;
+  c.k_stride_token = head_dim_qk;
+  c.k_stride_head = (int64_t)page_size * head_dim_qk;
+  c.k_stride_page = (int64_t)num_kv_heads * page_size * head_dim_qk;
+  c.v_stride_token = head_dim_vo;
+  c.v_stride_head = (int64_t)page_size * head_dim_vo;
+  c.v_stride_page = (int64_t)num_kv_heads * page_size * head_dim_vo;
+  c.k_scale = k_scale;
+  c.v_scale = v_scale;
+  pa_status st = check_cache(&c, false);
+  if (st != PA_OK) return st;
+  *out = c;
+  return PA_OK;
+}
+
+pa_status pa_validate_page_table_host(const int32_t* kv_indptr_host,
+                                      const int32_t* kv_indices_host,
+                                      const int32_t* kv_last_page_len_host, int32_t batch,
+                                      int32_t num_pages, int32_t page_size) {
+  if (page_size < 1) return fail(PA_ERR_INVALID_ARG, "page_size must be >= 1");
+  pa_status st = check_table_host(kv_indptr_host, kv_last_page_len_host, batch, page_size);
+  if (st != PA_OK || batch == 0 || !kv_indices_host) return st;
+  const int32_t n = kv_indptr_host[batch];
+  for (int32_t i = 0; i < n; ++i)
+    if (kv_indices_host[i] < 0 || kv_indices_host[i] >= num_pages)
+      return fail(PA_ERR_INVALID_ARG, "kv_indices[%d] = %d is outside [0, %d)", i,
+                  kv_indices_host[i], num_pages);
+  return PA_OK;
+}
+
+pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
+                         const int32_t* kv_indptr_host, const int32_t* kv_last_page_len_host,
+                         int32_t batch, int32_t num_splits, void* plan_buf_host,
+                         size_t plan_buf_bytes, pa_plan* plan) {
+  if (!plan) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
+  pa_status st = check_cache(cache, false);
+  if (st != PA_OK) return st;
+  if ((st = check_params(params, cache, kMaxDecodeGroup)) != PA_OK) return st;
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(PA_ERR_UNSUPPORTED, "num_splits = %d: must be in [0, %d] (0 = adaptive)",
+                num_splits, kMaxSplits);
+  if ((st = check_table_host(kv_indptr_host, kv_last_page_len_host, batch, cache->page_size)) != PA_OK)
+    return st;
+
+  const int window = params->window > 0 ? params->window : 0;
+  const int P = cache->page_size;
+  std::vector<int64_t> len(batch), start(batch), nblk(batch);
+  int64_t total_blocks = 0, max_len = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    len[b] = kv_len_of(kv_indptr_host, kv_last_page_len_host, b, P);
+    start[b] = window > 0 ? std::max<int64_t>(0, len[b] - window) : 0;
+    const int64_t fb = start[b] / kBlockTokens;
+    const int64_t eb = (len[b] + kBlockTokens - 1) / kBlockTokens;
+    nblk[b] = std::max<int64_t>(0, eb - fb);
+    total_blocks += nblk[b];
+    max_len = std::max(max_len, len[b]);
+  }
+  std::vector<int32_t> chunks(batch);
+  int64_t chunk_blocks = 0;
+  if (num_splits > 0) {
+    for (int32_t b = 0; b < batch; ++b)
+      chunks[b] = (int32_t)std::max<int64_t>(1, std::min<int64_t>(num_splits, nblk[b]));
+  } else {
+    const int64_t target_chunks =
+        (kTargetWorkgroups + cache->num_kv_heads - 1) / cache->num_kv_heads;
+    chunk_blocks = std::max<int64_t>(kMinChunkBlocks, (total_blocks + target_chunks - 1) / target_chunks);
+    for (int32_t b = 0; b < batch; ++b)
+      chunks[b] = (int32_t)std::max<int64_t>(
+          1, std::min<int64_t>(kMaxSplits, (nblk[b] + chunk_blocks - 1) / chunk_blocks));
+  }
+
+  struct Tmp { DecodeItem it; int32_t c; };
+  std::vector<Tmp> items;
+  std::vector<MergeItem> merges;
+  int32_t next_slot = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t cb = chunks[b];
+    const int64_t fb = start[b] / kBlockTokens;
+    int32_t slot0 = -1;
+    if (cb > 1) {
+      slot0 = next_slot;
+      merges.push_back(MergeItem{b, next_slot, cb, 0});
+      next_slot += cb;
+    }
+    for (int32_t c = 0; c < cb; ++c) {
+      const int64_t lo = fb + (nblk[b] * c) / cb;
+      const int64_t hi = fb + (nblk[b] * (c + 1)) / cb;
+      int64_t t0 = std::max<int64_t>(start[b], lo * kBlockTokens);
+      int64_t t1 = std::min<int64_t>(len[b], hi * kBlockTokens);
+      if (len[b] == 0) t0 = t1 = 0;
+      items.push_back(Tmp{DecodeItem{b, (int32_t)t0, (int32_t)t1, cb == 1 ? -1 : slot0 + c}, c});
+    }
+  }
+  // Longest first; the generation order (b, c) breaks ties.
+  std::stable_sort(items.begin(), items.end(), [](const Tmp& a, const Tmp& b) {
+    return (a.it.t_end - a.it.t_begin) > (b.it.t_end - b.it.t_begin);
+  });
+
+  plan_header(plan, 1, params, cache, batch);
+  plan->num_items = (int32_t)items.size();
+  plan->num_slots = next_slot;
+  plan->num_merges = (int32_t)merges.size();
+  plan->block_tokens = kBlockTokens;
+  plan->chunk_blocks = (int32_t)chunk_blocks;
+  plan->num_splits = num_splits;
+  plan->max_kv_len = (int32_t)max_len;
+  plan->items_offset = 0;
+  plan->merges_offset = align_up((int64_t)items.size() * sizeof(DecodeItem), 16);
+  plan->plan_bytes = align_up(plan->merges_offset + (int64_t)merges.size() * sizeof(MergeItem), 256);
+  plan->partial_o_offset = plan->plan_bytes;
+  const int64_t o_bytes = (int64_t)next_slot * params->num_qo_heads * cache->head_dim_vo * 4;
+  plan->partial_lse_offset = align_up(plan->partial_o_offset + o_bytes, 256);
+  plan->workspace_bytes =
+      align_up(plan->partial_lse_offset + (int64_t)next_slot * params->num_qo_heads * 4, 256);
+
+  if (!plan_buf_host) return PA_OK;  // sizing call
+  if ((int64_t)plan_buf_bytes < plan->plan_bytes)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "plan buffer has %zu bytes, plan needs %lld",
+                plan_buf_bytes, (long long)plan->plan_bytes);
+  char* buf = (char*)plan_buf_host;
+  memset(buf, 0, (size_t)plan->plan_bytes);
+  DecodeItem* out_items = (DecodeItem*)(buf + plan->items_offset);
+  for (size_t i = 0; i < items.size(); ++i) out_items[i] = items[i].it;
+  memcpy(buf + plan->merges_offset, merges.data(), merges.size() * sizeof(MergeItem));
+  return PA_OK;
+}
+
+pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache,
+                          const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+                          const int32_t* kv_last_page_len_host, int32_t batch,
+                          void* plan_buf_host, size_t plan_buf_bytes, pa_plan* plan) {
+  if (!plan) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
+  pa_status st = check_cache(cache, false);
+  if (st != PA_OK) return st;
+  if (cache->kv_dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 KV only");
+  if ((st = check_params(params, cache, kMaxPrefillGroup)) != PA_OK) return st;
+  if ((st = check_table_host(kv_indptr_host, kv_last_page_len_host, batch, cache->page_size)) != PA_OK)
+    return st;
+  if (batch > 0) {
+    if (!qo_indptr_host) return fail(PA_ERR_INVALID_ARG, "host qo_indptr is NULL");
+    if (qo_indptr_host[0] != 0) return fail(PA_ERR_INVALID_ARG, "qo_indptr[0] must be 0");
+  }
+  const int P = cache->page_size;
+  const int group = params->num_qo_heads / cache->num_kv_heads;
+  const int window = params->window > 0 ? params->window : 0;
+  const bool causal = params->causal != 0;
+  struct Tmp { PrefillItem it; int32_t j; };
+  std::vector<Tmp> tiles;
+  int64_t max_len = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t q_len = (int64_t)qo_indptr_host[b + 1] - qo_indptr_host[b];
+    if (q_len < 0) return fail(PA_ERR_INVALID_ARG, "qo_indptr decreases at request %d", b);
+    const int64_t L = kv_len_of(kv_indptr_host, kv_last_page_len_host, b, P);
+    if (q_len > L)
+      return fail(PA_ERR_INVALID_ARG, "request %d has %lld new tokens but only %lld keys", b,
+                  (long long)q_len, (long long)L);
+    max_len = std::max(max_len, L);
+    const int64_t rows = q_len * group;
+    if (rows > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "request %d has too many query rows", b);
+    int32_t j = 0;
+    for (int64_t r0 = 0; r0 < rows; r0 += kPrefillTileRows, ++j) {
+      const int64_t r1 = std::min<int64_t>(rows, r0 + kPrefillTileRows);
+      const int64_t pos_first = L - q_len + r0 / group;
+      const int64_t pos_last = L - q_len + (r1 - 1) / group;
+      const int64_t kv_end = causal ? pos_last + 1 : L;
+      const int64_t kv_begin = window > 0 ? std::max<int64_t>(0, pos_first - window + 1) : 0;
+      tiles.push_back(Tmp{PrefillItem{b, (int32_t)r0, (int32_t)r1, (int32_t)kv_begin,
+                                      (int32_t)kv_end, qo_indptr_host[b], (int32_t)L,
+                                      (int32_t)q_len},
+                          j});
+    }
+  }
+  std::stable_sort(tiles.begin(), tiles.end(), [](const Tmp& a, const Tmp& b) {
+    return (a.it.kv_end - a.it.kv_begin) > (b.it.kv_end - b.it.kv_begin);
+  });
+  plan_header(plan, 2, params, cache, batch);
+  plan->num_items = (int32_t)tiles.size();
+  plan->tile_rows = kPrefillTileRows;
+  plan->total_q = batch > 0 ? qo_indptr_host[batch] : 0;
+  plan->max_kv_len = (int32_t)max_len;
+  plan->items_offset = 0;
+  plan->merges_offset = align_up((int64_t)tiles.size() * sizeof(PrefillItem), 16);
+  plan->plan_bytes = align_up(plan->merges_offset, 256);
+  plan->partial_o_offset = plan->partial_lse_offset = plan->plan_bytes;
+  plan->workspace_bytes = plan->plan_bytes;
+  if (!plan_buf_host) return PA_OK;
+  if ((int64_t)plan_buf_bytes < plan->plan_bytes)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "plan buffer has %zu bytes, plan needs %lld",
+                plan_buf_bytes, (long long)plan->plan_bytes);
+  char* buf = (char*)plan_buf_host;
+  memset(buf, 0, (size_t)plan->plan_bytes);
+  PrefillItem* out = (PrefillItem*)(buf + plan->items_offset);
+  for (size_t i = 0; i < tiles.size(); ++i) out[i] = tiles[i].it;
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal declarations shared by the host planner (pa_host.cpp) and the HIP launchers.
+#pragma once
+
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// Decode partition: keys are grouped in logical blocks of 16 tokens (one MFMA tile of
+// keys); a work item is a contiguous run of blocks of one request.
+constexpr int kBlockTokens = 16;
+constexpr int kTargetWorkgroups = 2048;  // adaptive split aims at about this many
+constexpr int kMinChunkBlocks = 8;
+constexpr int kMaxSplits = 64;
+constexpr int kMaxDecodeGroup = 8;       // query heads per KV head in decode
+constexpr int kMaxPrefillGroup = 16;
+
+// Prefill: query rows per tile ((token, head) pairs of one head group).
+constexpr int kPrefillTileRows = 128;
+
+struct DecodeItem {   // 16 bytes
+  int32_t b;          // request
+  int32_t t_begin;    // first visible key of the chunk
+  int32_t t_end;      // one past the last key of the chunk
+  int32_t slot;       // partial slot, or -1: write the final output directly
+};
+
+struct MergeItem {    // 16 bytes
+  int32_t b;
+  int32_t slot_begin;
+  int32_t num_chunks;
+  int32_t pad;
+};
+
+struct PrefillItem {  // 32 bytes
+  int32_t b;
+  int32_t row_begin;  // first (token, head) row of the tile within the request's group
+  int32_t row_end;
+  int32_t kv_begin;   // keys the tile can see: [kv_begin, kv_end)
+  int32_t kv_end;
+  int32_t q_begin;    // qo_indptr[b]
+  int32_t kv_len;     // L_b
+  int32_t q_len;      // qo_indptr[b+1] - qo_indptr[b]
+};
+
+pa_status fail(pa_status code, const char* fmt, ...);
+void count_launches(uint64_t n);
+
+// Argument checks shared by planning and running.  `need_pointers` also checks the
+// cache's base pointers and their alignment.
+pa_status check_cache(const pa_kv_cache* c, bool need_pointers);
+pa_status check_params(const pa_attn_params* p, const pa_kv_cache* c, int max_group);
+pa_status check_plan_matches(const pa_plan* plan, int kind, const pa_attn_params* p,
+                             const pa_kv_cache* c, const pa_page_table* t,
+                             size_t workspace_bytes);
+
+inline int dtype_bytes(int32_t dt) { return dt == PA_DTYPE_FP8_E4M3FN ? 1 : (dt == PA_DTYPE_FP32 ? 4 : 2); }
+
+}  // namespace pa

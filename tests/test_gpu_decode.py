@@ -1,0 +1,153 @@
+"""GPU parity of the decode path (libpa's HIP kernels through the C ABI) with the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import make_decode_case, decode_workload
+from parity import (say, compare, oracle_decode, gpu_decode, out_to_np, pool_to_np,
+                    bf16_to_np)
+import paged_attention_hd512_amd.pa as pa
+
+pytestmark = pytest.mark.gpu
+
+
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return "cuda"
+
+
+def test_fp8_conversion_matches_the_code_table():
+    say("fp8 conversion, all 256 codes")
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).to(dev())
+    out = torch.empty(256, dtype=torch.float32, device=dev())
+    pa.pa_debug_fp8_to_f32(codes.data_ptr(), out.data_ptr(), 256, pa.current_stream_handle())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = oracle.E4M3FN_VALUES
+    nan = np.isnan(ref)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("dim,dvo,page,kv_dtype", [(512, 512, 16, "bf16"), (256, 256, 1, "bf16"),
+                                                   (512, 256, 3, "bf16"), (512, 512, 64, "fp8"),
+                                                   (256, 256, 32, "fp8")])
+def test_gather_is_bit_exact(dim, dvo, page, kv_dtype):
+    say(f"gather dim={dim}/{dvo} page={page} {kv_dtype}")
+    c = make_decode_case([37, 64, 1, 100], 4, 2, dim, page, head_dim_vo=dvo, kv_dtype=kv_dtype,
+                         seed=3, device=dev())
+    cache = pa.cache_from_pools(c.k_pool, c.v_pool, kv_dtype, c.k_scale, c.v_scale)
+    ip = torch.as_tensor(c.kv_indptr).to(dev())
+    ix = torch.as_tensor(c.kv_indices).to(dev())
+    la = torch.as_tensor(c.kv_last_page_len).to(dev())
+    table = pa.pa_page_table(ip.data_ptr(), ix.data_ptr(), la.data_ptr(), c.batch)
+    kp, vp = pool_to_np(c.k_pool, kv_dtype), pool_to_np(c.v_pool, kv_dtype)
+    edt = torch.bfloat16 if kv_dtype == "bf16" else torch.uint8
+    for b in range(c.batch):
+        L = int(c.kv_lens[b])
+        for h in range(c.num_kv_heads):
+            ko = torch.empty((L, dim), dtype=edt, device=dev())
+            vo = torch.empty((L, dvo), dtype=edt, device=dev())
+            pa.pa_debug_gather_kv(cache, table, b, L, h, ko.data_ptr(), vo.data_ptr(),
+                                  pa.current_stream_handle())
+            torch.cuda.synchronize()
+            kr = oracle.gather_request_kv(kp, c.kv_indptr, c.kv_indices, c.kv_last_page_len,
+                                          page, b)[:, h]
+            vr = oracle.gather_request_kv(vp, c.kv_indptr, c.kv_indices, c.kv_last_page_len,
+                                          page, b)[:, h]
+            assert np.array_equal(pool_to_np(ko, kv_dtype), kr)
+            assert np.array_equal(pool_to_np(vo, kv_dtype), vr)
+
+
+def test_tiny_decode_workload_split_1_and_2():
+    c = decode_workload("tiny_decode", device=dev())
+    ref, ref_lse = oracle_decode(c)
+    for splits in (1, 2):
+        say(f"tiny decode split={splits}")
+        before = pa.pa_launch_count()
+        runner, out, lse = gpu_decode(c, num_splits=splits)
+        launched = pa.pa_launch_count() - before
+        assert launched == (1 if splits == 1 else 2)  # the HIP kernels actually ran
+        assert out.dtype == torch.float32
+        compare(f"tiny split={splits}", out_to_np(out), ref, lse.cpu().numpy(), ref_lse)
+
+
+SWEEP = [
+    # lens, hq, hkv, dim, dvo, page, kv_dtype, window, splits, out
+    ([37, 64, 1, 16, 17, 300], 8, 1, 512, 512, 16, "bf16", 0, 0, "fp32"),
+    ([37, 64, 1, 16, 17, 300], 24, 4, 512, 512, 16, "bf16", 0, 8, "bf16"),
+    ([5, 130, 777, 64], 12, 4, 512, 512, 64, "fp8", 0, 0, "bf16"),
+    ([5, 130, 777, 64], 12, 4, 512, 512, 64, "fp8", 0, 3, "fp32"),
+    ([600, 1500, 33, 2048], 16, 8, 512, 512, 1, "bf16", 100, 0, "bf16"),
+    ([600, 1500, 33, 2048], 16, 8, 512, 512, 32, "bf16", 1024, 0, "fp32"),
+    ([600, 1500, 33, 2048], 16, 8, 256, 256, 1, "bf16", 1024, 0, "bf16"),
+    ([600, 1500, 33, 2048], 16, 8, 256, 256, 32, "bf16", 100, 4, "bf16"),
+    ([45, 46, 47, 200], 6, 2, 512, 256, 3, "bf16", 0, 2, "fp32"),
+    ([45, 46, 47, 200], 6, 2, 512, 256, 16, "fp8", 17, 0, "fp32"),
+    ([100, 200, 300], 2, 2, 512, 512, 16, "bf16", 0, 5, "fp32"),
+    ([100, 200, 300], 4, 1, 256, 256, 8, "fp8", 0, 0, "bf16"),
+    ([1, 2, 3, 1000], 16, 2, 512, 512, 16, "bf16", 1, 0, "fp32"),
+    ([64, 128, 192], 40, 8, 512, 512, 16, "bf16", 0, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("lens,hq,hkv,dim,dvo,page,kv_dtype,window,splits,out", SWEEP)
+def test_decode_sweep(lens, hq, hkv, dim, dvo, page, kv_dtype, window, splits, out):
+    name = (f"lens={lens} heads={hq}/{hkv} dims={dim}/{dvo} page={page} {kv_dtype} "
+            f"window={window} splits={splits} out={out}")
+    say(name)
+    c = make_decode_case(lens, hq, hkv, dim, page, head_dim_vo=dvo, kv_dtype=kv_dtype,
+                         window=window, num_splits=splits, out_dtype=out, seed=len(lens) + hq,
+                         device=dev())
+    _, o, lse = gpu_decode(c)
+    ref, ref_lse = oracle_decode(c)
+    compare(name, out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
+
+
+def test_empty_requests_give_zero_output_and_minus_inf_lse():
+    say("empty requests")
+    c = make_decode_case([0, 20, 0], 8, 1, 512, 16, seed=5, device=dev(), out_dtype="fp32",
+                         num_splits=2)
+    _, o, lse = gpu_decode(c)
+    o, lse = out_to_np(o), lse.cpu().numpy()
+    assert np.array_equal(o[0], np.zeros_like(o[0])) and np.array_equal(o[2], np.zeros_like(o[2]))
+    assert np.all(lse[[0, 2]] == -np.inf)
+    ref, ref_lse = oracle_decode(c)
+    compare("empty requests", o, ref, lse, ref_lse)
+
+
+def test_page_relabeling_gives_bit_identical_output_and_runs_are_deterministic():
+    say("page permutation invariance")
+    c = make_decode_case([37, 64, 500, 1000], 24, 4, 512, 16, num_splits=3, seed=8, device=dev())
+    _, o1, l1 = gpu_decode(c)
+    _, o1b, l1b = gpu_decode(c)
+    assert torch.equal(o1, o1b) and torch.equal(l1, l1b)
+    perm = np.random.default_rng(2).permutation(c.num_pages)
+    inv = torch.as_tensor(np.argsort(perm)).to(dev())
+    cache2 = c.cache.index_select(0, inv)  # page p of the old pool is page perm[p] now
+    c.cache, c.k_pool, c.v_pool = cache2, cache2[:, 0], cache2[:, 1]
+    c.kv_indices = perm[c.kv_indices].astype(np.int32)
+    _, o2, l2 = gpu_decode(c)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,variant", [("gqa_decode", None), ("fp8_decode", None),
+                                          ("window_decode", (512, 1)),
+                                          ("window_decode", (512, 32)),
+                                          ("window_decode", (256, 1)),
+                                          ("window_decode", (256, 32))])
+def test_full_size_workloads_on_sampled_requests(name, variant):
+    """The benchmark's workloads at full size, in its launch configuration; the oracle
+    checks a sample of requests (shortest, longest and a random one)."""
+    say(f"full-size {name} {variant}")
+    c = decode_workload(name, device=dev(), variant=variant)
+    _, o, lse = gpu_decode(c)
+    lens = c.kv_lens
+    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)),
+                     int(np.random.default_rng(0).integers(0, c.batch))})
+    ref, ref_lse = oracle_decode(c, requests=sample)
+    compare(f"{name} {variant} requests {sample}", out_to_np(o[sample]), ref,
+            lse[sample].cpu().numpy(), ref_lse)
+    assert torch.isfinite(o.float()).all()

@@ -1,0 +1,261 @@
+"""CPU tests of libpa's host half: exports, descriptors, planners and argument checks.
+
+Nothing here launches a kernel: the planners and validators never call HIP, and every
+failing run-call case below is refused by the host checks before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle.partition import decode_partition_ref, prefill_tiles_ref
+import paged_attention_hd512_amd.pa as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) == 13
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pa_[a-z0-9_]+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(names) == set(pa.SIGNATURES)  # the binding covers exactly the header
+
+
+def test_version_and_counter():
+    assert "gfx950" in pa.pa_version()
+    assert pa.pa_launch_count() >= 0
+
+
+def params(hq=8, window=0, causal=1, out=pa.PA_DTYPE_FP32, scale=0.05):
+    return pa.pa_attn_params(hq, scale, window, causal, pa.PA_DTYPE_BF16, out)
+
+
+def test_hnd_descriptor_layout():
+    c = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, 10, 4, 16, 512)
+    assert (c.k_stride_page, c.k_stride_head, c.k_stride_token) == (2 * 4 * 16 * 512, 16 * 512, 512)
+    assert (c.v_stride_page, c.v_stride_head, c.v_stride_token) == (2 * 4 * 16 * 512, 16 * 512, 512)
+    assert c.v - c.k == 4 * 16 * 512 * 2  # V half starts one [H, P, D] block later, in bytes
+    c8 = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_FP8_E4M3FN, 10, 4, 64, 512, 0.5, 0.25)
+    assert c8.v - c8.k == 4 * 64 * 512 and (c8.k_scale, c8.v_scale) == (0.5, 0.25)
+    s = pa.pa_kv_cache_separate(0x10000, 0x20000, pa.PA_DTYPE_BF16, 7, 8, 64, 512, 256)
+    assert (s.k_stride_page, s.v_stride_page) == (8 * 64 * 512, 8 * 64 * 256)
+    assert (s.head_dim_qk, s.head_dim_vo) == (512, 256)
+
+
+def lens_to_table(lens, P):
+    n = [(L + P - 1) // P for L in lens]
+    indptr = np.zeros(len(lens) + 1, np.int32)
+    indptr[1:] = np.cumsum(n)
+    last = np.array([(L - 1) % P + 1 if L > 0 else 0 for L in lens], np.int32)
+    return indptr, last
+
+
+DECODE_CASES = [
+    ([37, 64], 16, 0, 1, 1),
+    ([37, 64], 16, 0, 2, 1),
+    ([1, 15, 16, 17, 0, 300], 16, 0, 8, 2),
+    ([1024, 8192, 5000, 4097], 16, 0, 8, 4),
+    ([4096, 32768, 9000], 64, 0, 0, 4),
+    ([512, 16384, 1000, 1023, 1025], 1, 1024, 0, 8),
+    ([512, 16384, 1000], 32, 1024, 0, 8),
+    ([100, 5, 0], 3, 7, 3, 1),
+    (list(np.random.default_rng(0).integers(1024, 8193, size=32)), 16, 0, 8, 4),
+    (list(np.random.default_rng(1).integers(4096, 32769, size=64)), 64, 0, 0, 4),
+]
+
+
+@pytest.mark.parametrize("lens,P,window,splits,hkv", DECODE_CASES)
+def test_decode_plan_matches_reference_partition(lens, P, window, splits, hkv):
+    indptr, last = lens_to_table(lens, P)
+    cache = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, int(indptr[-1]) + 1, hkv, P, 512)
+    plan, buf = pa.pa_decode_plan(params(hq=hkv * 2, window=window), cache, indptr, last, splits)
+    items = pa.decode_items(plan, buf)
+    merges = pa.decode_merges(plan, buf)
+    ref_items, ref_merges = decode_partition_ref(lens, window, splits, hkv)
+    assert [tuple(r) for r in items.tolist()] == [tuple(r) for r in ref_items]
+    assert [tuple(r) for r in merges.tolist()] == [tuple(r) for r in ref_merges]
+    assert plan.num_items == len(ref_items) and plan.num_merges == len(ref_merges)
+    assert plan.num_slots == sum(m[2] for m in ref_merges)
+    hq, dvo = hkv * 2, 512
+    assert plan.partial_lse_offset - plan.partial_o_offset >= plan.num_slots * hq * dvo * 4
+    assert plan.workspace_bytes >= plan.partial_lse_offset + plan.num_slots * hq * 4
+
+
+@pytest.mark.parametrize("lens,P,window,splits,hkv", DECODE_CASES)
+def test_reference_partition_covers_visible_keys_exactly(lens, P, window, splits, hkv):
+    items, merges = decode_partition_ref(lens, window, splits, hkv)
+    per_req = {}
+    for b, t0, t1, slot in items:
+        per_req.setdefault(b, []).append((t0, t1, slot))
+    for b, L in enumerate(lens):
+        L = int(L)
+        chunks = sorted(per_req[b])
+        start = max(0, L - window) if window > 0 else 0
+        if L == 0:
+            assert chunks == [(0, 0, -1)]
+            continue
+        assert chunks[0][0] == start and chunks[-1][1] == L
+        for (a0, a1, _), (b0, b1, _) in zip(chunks, chunks[1:]):
+            assert a1 == b0 and b0 % 16 == 0  # contiguous, inner cuts on 16-key blocks
+        assert all(t1 > t0 for t0, t1, _ in chunks)
+        if splits > 0:
+            assert len(chunks) <= splits
+    counts = [t1 - t0 for _, t0, t1, _ in items]
+    assert counts == sorted(counts, reverse=True)  # longest first
+
+
+PREFILL_CASES = [
+    ([4096] * 4, [5120] * 4, 2, True, 0),
+    ([5, 1, 0], [37, 20, 9], 3, True, 0),
+    ([33, 7], [40, 7], 6, True, 5),
+    ([17], [17], 1, False, 0),
+    ([200, 64], [1000, 64], 8, True, 100),
+]
+
+
+@pytest.mark.parametrize("qo,kv,group,causal,window", PREFILL_CASES)
+def test_prefill_plan_matches_reference_tiles(qo, kv, group, causal, window):
+    P = 16
+    indptr, last = lens_to_table(kv, P)
+    qo_indptr = np.zeros(len(qo) + 1, np.int32)
+    qo_indptr[1:] = np.cumsum(qo)
+    hkv = 2
+    cache = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, int(indptr[-1]) + 1, hkv, P, 512)
+    plan, buf = pa.pa_prefill_plan(params(hq=hkv * group, window=window, causal=int(causal)),
+                                   cache, qo_indptr, indptr, last)
+    items = pa.prefill_items(plan, buf)
+    ref = prefill_tiles_ref(qo, kv, group, plan.tile_rows, causal, window)
+    assert [tuple(r[:5]) for r in items.tolist()] == [tuple(r) for r in ref]
+    for r in items:
+        b = r[0]
+        assert (r[5], r[6], r[7]) == (qo_indptr[b], kv[b], qo[b])
+    assert plan.total_q == sum(qo)
+
+
+# ----------------------------------------------------------------------------- error paths
+
+def decode_plan_status(lens=(37, 64), P=16, hq=8, hkv=1, dim=512, dvo=None, splits=1,
+                       kv_dtype=pa.PA_DTYPE_BF16, indptr=None, last=None, scale=(1.0, 1.0)):
+    ip, la = lens_to_table(list(lens), P)
+    ip = ip if indptr is None else np.asarray(indptr, np.int32)
+    la = la if last is None else np.asarray(last, np.int32)
+    c = pa.pa_kv_cache()
+    c.k, c.v, c.kv_dtype, c.num_pages, c.num_kv_heads, c.page_size = 0, 0, kv_dtype, 100, hkv, P
+    c.head_dim_qk, c.head_dim_vo = dim, dim if dvo is None else dvo
+    c.k_stride_token = c.v_stride_token = dim
+    c.k_stride_head = c.v_stride_head = P * dim
+    c.k_stride_page = c.v_stride_page = 2 * hkv * P * dim
+    c.k_scale, c.v_scale = scale
+    try:
+        pa.pa_decode_plan(params(hq=hq), c, ip, la, splits)
+        return pa.PA_OK
+    except pa.PaError as e:
+        assert e.message  # every failure names its cause
+        return e.status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), pa.PA_OK),
+    (dict(indptr=[0, 3, 2], last=[5, 16]), pa.PA_ERR_INVALID_ARG),       # decreasing indptr
+    (dict(indptr=[1, 3, 7], last=[5, 16]), pa.PA_ERR_INVALID_ARG),       # indptr[0] != 0
+    (dict(last=[0, 16]), pa.PA_ERR_INVALID_ARG),                         # last page empty
+    (dict(last=[5, 17]), pa.PA_ERR_INVALID_ARG),                         # last page > P
+    (dict(hq=6, hkv=4), pa.PA_ERR_INVALID_ARG),                          # Hq % Hkv != 0
+    (dict(hq=18, hkv=2), pa.PA_ERR_UNSUPPORTED),                         # group 9 > 8
+    (dict(hq=16, hkv=2), pa.PA_OK),                                      # group 8: control
+    (dict(dim=128), pa.PA_ERR_UNSUPPORTED),                              # head_dim 128
+    (dict(dim=256, dvo=512), pa.PA_ERR_UNSUPPORTED),                     # (256, 512)
+    (dict(dim=512, dvo=256), pa.PA_OK),                                  # (512, 256): control
+    (dict(kv_dtype=pa.PA_DTYPE_FP32), pa.PA_ERR_UNSUPPORTED),            # fp32 KV
+    (dict(kv_dtype=pa.PA_DTYPE_FP8_E4M3FN, scale=(0.5, 2.0)), pa.PA_OK), # fp8: control
+    (dict(scale=(0.5, 1.0)), pa.PA_ERR_INVALID_ARG),                     # bf16 with a scale
+    (dict(kv_dtype=pa.PA_DTYPE_FP8_E4M3FN, scale=(0.0, 1.0)), pa.PA_ERR_INVALID_ARG),
+    (dict(splits=65), pa.PA_ERR_UNSUPPORTED),
+    (dict(splits=-1), pa.PA_ERR_UNSUPPORTED),
+    (dict(splits=64), pa.PA_OK),
+])
+def test_decode_plan_rejects_bad_input_with_positive_controls(kw, status):
+    assert decode_plan_status(**kw) == status
+
+
+def test_misaligned_strides_are_rejected_and_aligned_padding_is_accepted():
+    c = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, 10, 2, 16, 512)
+    c.v_stride_token = 520  # 1040 bytes: padded rows, still 16-byte aligned
+    pa.pa_decode_plan(params(hq=2), c, *lens_to_table([20], 16), 1)
+    c.v_stride_token = 516  # 1032 bytes: breaks 16-byte alignment
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode_plan(params(hq=2), c, *lens_to_table([20], 16), 1)
+    assert e.value.status == pa.PA_ERR_UNSUPPORTED and "v_stride_token" in e.value.message
+
+
+def test_prefill_rejects_more_new_tokens_than_keys_and_fp8():
+    P = 16
+    ip, la = lens_to_table([10], P)
+    c = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, 10, 2, P, 512)
+    pa.pa_prefill_plan(params(hq=4), c, [0, 10], ip, la)  # control: q_len == kv_len
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_prefill_plan(params(hq=4), c, [0, 11], ip, la)
+    assert e.value.status == pa.PA_ERR_INVALID_ARG
+    c8 = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_FP8_E4M3FN, 10, 2, P, 512, 1.0, 1.0)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_prefill_plan(params(hq=4), c8, [0, 10], ip, la)
+    assert e.value.status == pa.PA_ERR_UNSUPPORTED
+
+
+def test_plan_buffer_too_small_is_rejected():
+    ip, la = lens_to_table([100, 200], 16)
+    c = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, 20, 1, 16, 512)
+    p = params(hq=8)
+    plan = pa.pa_plan()
+    lib = pa.lib()
+    ipa, ipp = pa._i32(ip)
+    laa, lap = pa._i32(la)
+    assert lib.pa_decode_plan(ctypes.byref(p), ctypes.byref(c), ipp, lap, 2, 2, None, 0,
+                              ctypes.byref(plan)) == pa.PA_OK
+    small = np.zeros(plan.plan_bytes - 1, np.uint8)
+    st = lib.pa_decode_plan(ctypes.byref(p), ctypes.byref(c), ipp, lap, 2, 2,
+                            small.ctypes.data_as(ctypes.c_void_p), small.nbytes,
+                            ctypes.byref(plan))
+    assert st == pa.PA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_validate_page_table_host():
+    pa.pa_validate_page_table_host([0, 2, 3], [4, 1, 0], [5, 16], 5, 16)
+    with pytest.raises(pa.PaError):
+        pa.pa_validate_page_table_host([0, 2, 3], [4, 5, 0], [5, 16], 5, 16)  # index 5 >= 5
+    with pytest.raises(pa.PaError):
+        pa.pa_validate_page_table_host([0, 2, 3], [4, -1, 0], [5, 16], 5, 16)
+
+
+def test_run_calls_refuse_a_plan_made_for_other_sizes():
+    """Forced from the host: the check fails before anything reaches HIP."""
+    ip, la = lens_to_table([37, 64], 16)
+    c = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, 10, 1, 16, 512)
+    p = params(hq=8)
+    plan, buf = pa.pa_decode_plan(p, c, ip, la, 2)
+    table = pa.pa_page_table(0x1000, 0x2000, 0x3000, 2)
+    p_other = params(hq=8, window=4)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_paged_decode(plan, 0x4000, c, table, p_other, 0x5000, None, 0x6000, 1 << 20)
+    assert e.value.status == pa.PA_ERR_INVALID_ARG
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_paged_decode(plan, 0x4000, c, table, p, 0x5000, None, 0x6000, 16)
+    assert e.value.status == pa.PA_ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_paged_decode(plan, 0x4001, c, table, p, 0x5000, None, 0x6000, 1 << 20)
+    assert e.value.status == pa.PA_ERR_UNSUPPORTED  # misaligned q
