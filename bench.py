@@ -1,0 +1,413 @@
+"""Benchmark of paged GQA attention at head_dim 512 on one MI355X.
+
+Prints ONE JSON line.  The headline is paged decode HBM throughput on the GQA decode
+workload (batch 32, 24 query / 4 KV heads, head_dim 512, page size 16, KV lengths
+uniform in [1024, 8192], split-K 8, bf16): ``value`` is algorithmic bytes per step divided
+by the measured step time, with the inputs resident in HBM.  A step is one pass of the
+decode hot path: the split-K partial kernel and the log-sum-exp merge kernel (the plan is
+host work, made and uploaded once before timing).  The other workloads (FP8 decode,
+sliding-window decode, causal prefill) are reported under ``secondary``.
+
+Algorithmic work:
+  decode bytes  = sum_b Hkv * |visible keys_b| * (Dqk + Dvo) * bytes_per_kv_element
+                  + Q bytes + output bytes + 4 * (pages touched) + 4 * (2B + 1)
+  prefill flops = sum_b sum_i Hq * |visible keys of row i| * 2 * (Dqk + Dvo)
+Both are counted from the realised seeded lengths.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-secondary] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "paged decode attn HBM GB/s (% peak) at hd512 GQA; prefill TFLOP/s"
+KERNEL_SOURCES = ["paged_attention_hd512_amd/csrc/pa_decode.hip",
+                  "paged_attention_hd512_amd/csrc/pa_prefill.hip",
+                  "paged_attention_hd512_amd/csrc/pa_device.hpp"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------- work counts
+
+def decode_algorithmic_bytes(case, requests=None):
+    import numpy as np
+    reqs = range(case.batch) if requests is None else requests
+    esz = 1 if case.kv_dtype == "fp8" else 2
+    out_sz = 4 if case.out_dtype == "fp32" else 2
+    total = 0
+    for b in reqs:
+        L = int(case.kv_lens[b])
+        start = max(0, L - case.window) if case.window > 0 else 0
+        vis = L - start
+        pages = 0 if vis == 0 else (L - 1) // case.page_size - start // case.page_size + 1
+        total += case.num_kv_heads * vis * (case.head_dim_qk + case.head_dim_vo) * esz
+        total += case.num_qo_heads * (case.head_dim_qk * 2 + case.head_dim_vo * out_sz)
+        total += 4 * pages
+    total += 4 * (2 * len(list(reqs)) + 1)
+    return int(total)
+
+
+def prefill_algorithmic_flops(case, requests=None):
+    reqs = range(case.batch) if requests is None else requests
+    total = 0
+    for b in reqs:
+        q_len, L = int(case.qo_lens[b]), int(case.kv_lens[b])
+        for i in range(q_len):
+            pos = L - q_len + i
+            hi = pos + 1 if case.causal else L
+            lo = max(0, pos - case.window + 1) if case.window > 0 else 0
+            total += case.num_qo_heads * max(0, hi - lo) * 2 * (case.head_dim_qk + case.head_dim_vo)
+    return int(total)
+
+
+# ----------------------------------------------------------------------------- timing
+
+def time_decode(case, steps, warmup):
+    """Returns (ms_per_step, partial_kernel_ms, merge_ms) measured with HIP events on the
+    stream the kernels run on."""
+    import torch
+    from paged_attention_hd512_amd import PagedDecode
+    import paged_attention_hd512_amd.pa as pa
+
+    run = PagedDecode(case.k_pool, case.v_pool, case.kv_indptr, case.kv_indices,
+                      case.kv_last_page_len, case.num_qo_heads, kv_dtype=case.kv_dtype,
+                      k_scale=case.k_scale, v_scale=case.v_scale, sm_scale=case.sm_scale,
+                      window=case.window, num_splits=case.num_splits, out_dtype=case.out_dtype)
+    out, lse = run.run(case.q)
+    stream = torch.cuda.current_stream()
+    sh = pa.current_stream_handle()
+    args = (run.plan, case.q.data_ptr(), run.cache, run.table, run.params, out.data_ptr(),
+            lse.data_ptr(), run.workspace.data_ptr(), run.workspace.numel(), sh)
+    for _ in range(warmup):
+        pa.pa_paged_decode(*args)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        pa.pa_paged_decode_partial(*args)
+        ev[i][1].record(stream)
+        pa.pa_paged_decode_merge(*args)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    part = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    merge = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    step = ev[0][0].elapsed_time(ev[-1][2]) / steps
+    return max(step, 1e-9), part, merge, wall, run.plan
+
+
+def time_prefill(case, steps, warmup):
+    import torch
+    from paged_attention_hd512_amd import PagedPrefill
+    import paged_attention_hd512_amd.pa as pa
+
+    run = PagedPrefill(case.k_pool, case.v_pool, case.qo_indptr, case.kv_indptr,
+                       case.kv_indices, case.kv_last_page_len, case.num_qo_heads,
+                       kv_dtype=case.kv_dtype, sm_scale=case.sm_scale, window=case.window,
+                       causal=case.causal, out_dtype=case.out_dtype)
+    out, lse = run.run(case.q)
+    stream = torch.cuda.current_stream()
+    sh = pa.current_stream_handle()
+    args = (run.plan, case.q.data_ptr(), run.qo_indptr_d.data_ptr(), run.cache, run.table,
+            run.params, out.data_ptr(), lse.data_ptr(), run.workspace.data_ptr(),
+            run.workspace.numel(), sh)
+    for _ in range(warmup):
+        pa.pa_paged_prefill(*args)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        pa.pa_paged_prefill(*args)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    kern = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    step = ev[0][0].elapsed_time(ev[-1][1]) / steps
+    return step, kern, wall, run.plan
+
+
+# ----------------------------------------------------------------------------- cpu baseline
+
+def cpu_threads():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_decode_baseline(case, budget_s=12.0):
+    """The oracle, as it stands, timed on requests of the same batch until the budget is
+    spent; throughput in algorithmic GB/s of the requests it finished."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from synth import extract_requests
+
+    threads = cpu_threads()
+    done, spent, nbytes = [], 0.0, 0
+    order = list(range(case.batch))
+    with threadpool_limits(limits=threads):
+        for b in order:
+            sub = extract_requests(case, [b])
+            dt = torch.int16 if case.kv_dtype == "bf16" else torch.uint8
+            kp = sub["k_pool"].contiguous().view(dt).numpy()
+            vp = sub["v_pool"].contiguous().view(dt).numpy()
+            if case.kv_dtype == "bf16":
+                kp, vp = kp.view(np.uint16), vp.view(np.uint16)
+            q = oracle.bf16_bits_to_f64(sub["q"].contiguous().view(torch.int16).numpy().view(np.uint16))
+            t0 = time.perf_counter()
+            oracle.decode_ref(q, kp, vp, sub["kv_indptr"], sub["kv_indices"],
+                              sub["kv_last_page_len"], case.page_size, case.sm_scale,
+                              window=case.window, kv_dtype=case.kv_dtype,
+                              k_scale=case.k_scale, v_scale=case.v_scale)
+            spent += time.perf_counter() - t0
+            done.append(b)
+            if spent >= budget_s:
+                break
+    nbytes = decode_algorithmic_bytes(case, done)
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(done)} of {case.batch} requests of the same batch "
+                      f"({sum(int(case.kv_lens[b]) for b in done)} keys), fp64 numpy on "
+                      f"{cpu_model()}, {spent:.1f} s"}
+
+
+def oracle_prefill_baseline(case, budget_s=12.0):
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+    import oracle
+
+    threads = cpu_threads()
+    dt = torch.int16
+    kp = case.k_pool.contiguous().cpu().view(dt).numpy().view(np.uint16)
+    vp = case.v_pool.contiguous().cpu().view(dt).numpy().view(np.uint16)
+    q = oracle.bf16_bits_to_f64(case.q.contiguous().cpu().view(dt).numpy().view(np.uint16))
+    flops, spent, rows = 0, 0.0, 0
+    with threadpool_limits(limits=threads):
+        # Rows of request 0 in chunks of 64 tokens, last (longest) rows first.
+        q_len = int(case.qo_lens[0])
+        for end in range(q_len, 0, -64):
+            toks = np.arange(max(0, end - 64), end)
+            t0 = time.perf_counter()
+            oracle.prefill_ref(q, case.qo_indptr, kp, vp, case.kv_indptr, case.kv_indices,
+                               case.kv_last_page_len, case.page_size, case.sm_scale,
+                               causal=case.causal, window=case.window, tokens=toks)
+            spent += time.perf_counter() - t0
+            L = int(case.kv_lens[0])
+            for i in toks:
+                pos = L - q_len + int(i)
+                flops += case.num_qo_heads * (pos + 1) * 2 * (case.head_dim_qk + case.head_dim_vo)
+            rows += len(toks)
+            if spent >= budget_s:
+                break
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows} of {int(case.qo_lens.sum())} query tokens (all heads) of "
+                      f"request 0, fp64 numpy on {cpu_model()}, {spent:.1f} s"}
+
+
+# ----------------------------------------------------------------------------- counters
+
+def traffic_for(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(workload)
+    if not ent or ent.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def decode_config(case):
+    return {"workload": case.name, "batch": case.batch, "num_qo_heads": case.num_qo_heads,
+            "num_kv_heads": case.num_kv_heads, "head_dim_qk": case.head_dim_qk,
+            "head_dim_vo": case.head_dim_vo, "page_size": case.page_size,
+            "kv_dtype": case.kv_dtype, "window": case.window, "num_splits": case.num_splits,
+            "kv_len_min": int(case.kv_lens.min()), "kv_len_max": int(case.kv_lens.max()),
+            "kv_len_mean": float(case.kv_lens.mean()), "out_dtype": case.out_dtype}
+
+
+def measure_decode(name, steps, warmup, variant=None):
+    import torch
+    from synth import decode_workload
+    case = decode_workload(name, device="cuda", variant=variant)
+    if variant is not None:
+        case.name = f"{name}_d{variant[0]}_p{variant[1]}"
+    step_ms, part_ms, merge_ms, wall_ms, plan = time_decode(case, steps, warmup)
+    nbytes = decode_algorithmic_bytes(case)
+    achieved = nbytes / (part_ms * 1e-3) / 1e9
+    res = {
+        "case": case, "bytes": nbytes, "step_ms": step_ms, "wall_ms": wall_ms,
+        "kernel_ms": part_ms, "merge_ms": merge_ms,
+        "value": nbytes / (step_ms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for(case.name), "kernel": "decode_partial_kernel",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "kernel_avg_ms": round(part_ms, 5)},
+        "plan": {"items": plan.num_items, "workgroups": plan.num_items * case.num_kv_heads,
+                 "merges": plan.num_merges, "chunk_blocks": plan.chunk_blocks},
+    }
+    return res
+
+
+def measure_prefill(name, steps, warmup, head_dim_vo):
+    from synth import prefill_workload
+    case = prefill_workload(name, device="cuda", head_dim_vo=head_dim_vo)
+    case.name = f"{name}_qk512_vo{head_dim_vo}"
+    step_ms, kern_ms, wall_ms, plan = time_prefill(case, steps, warmup)
+    flops = prefill_algorithmic_flops(case)
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    return {
+        "case": case, "flops": flops, "step_ms": step_ms, "wall_ms": wall_ms,
+        "kernel_ms": kern_ms, "value": flops / (step_ms * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": traffic_for(case.name), "kernel": "prefill_kernel",
+                     "algorithmic_flops_per_launch": flops, "kernel_avg_ms": round(kern_ms, 5)},
+    }
+
+
+def copy_calibration(nbytes=1 << 30, steps=5):
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "steps": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa_decode",
+                    help="gqa_decode | fp8_decode | window_decode_d512_p1 | ... | "
+                         "causal_prefill_vo512 | causal_prefill_vo256")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    def run_named(wl):
+        if wl.startswith("window_decode_d"):
+            d, p = wl[len("window_decode_d"):].split("_p")
+            return measure_decode("window_decode", args.steps, args.warmup, (int(d), int(p)))
+        if wl.startswith("causal_prefill_vo"):
+            return measure_prefill("causal_prefill", args.steps, args.warmup,
+                                   int(wl[len("causal_prefill_vo"):]))
+        return measure_decode(wl, args.steps, args.warmup)
+
+    main_res = run_named(args.workload)
+    case = main_res["case"]
+    is_prefill = "flops" in main_res
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["value"], 3),
+        "unit": "TFLOP/s" if is_prefill else "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(main_res["step_ms"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if case.kv_dtype == "bf16" else "fp8-kv/bf16",
+        "data": "synthetic",
+        "config": decode_config(case) if not is_prefill else {
+            "workload": case.name, "batch": case.batch, "qo_len": int(case.qo_lens[0]),
+            "kv_len": int(case.kv_lens[0]), "num_qo_heads": case.num_qo_heads,
+            "num_kv_heads": case.num_kv_heads, "head_dim_qk": case.head_dim_qk,
+            "head_dim_vo": case.head_dim_vo, "page_size": case.page_size, "causal": True},
+        "roofline": main_res["roofline"],
+        "wall_ms_per_step": round(main_res["wall_ms"], 5),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not is_prefill:
+        line["merge_ms"] = round(main_res["merge_ms"], 5)
+        line["plan"] = main_res["plan"]
+    if not args.no_cpu_baseline:
+        if is_prefill:
+            line["cpu_baseline"] = oracle_prefill_baseline(case)
+        else:
+            line["cpu_baseline"] = oracle_decode_baseline(case)
+    del main_res, case
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        sec = {}
+        names = ["gqa_decode", "fp8_decode", "window_decode_d512_p1", "window_decode_d512_p32",
+                 "window_decode_d256_p1", "window_decode_d256_p32", "causal_prefill_vo512",
+                 "causal_prefill_vo256"]
+        for wl in names:
+            if wl == args.workload:
+                continue
+            try:
+                r = run_named(wl)
+            except Exception as e:  # report, keep measuring the rest
+                sec[wl] = {"error": f"{type(e).__name__}: {e}"}
+                continue
+            unit = "TFLOP/s" if "flops" in r else "GB/s"
+            sec[wl] = {"value": round(r["value"], 3), "unit": unit,
+                       "ms_per_step": round(r["step_ms"], 5), "roofline": r["roofline"]}
+            del r
+            torch.cuda.empty_cache()
+        line["secondary"] = sec
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

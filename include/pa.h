@@ -201,6 +201,20 @@ pa_status pa_paged_decode(const pa_plan* plan, const void* q, const pa_kv_cache*
                           void* out, float* lse, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* The two phases of pa_paged_decode as separate calls, with the same arguments and
+ * checks, for callers that schedule or time them apart: _partial launches the split-K
+ * kernel (requests with a single chunk get their final out/lse from it), _merge launches
+ * the log-sum-exp merge of the split requests (nothing when the plan split none).  Calling
+ * _partial then _merge on one stream equals pa_paged_decode. */
+pa_status pa_paged_decode_partial(const pa_plan* plan, const void* q, const pa_kv_cache* cache,
+                                  const pa_page_table* table, const pa_attn_params* params,
+                                  void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+pa_status pa_paged_decode_merge(const pa_plan* plan, const void* q, const pa_kv_cache* cache,
+                                const pa_page_table* table, const pa_attn_params* params,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Enqueues one prefill: q [total_q, num_qo_heads, head_dim_qk] bf16 (contiguous, ragged
  * by qo_indptr) -> out [total_q, num_qo_heads, head_dim_vo] in params->out_dtype and
  * optional lse [total_q, num_qo_heads] fp32.  qo_indptr is the device copy of the array

@@ -502,10 +502,10 @@ pa_status pa_plan_upload(const pa_plan* plan, const void* plan_buf_host, void* w
   return PA_OK;
 }
 
-pa_status pa_paged_decode(const pa_plan* plan, const void* q, const pa_kv_cache* cache,
-                          const pa_page_table* table, const pa_attn_params* params,
-                          void* out, float* lse, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_cache* cache,
+                                const pa_page_table* table, const pa_attn_params* params,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream, bool run_partial, bool run_merge) {
   pa_status st = check_cache(cache, true);
   if (st != PA_OK) return st;
   if ((st = check_params(params, cache, kMaxDecodeGroup)) != PA_OK) return st;
@@ -520,49 +520,78 @@ pa_status pa_paged_decode(const pa_plan* plan, const void* q, const pa_kv_cache*
   const int group = params->num_qo_heads / cache->num_kv_heads;
   const int gmax = group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8;
   char* ws = (char*)workspace;
-  DecodeArgs a;
-  a.q = (const uint16_t*)q;
-  a.k = (const char*)cache->k;
-  a.v = (const char*)cache->v;
-  a.k_sp = cache->k_stride_page; a.k_sh = cache->k_stride_head; a.k_st = cache->k_stride_token;
-  a.v_sp = cache->v_stride_page; a.v_sh = cache->v_stride_head; a.v_st = cache->v_stride_token;
-  a.kv_indptr = table->kv_indptr;
-  a.kv_indices = table->kv_indices;
-  a.items = (const DecodeItem*)(ws + plan->items_offset);
-  a.out = out;
-  a.lse = lse;
-  a.part_o = (float*)(ws + plan->partial_o_offset);
-  a.part_lse = (float*)(ws + plan->partial_lse_offset);
-  a.num_qo_heads = params->num_qo_heads;
-  a.num_kv_heads = cache->num_kv_heads;
-  a.group = group;
-  a.page_size = cache->page_size;
-  a.out_fp32 = params->out_dtype == PA_DTYPE_FP32;
-  a.scale_log2 = params->sm_scale * cache->k_scale * kLog2e;
-  a.v_scale = cache->v_scale;
-  const int kvb = cache->kv_dtype == PA_DTYPE_FP8_E4M3FN ? 1 : 2;
-  const int grid = plan->num_items * cache->num_kv_heads;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_decode(a, cache->head_dim_qk, cache->head_dim_vo, kvb, gmax, grid, s);
-  if (e != hipSuccess) return fail(PA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
-  count_launches(1);
-  if (plan->num_merges > 0) {
+  const bool out_fp32 = params->out_dtype == PA_DTYPE_FP32;
+  float* part_o = (float*)(ws + plan->partial_o_offset);
+  float* part_lse = (float*)(ws + plan->partial_lse_offset);
+  if (run_partial) {
+    DecodeArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const char*)cache->k;
+    a.v = (const char*)cache->v;
+    a.k_sp = cache->k_stride_page; a.k_sh = cache->k_stride_head; a.k_st = cache->k_stride_token;
+    a.v_sp = cache->v_stride_page; a.v_sh = cache->v_stride_head; a.v_st = cache->v_stride_token;
+    a.kv_indptr = table->kv_indptr;
+    a.kv_indices = table->kv_indices;
+    a.items = (const DecodeItem*)(ws + plan->items_offset);
+    a.out = out;
+    a.lse = lse;
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    a.num_qo_heads = params->num_qo_heads;
+    a.num_kv_heads = cache->num_kv_heads;
+    a.group = group;
+    a.page_size = cache->page_size;
+    a.out_fp32 = out_fp32;
+    a.scale_log2 = params->sm_scale * cache->k_scale * kLog2e;
+    a.v_scale = cache->v_scale;
+    const int kvb = cache->kv_dtype == PA_DTYPE_FP8_E4M3FN ? 1 : 2;
+    const int grid = plan->num_items * cache->num_kv_heads;
+    hipError_t e = launch_decode(a, cache->head_dim_qk, cache->head_dim_vo, kvb, gmax, grid, s);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
+    count_launches(1);
+  }
+  if (run_merge && plan->num_merges > 0) {
     MergeArgs m;
     m.merges = (const MergeItem*)(ws + plan->merges_offset);
-    m.part_o = a.part_o;
-    m.part_lse = a.part_lse;
+    m.part_o = part_o;
+    m.part_lse = part_lse;
     m.out = out;
     m.lse = lse;
     m.num_qo_heads = params->num_qo_heads;
-    m.out_fp32 = a.out_fp32;
+    m.out_fp32 = out_fp32;
     dim3 mg(plan->num_merges, params->num_qo_heads);
     if (cache->head_dim_vo == 512) decode_merge_kernel<512><<<mg, 64, 0, s>>>(m);
     else decode_merge_kernel<256><<<mg, 64, 0, s>>>(m);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
     count_launches(1);
   }
   return PA_OK;
+}
+
+pa_status pa_paged_decode(const pa_plan* plan, const void* q, const pa_kv_cache* cache,
+                          const pa_page_table* table, const pa_attn_params* params,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return decode_enqueue(plan, q, cache, table, params, out, lse, workspace, workspace_bytes,
+                        stream, true, true);
+}
+
+pa_status pa_paged_decode_partial(const pa_plan* plan, const void* q, const pa_kv_cache* cache,
+                                  const pa_page_table* table, const pa_attn_params* params,
+                                  void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return decode_enqueue(plan, q, cache, table, params, out, lse, workspace, workspace_bytes,
+                        stream, true, false);
+}
+
+pa_status pa_paged_decode_merge(const pa_plan* plan, const void* q, const pa_kv_cache* cache,
+                                const pa_page_table* table, const pa_attn_params* params,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return decode_enqueue(plan, q, cache, table, params, out, lse, workspace, workspace_bytes,
+                        stream, false, true);
 }
 
 pa_status pa_debug_gather_kv(const pa_kv_cache* cache, const pa_page_table* table,

@@ -54,6 +54,15 @@ __device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+// LDS transpose load (ds_read_b64_tr_b16): within each block of 16 lanes, lane i = 4c + e
+// receives element e of the 8-byte rows addressed by lanes c, c+4, c+8 and c+12.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
 // ---------------------------------------------------------------- paged address path
 //
 // Logical token t of a request whose page list starts at `pages` is slot t % P of page

@@ -1,8 +1,296 @@
-// Paged prefill for gfx950 (placeholder until the MFMA kernel lands).
+// Paged causal prefill for gfx950 on bf16 MFMA (fp32 accumulation).
+//
+// What is computed ("[None][feat] Run Gemma4 head_dim 512 attention on Triton",
+// TensorRT-LLM pull request 17772, section "Approach": causal attention when no custom mask
+// is given over FlashInfer's HND paged layout; section "Not covered": the current tokens
+// versus the cached prefix): the q_len new tokens of a request are its last keys, row i
+// sits at position L - q_len + i and attends keys t <= position (and t > position - W with
+// a sliding window).  head_dim_qk = 512 with head_dim_vo = 256 reads V from its own pool
+// ("feat(attention): asymmetric VO-split NVFP4 paged prefill (qk=512/vo=256) for Gemma-4
+// on SM120/121", FlashInfer pull request 3684, section "Summary").
+//
+// Work decomposition.  A tile is 128 query rows of one (request, KV head): the (token,
+// head) pairs of the head group, flattened token-major, so the G heads that share a KV
+// head share every K/V tile.  One workgroup of 4 waves runs a tile; each wave owns 32 rows.
+// Keys stream through LDS in tiles of 32 (K and V rows staged from their pages).  Per key
+// tile and wave, with v_mfma_f32_32x32x16_bf16:
+//   * S^T = K Q^T (keys on M, the wave's 32 rows on N, head_dim on K): A = K rows from LDS,
+//     B = Q held in registers for the whole tile.  In the output layout every lane holds
+//     16 scores of one query row, so the online softmax of a row lives in one lane pair.
+//   * O^T += V^T P^T (head_dim on M, rows on N, keys on K): B = P straight from the score
+//     registers (same lane, same key order), A = V read transposed from LDS.  The O^T
+//     accumulators of a lane again all belong to its own row.
+//   * The running max is only moved when a row's max grows by more than 2^8, so the
+//     accumulators are rescaled rarely; the final normalisation uses the same reference
+//     max, so the result is unchanged.
+
 #include <hip/hip_runtime.h>
+
+#include <math.h>
 
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
+
+namespace pa {
+
+constexpr int kPrefillWaves = 8;          // 16 query rows each: 128 rows per tile
+constexpr int kKeyTile = 32;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+
+struct PrefillArgs {
+  const uint16_t* q;          // [total_q, Hq, DQK] bf16
+  const char* k;
+  const char* v;
+  int64_t k_sp, k_sh, k_st;
+  int64_t v_sp, v_sh, v_st;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const PrefillItem* items;
+  void* out;                  // [total_q, Hq, DVO]
+  float* lse;                 // [total_q, Hq] or null
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t page_size;
+  int32_t window;             // 0 = none
+  int32_t causal;
+  int32_t out_fp32;
+  float scale_log2;
+};
+
+// LDS tiles hold key rows unpadded; 16-byte chunk c of row r sits at chunk position
+// c ^ swz(r).  The K swizzle spreads the 16 rows a K-operand read touches over all banks;
+// the V swizzle (even values, so 32-byte pairs stay together) spreads the 4 key rows of a
+// transpose read and its neighbouring lane block.
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+__device__ __forceinline__ int v_swz(int row) { return 2 * (row & 7); }
+
+// Waits until at most n of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int DQK, int DVO>
+__global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
+  constexpr int NW = kPrefillWaves;
+  constexpr int KT = kKeyTile;
+  constexpr int QSTEPS = DQK / 32;          // MFMA K-steps of S^T
+  constexpr int OT = DVO / 16;              // 16-wide head_dim tiles of O^T
+  constexpr int KCH = DQK / 8;              // 16-byte chunks per K row
+  constexpr int VCH = DVO / 8;
+  constexpr int KRPI = 64 / KCH;            // K rows per copy instruction (1 or 2)
+  constexpr int VRPI = 64 / VCH;
+  constexpr int KCOPIES = KT / KRPI / NW;   // copy instructions per wave per tile
+  constexpr int VCOPIES = KT / VRPI / NW;
+  constexpr int COPIES = KCOPIES + VCOPIES;
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * DQK];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][KT * DVO];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4;   // k-slot group of the MFMA operands
+  const int n = lane & 15;    // this lane's query row within the wave (and operand row)
+  const int hkv = a.num_kv_heads;
+  const int kvh = blockIdx.x % hkv;
+  const PrefillItem it = a.items[blockIdx.x / hkv];
+  const int G = a.group;
+  const int32_t* __restrict__ pages = a.kv_indices + a.kv_indptr[it.b];
+
+  // This lane's query row: (token, head) pair r of the group.
+  const int r = it.row_begin + 16 * w + n;
+  const bool row_valid = r < it.row_end;
+  const int tok = row_valid ? r / G : 0;
+  const int head = kvh * G + (row_valid ? r % G : 0);
+  const int pos = it.kv_len - it.q_len + tok;
+  const int64_t q_row = (int64_t)(it.q_begin + tok) * a.num_qo_heads + head;
+
+  const int kv_lo = it.kv_begin, kv_hi = it.kv_end;
+  const int tile_first = kv_lo / KT;
+  const int tile_end = (kv_hi + KT - 1) / KT;
+  const int64_t k_head = (int64_t)kvh * a.k_sh;
+  const int64_t v_head = (int64_t)kvh * a.v_sh;
+
+  // Copies key tile `tile` into buffer `buf`: each instruction moves KRPI (or VRPI) whole
+  // rows straight from the pages into LDS; lane L fills chunk position L of its row with
+  // the logical chunk that the swizzle puts there.
+  auto copy_tile = [&](int tile, int buf) {
+    const int t0 = tile * KT;
+#pragma unroll
+    for (int c = 0; c < KCOPIES; ++c) {
+      const int row0 = (w * KCOPIES + c) * KRPI;
+      const int row = row0 + lane / KCH;
+      int t = t0 + row;
+      t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
+      int32_t page, slot;
+      token_page_slot(pages, t, a.page_size, page, slot);
+      const int chunk = (lane % KCH) ^ k_swz(row);
+      const char* src = a.k + (row_elem_offset(page, 0, slot, a.k_sp, 0, a.k_st) + k_head) * 2 + 16 * chunk;
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (__attribute__((address_space(3))) void*)(&k_lds[buf][row0 * DQK]),
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < VCOPIES; ++c) {
+      const int row0 = (w * VCOPIES + c) * VRPI;
+      const int row = row0 + lane / VCH;
+      int t = t0 + row;
+      t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
+      int32_t page, slot;
+      token_page_slot(pages, t, a.page_size, page, slot);
+      const int chunk = (lane % VCH) ^ v_swz(row);
+      const char* src = a.v + (row_elem_offset(page, 0, slot, a.v_sp, 0, a.v_st) + v_head) * 2 + 16 * chunk;
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (__attribute__((address_space(3))) void*)(&v_lds[buf][row0 * DVO]),
+                                       16, 0, 0);
+    }
+  };
+
+  if (tile_first < tile_end) copy_tile(tile_first, 0);
+
+  // Q^T operand for the whole tile: step j holds dims 32j + 8*g4 .. +7 of row n.
+  u32x4_t qf[QSTEPS];
+  {
+    const uint16_t* src = a.q + q_row * DQK + 8 * g4;
+#pragma unroll
+    for (int j = 0; j < QSTEPS; ++j)
+      qf[j] = row_valid ? *(const u32x4_t*)(src + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+
+  f32x4_t o[OT];
+#pragma unroll
+  for (int t = 0; t < OT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;  // reference max of row n (log2 domain)
+  float l_run = 0.f;        // this lane's share of the row sum
+
+  // Transpose-read source of this lane within its 16-lane block: key (n / 4) of the 4-key
+  // group, dims 4*(n % 4) .. +3 of the 16-dim tile.
+  const int tr_row = n >> 2;
+  const int tr_half = (n & 3) >> 1;         // which 16-byte chunk of the 32-byte pair
+  const int tr_off = 4 * (n & 1);           // element offset inside that chunk
+
+  int buf = 0;
+  for (int tile = tile_first; tile < tile_end; ++tile, buf ^= 1) {
+    const int t0 = tile * KT;
+    if (tile + 1 < tile_end) {
+      copy_tile(tile + 1, buf ^ 1);
+      wait_vmcnt<COPIES>();  // this tile's copies have landed; the next tile's may fly
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+
+    const uint16_t* kt = k_lds[buf];
+    const uint16_t* vt = v_lds[buf];
+    // ---- S^T = K Q^T for keys 0..15 (s0) and 16..31 (s1); lane holds keys 4*g4 + i.
+    // Chunk 4j + g4 of row n (or 16 + n) sits at 4*(j ^ (n>>2)) + (g4 ^ (n&3)): four
+    // per-lane bases (one per j % 4) plus compile-time offsets cover every step.
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint16_t* kb = kt + n * DQK + 8 * (g4 ^ (n & 3));
+#pragma unroll
+      for (int jl = 0; jl < 4; ++jl) {
+        const uint16_t* kbl = kb + 32 * (jl ^ (n >> 2));
+#pragma unroll
+        for (int jh = 0; jh < QSTEPS / 4; ++jh) {
+          const int j = 4 * jh + jl;
+          const u32x4_t k0 = *(const u32x4_t*)(kbl + 128 * jh);
+          const u32x4_t k1 = *(const u32x4_t*)(kbl + 128 * jh + 16 * DQK);
+          const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, qf[j]);
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k0), qb, s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k1), qb, s1, 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- masks and online softmax of row n (its 32 keys are spread over the 4 lanes g4).
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = i < 4 ? s0[i] : s1[i - 4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = t0 + 16 * (i >> 2) + 4 * g4 + (i & 3);
+      bool ok = row_valid && t >= kv_lo && t < kv_hi;
+      if (a.causal) ok = ok && t <= pos;
+      if (a.window > 0) ok = ok && t > pos - a.window;
+      sv[i] = ok ? sv[i] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sv[i]);
+    }
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    // Move the reference max only when the row max outgrows it by the threshold.
+    const bool grow = mx > m_ref + kRescaleThreshold || (m_ref == -INFINITY && mx != -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mx : m_ref;
+      const float alpha = grow ? (m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new)) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < OT; ++t) o[t] *= alpha;
+      m_ref = m_new;
+    }
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    // P^T operand: k-slot e of lane group g4 is key 4*g4 + e (e < 4) or 16 + 4*g4 + e - 4.
+    u32x4_t pf;
+    {
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = exp2f(sv[i] - m_use);
+        l_run += p[i];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pf[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+    }
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pf);
+
+    // ---- O^T += V^T P^T.  A operand of lane (g4, m=n): V[k-slot keys][dim 16t + m], from
+    // two transpose reads (keys 4*g4 + 0..3 and 16 + 4*g4 + 0..3; both rows have the same
+    // swizzle, and the second is 16 rows below the first).  Chunk 2t + half of the row sits
+    // at 2*(t ^ s) + half with s = row & 7: eight per-lane bases plus constant offsets.
+    {
+      const int ra = 4 * g4 + tr_row;
+      const uint16_t* vb = vt + ra * DVO + tr_off + 8 * tr_half;
+#pragma unroll
+      for (int tl = 0; tl < 8; ++tl) {
+        const uint16_t* vbl = vb + 16 * (tl ^ (ra & 7));
+#pragma unroll
+        for (int th = 0; th < OT / 8; ++th) {
+          const int t = 8 * th + tl;
+          const u32x2_t lo = lds_read_tr16(vbl + 128 * th);
+          const u32x2_t hi = lds_read_tr16(vbl + 128 * th + 16 * DVO);
+          const u32x4_t vf = {lo[0], lo[1], hi[0], hi[1]};
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf), pb, o[t], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_barrier();  // every wave is done with this buffer before it is refilled
+  }
+
+  // ---- normalise and write row n: O^T tile t, register i holds dim 16t + 4*g4 + i.
+  float l_tot = l_run + shfl_xor_f(l_run, 16);
+  l_tot += shfl_xor_f(l_tot, 32);
+  if (!row_valid) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int64_t out_row = q_row * DVO;
+#pragma unroll
+  for (int t = 0; t < OT; ++t) {
+    const int d = 16 * t + 4 * g4;
+    const f32x4_t v = o[t] * inv;
+    if (a.out_fp32) {
+      *(f32x4_t*)((float*)a.out + out_row + d) = v;
+    } else {
+      *(u32x2_t*)((uint16_t*)a.out + out_row + d) = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+    }
+  }
+  if (a.lse && g4 == 0)
+    a.lse[q_row] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+}  // namespace pa
 
 using namespace pa;
 
@@ -10,7 +298,45 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
                                       const pa_kv_cache* cache, const pa_page_table* table,
                                       const pa_attn_params* params, void* out, float* lse,
                                       void* workspace, size_t workspace_bytes, void* stream) {
-  (void)plan; (void)q; (void)qo_indptr; (void)cache; (void)table; (void)params; (void)out;
-  (void)lse; (void)workspace; (void)workspace_bytes; (void)stream;
-  return fail(PA_ERR_UNSUPPORTED, "paged prefill is not built yet");
+  pa_status st = check_cache(cache, true);
+  if (st != PA_OK) return st;
+  if (cache->kv_dtype != PA_DTYPE_BF16) return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 KV only");
+  if ((st = check_params(params, cache, kMaxPrefillGroup)) != PA_OK) return st;
+  if ((st = check_plan_matches(plan, 2, params, cache, table, workspace_bytes)) != PA_OK) return st;
+  if (plan->num_items == 0) return PA_OK;
+  if (!q || !out || !qo_indptr) return fail(PA_ERR_INVALID_ARG, "q, qo_indptr or out is NULL");
+  if (!workspace) return fail(PA_ERR_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)workspace) & 15)
+    return fail(PA_ERR_UNSUPPORTED, "q, out and workspace must be 16-byte aligned");
+  if ((uintptr_t)lse & 3) return fail(PA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const char* ws = (const char*)workspace;
+  PrefillArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const char*)cache->k;
+  a.v = (const char*)cache->v;
+  a.k_sp = cache->k_stride_page; a.k_sh = cache->k_stride_head; a.k_st = cache->k_stride_token;
+  a.v_sp = cache->v_stride_page; a.v_sh = cache->v_stride_head; a.v_st = cache->v_stride_token;
+  a.kv_indptr = table->kv_indptr;
+  a.kv_indices = table->kv_indices;
+  a.items = (const PrefillItem*)(ws + plan->items_offset);
+  a.out = out;
+  a.lse = lse;
+  a.num_qo_heads = params->num_qo_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = params->num_qo_heads / cache->num_kv_heads;
+  a.page_size = cache->page_size;
+  a.window = params->window > 0 ? params->window : 0;
+  a.causal = params->causal ? 1 : 0;
+  a.out_fp32 = params->out_dtype == PA_DTYPE_FP32;
+  a.scale_log2 = params->sm_scale * kLog2e;
+  const int grid = plan->num_items * cache->num_kv_heads;
+  hipStream_t s = (hipStream_t)stream;
+  const int dqk = cache->head_dim_qk, dvo = cache->head_dim_vo;
+  if (dqk == 512 && dvo == 512) prefill_kernel<512, 512><<<grid, 512, 0, s>>>(a);
+  else if (dqk == 256 && dvo == 256) prefill_kernel<256, 256><<<grid, 512, 0, s>>>(a);
+  else prefill_kernel<512, 256><<<grid, 512, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
+  count_launches(1);
+  return PA_OK;
 }

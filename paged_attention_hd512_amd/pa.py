@@ -83,6 +83,12 @@ SIGNATURES = {
     "pa_paged_decode": (c_int32, [POINTER(pa_plan), _P, POINTER(pa_kv_cache),
                                   POINTER(pa_page_table), POINTER(pa_attn_params), _P, _P, _P,
                                   c_size_t, _P]),
+    "pa_paged_decode_partial": (c_int32, [POINTER(pa_plan), _P, POINTER(pa_kv_cache),
+                                          POINTER(pa_page_table), POINTER(pa_attn_params), _P,
+                                          _P, _P, c_size_t, _P]),
+    "pa_paged_decode_merge": (c_int32, [POINTER(pa_plan), _P, POINTER(pa_kv_cache),
+                                        POINTER(pa_page_table), POINTER(pa_attn_params), _P, _P,
+                                        _P, c_size_t, _P]),
     "pa_paged_prefill": (c_int32, [POINTER(pa_plan), _P, _P, POINTER(pa_kv_cache),
                                    POINTER(pa_page_table), POINTER(pa_attn_params), _P, _P, _P,
                                    c_size_t, _P]),
@@ -202,6 +208,20 @@ def pa_paged_decode(plan, q, cache, table, params, out, lse, workspace, workspac
     _check(lib().pa_paged_decode(ctypes.byref(plan), q, ctypes.byref(cache), ctypes.byref(table),
                                  ctypes.byref(params), out, lse, workspace, workspace_bytes,
                                  stream))
+
+
+def pa_paged_decode_partial(plan, q, cache, table, params, out, lse, workspace,
+                            workspace_bytes, stream=None):
+    _check(lib().pa_paged_decode_partial(ctypes.byref(plan), q, ctypes.byref(cache),
+                                         ctypes.byref(table), ctypes.byref(params), out, lse,
+                                         workspace, workspace_bytes, stream))
+
+
+def pa_paged_decode_merge(plan, q, cache, table, params, out, lse, workspace, workspace_bytes,
+                          stream=None):
+    _check(lib().pa_paged_decode_merge(ctypes.byref(plan), q, ctypes.byref(cache),
+                                       ctypes.byref(table), ctypes.byref(params), out, lse,
+                                       workspace, workspace_bytes, stream))
 
 
 def pa_paged_prefill(plan, q, qo_indptr, cache, table, params, out, lse, workspace,
