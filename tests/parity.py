@@ -3,6 +3,12 @@
 Tolerances: for bf16 inputs with fp32 accumulation, max-abs error <= 1e-2 and mean-abs
 error <= 1e-3 over every valid output element; lse max-abs <= 1e-3 where finite, and the
 same -inf positions.  FP8 KV is compared with the oracle run on the dequantised codes.
+
+A bf16 output also carries the rounding of the exact result to bf16, up to half an ulp,
+i.e. 2^-8 |ref|; that alone exceeds 1e-2 once |ref| > 2.56 (rows that see few keys).  For
+bf16 outputs the per-element bound is therefore 1e-2 + 2^-8 |ref|, and a separate
+bit-exact test checks that the bf16 output is the round-to-nearest-even of the fp32
+output of the same computation.
 """
 
 import sys
@@ -38,11 +44,12 @@ def out_to_np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def compare(name, got, ref, got_lse=None, ref_lse=None):
+def compare(name, got, ref, got_lse=None, ref_lse=None, out_dtype="fp32"):
     err = np.abs(got - ref)
     max_abs, mean_abs = float(err.max(initial=0.0)), float(err.mean()) if err.size else 0.0
     msg = f"{name}: max_abs={max_abs:.3e} mean_abs={mean_abs:.3e}"
-    ok = max_abs <= MAX_ABS and mean_abs <= MEAN_ABS and np.isfinite(got).all()
+    bound = MAX_ABS + (np.abs(ref) * 2.0 ** -8 if out_dtype == "bf16" else 0.0)
+    ok = bool(np.all(err <= bound)) and mean_abs <= MEAN_ABS and np.isfinite(got).all()
     if got_lse is not None:
         fin = np.isfinite(ref_lse)
         assert np.array_equal(np.isfinite(got_lse), fin), f"{name}: lse -inf pattern differs"
@@ -114,3 +121,10 @@ def gpu_prefill(case, out_dtype=None):
     out, lse = runner.run(case.q)
     torch.cuda.synchronize()
     return runner, out, lse
+
+
+def bf16_rne_bits(x):
+    """Round-to-nearest-even of float32 values to bf16 bit patterns (test-side helper)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)

@@ -7,7 +7,7 @@ import torch
 import oracle
 from synth import make_decode_case, decode_workload
 from parity import (say, compare, oracle_decode, gpu_decode, out_to_np, pool_to_np,
-                    bf16_to_np)
+                    bf16_to_np, bf16_rne_bits)
 import paged_attention_hd512_amd.pa as pa
 
 pytestmark = pytest.mark.gpu
@@ -102,7 +102,7 @@ def test_decode_sweep(lens, hq, hkv, dim, dvo, page, kv_dtype, window, splits, o
                          device=dev())
     _, o, lse = gpu_decode(c)
     ref, ref_lse = oracle_decode(c)
-    compare(name, out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
+    compare(name, out_to_np(o), ref, lse.cpu().numpy(), ref_lse, out_dtype=out)
 
 
 def test_empty_requests_give_zero_output_and_minus_inf_lse():
@@ -149,5 +149,15 @@ def test_full_size_workloads_on_sampled_requests(name, variant):
                      int(np.random.default_rng(0).integers(0, c.batch))})
     ref, ref_lse = oracle_decode(c, requests=sample)
     compare(f"{name} {variant} requests {sample}", out_to_np(o[sample]), ref,
-            lse[sample].cpu().numpy(), ref_lse)
+            lse[sample].cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
     assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_bf16_output_is_the_rounded_fp32_output(splits):
+    say(f"bf16 output = RNE(fp32 output), splits={splits}")
+    c = make_decode_case([37, 64, 500], 24, 4, 512, 16, num_splits=splits, seed=4, device=dev())
+    _, o32, l32 = gpu_decode(c, out_dtype="fp32")
+    _, o16, l16 = gpu_decode(c, out_dtype="bf16")
+    assert np.array_equal(bf16_to_np(o16), bf16_rne_bits(o32.cpu().numpy()))
+    assert torch.equal(l32, l16)

@@ -5,7 +5,8 @@ import pytest
 import torch
 
 from synth import make_prefill_case, prefill_workload
-from parity import say, compare, oracle_prefill, gpu_prefill, out_to_np
+from parity import (say, compare, oracle_prefill, gpu_prefill, out_to_np, bf16_to_np,
+                    bf16_rne_bits)
 import paged_attention_hd512_amd.pa as pa
 
 pytestmark = pytest.mark.gpu
@@ -42,7 +43,7 @@ def test_prefill_sweep(qo, kv, hq, hkv, dqk, dvo, page, causal, window, out):
     _, o, lse = gpu_prefill(c)
     assert pa.pa_launch_count() == before + (1 if sum(qo) > 0 else 0)
     ref, ref_lse = oracle_prefill(c)
-    compare(name, out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
+    compare(name, out_to_np(o), ref, lse.cpu().numpy(), ref_lse, out_dtype=out)
 
 
 def test_prefill_with_one_new_token_equals_decode():
@@ -81,5 +82,14 @@ def test_full_size_causal_prefill_on_sampled_rows(dvo):
     ref, ref_lse = oracle_prefill(c, tokens=toks)
     idx = torch.as_tensor(toks).to(o.device)
     compare(f"prefill vo={dvo} rows {len(toks)}", out_to_np(o.index_select(0, idx)), ref,
-            lse.index_select(0, idx).cpu().numpy(), ref_lse)
+            lse.index_select(0, idx).cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
     assert torch.isfinite(o.float()).all()
+
+
+def test_bf16_output_is_the_rounded_fp32_output():
+    say("prefill bf16 output = RNE(fp32 output)")
+    c = make_prefill_case([130, 64], [300, 64], 16, 8, 512, 64, seed=6, device=dev())
+    _, o32, l32 = gpu_prefill(c, out_dtype="fp32")
+    _, o16, l16 = gpu_prefill(c, out_dtype="bf16")
+    assert np.array_equal(bf16_to_np(o16), bf16_rne_bits(o32.cpu().numpy()))
+    assert torch.equal(l32, l16)
