@@ -21,14 +21,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (inputs here are finite or +-inf).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// Two fp32 -> two bf16 in one dword, round to nearest even (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Four FP8 E4M3FN codes (one dword) -> four fp32 values, exact.  gfx950's conversion
@@ -77,10 +74,42 @@ __device__ __forceinline__ void token_page_slot(const int32_t* __restrict__ page
   slot = t - j * page_size;
 }
 
+// Same, with the division replaced by a shift when page_size = 2^page_shift
+// (page_shift < 0: any page size).
+__device__ __forceinline__ void token_page_slot_fast(const int32_t* __restrict__ pages, int32_t t,
+                                                     int32_t page_size, int32_t page_shift,
+                                                     int32_t& page, int32_t& slot) {
+  if (page_shift >= 0) {
+    page = pages[t >> page_shift];
+    slot = t & (page_size - 1);
+  } else {
+    token_page_slot(pages, t, page_size, page, slot);
+  }
+}
+
 __device__ __forceinline__ int64_t row_elem_offset(int32_t page, int32_t head, int32_t slot,
                                                    int64_t stride_page, int64_t stride_head,
                                                    int64_t stride_token) {
   return (int64_t)page * stride_page + (int64_t)head * stride_head + (int64_t)slot * stride_token;
+}
+
+// Wave-uniform variant: reads the page table through the constant address space, so the
+// index load is a scalar load (it is then counted apart from vector memory operations).
+typedef const int32_t __attribute__((address_space(4))) * const_i32_ptr;
+__device__ __forceinline__ void token_page_slot_uniform(const int32_t* pages, int32_t t,
+                                                        int32_t page_size, int32_t page_shift,
+                                                        int32_t& page, int32_t& slot) {
+  const_i32_ptr cp = (const_i32_ptr)pages;
+  t = __builtin_amdgcn_readfirstlane(t);
+  int32_t j;
+  if (page_shift >= 0) {
+    j = t >> page_shift;
+    slot = t & (page_size - 1);
+  } else {
+    j = t / page_size;
+    slot = t - j * page_size;
+  }
+  page = cp[j];
 }
 
 // ---------------------------------------------------------------- wave primitives
@@ -90,6 +119,25 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Cross-lane max / sum with the lane 32 (or 16) apart, on the VALU: each swap returns, per
+// lane, the lane's own value in one result and its partner's in the other.
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {

@@ -28,20 +28,22 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
 namespace pa {
 
 constexpr int kPrefillWaves = 8;          // 16 query rows each: 128 rows per tile
-constexpr int kKeyTile = 32;
+constexpr int kKeyStage = 32;             // keys per LDS stage (double-buffered)
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 struct PrefillArgs {
   const uint16_t* q;          // [total_q, Hq, DQK] bf16
   const char* k;
   const char* v;
-  int64_t k_sp, k_sh, k_st;
+  int64_t k_sp, k_sh, k_st;   // byte strides (page, head, token)
   int64_t v_sp, v_sh, v_st;
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
@@ -52,42 +54,60 @@ struct PrefillArgs {
   int32_t num_kv_heads;
   int32_t group;
   int32_t page_size;
+  int32_t page_shift;         // log2(page_size) when it is a power of two
   int32_t window;             // 0 = none
   int32_t causal;
   int32_t out_fp32;
   float scale_log2;
 };
 
-// LDS tiles hold key rows unpadded; 16-byte chunk c of row r sits at chunk position
+// LDS stages hold key rows unpadded; 16-byte chunk c of row r sits at chunk position
 // c ^ swz(r).  The K swizzle spreads the 16 rows a K-operand read touches over all banks;
 // the V swizzle (even values, so 32-byte pairs stay together) spreads the 4 key rows of a
 // transpose read and its neighbouring lane block.
 __device__ __forceinline__ int k_swz(int row) { return row & 15; }
 __device__ __forceinline__ int v_swz(int row) { return 2 * (row & 7); }
 
-// Waits until at most n of this wave's vector memory operations are outstanding.
+// Waits until at most N of this wave's vector memory operations are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int DQK, int DVO>
+// Page and slot of a wave-uniform logical token, through a scalar load.
+template <bool POW2>
+__device__ __forceinline__ void uniform_page_slot(const int32_t* pages, int t, int page_size,
+                                                  int page_shift, int& page, int& slot) {
+  const_i32_ptr cp = (const_i32_ptr)pages;
+  t = __builtin_amdgcn_readfirstlane(t);
+  int j;
+  if constexpr (POW2) {
+    j = t >> page_shift;
+    slot = t & (page_size - 1);
+  } else {
+    j = t / page_size;
+    slot = t - j * page_size;
+  }
+  page = cp[j];
+}
+
+template <int DQK, int DVO, bool POW2>
 __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = kPrefillWaves;
-  constexpr int KT = kKeyTile;
+  constexpr int KS = kKeyStage;
   constexpr int QSTEPS = DQK / 32;          // MFMA K-steps of S^T
   constexpr int OT = DVO / 16;              // 16-wide head_dim tiles of O^T
   constexpr int KCH = DQK / 8;              // 16-byte chunks per K row
   constexpr int VCH = DVO / 8;
   constexpr int KRPI = 64 / KCH;            // K rows per copy instruction (1 or 2)
   constexpr int VRPI = 64 / VCH;
-  constexpr int KCOPIES = KT / KRPI / NW;   // copy instructions per wave per tile
-  constexpr int VCOPIES = KT / VRPI / NW;
-  constexpr int COPIES = KCOPIES + VCOPIES;
+  constexpr int RPW = KS / NW;              // key rows each wave copies per stage
+  constexpr int CPW = RPW / KRPI + RPW / VRPI;  // copy instructions per wave per stage
+  static_assert(RPW == 4, "each wave copies four key rows per stage");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * DQK];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][KT * DVO];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KS * DQK];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][KS * DVO];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -109,49 +129,27 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   const int64_t q_row = (int64_t)(it.q_begin + tok) * a.num_qo_heads + head;
 
   const int kv_lo = it.kv_begin, kv_hi = it.kv_end;
-  const int tile_first = kv_lo / KT;
-  const int tile_end = (kv_hi + KT - 1) / KT;
-  const int64_t k_head = (int64_t)kvh * a.k_sh;
-  const int64_t v_head = (int64_t)kvh * a.v_sh;
+  const int st_first = kv_lo / KS;
+  const int st_end = (kv_hi + KS - 1) / KS;
 
-  // Copies key tile `tile` into buffer `buf`: each instruction moves KRPI (or VRPI) whole
-  // rows straight from the pages into LDS; lane L fills chunk position L of its row with
-  // the logical chunk that the swizzle puts there.
-  auto copy_tile = [&](int tile, int buf) {
-    const int t0 = tile * KT;
-#pragma unroll
-    for (int c = 0; c < KCOPIES; ++c) {
-      const int row0 = (w * KCOPIES + c) * KRPI;
-      const int row = row0 + lane / KCH;
-      int t = t0 + row;
-      t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
-      int32_t page, slot;
-      token_page_slot(pages, t, a.page_size, page, slot);
-      const int chunk = (lane % KCH) ^ k_swz(row);
-      const char* src = a.k + (row_elem_offset(page, 0, slot, a.k_sp, 0, a.k_st) + k_head) * 2 + 16 * chunk;
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (__attribute__((address_space(3))) void*)(&k_lds[buf][row0 * DQK]),
-                                       16, 0, 0);
-    }
-#pragma unroll
-    for (int c = 0; c < VCOPIES; ++c) {
-      const int row0 = (w * VCOPIES + c) * VRPI;
-      const int row = row0 + lane / VCH;
-      int t = t0 + row;
-      t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
-      int32_t page, slot;
-      token_page_slot(pages, t, a.page_size, page, slot);
-      const int chunk = (lane % VCH) ^ v_swz(row);
-      const char* src = a.v + (row_elem_offset(page, 0, slot, a.v_sp, 0, a.v_st) + v_head) * 2 + 16 * chunk;
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (__attribute__((address_space(3))) void*)(&v_lds[buf][row0 * DVO]),
-                                       16, 0, 0);
-    }
-  };
+  // Stages [full_lo, full_hi) are visible to every row of this wave without a mask.
+  int full_lo, full_hi;
+  {
+    const int w_row0 = it.row_begin + 16 * w;
+    const int w_row1 = min(w_row0 + 15, it.row_end - 1);
+    const int p_first = it.kv_len - it.q_len + w_row0 / G;
+    const int p_last = it.kv_len - it.q_len + w_row1 / G;
+    int hi = kv_hi;                                   // keys < hi are below every bound
+    if (a.causal) hi = min(hi, p_first + 1);
+    int lo = kv_lo;
+    if (a.window > 0) lo = max(lo, p_last - a.window + 1);
+    full_lo = (lo + KS - 1) / KS;
+    full_hi = hi / KS;
+    if (w_row0 + 15 >= it.row_end) full_hi = full_lo;  // a wave with unused rows: masked path
+  }
 
-  if (tile_first < tile_end) copy_tile(tile_first, 0);
-
-  // Q^T operand for the whole tile: step j holds dims 32j + 8*g4 .. +7 of row n.
+  // Q^T operand for the whole tile: step j holds dims 32j + 8*g4 .. +7 of row n.  Loaded
+  // before any stage copy, so waiting for a copy also covers it.
   u32x4_t qf[QSTEPS];
   {
     const uint16_t* src = a.q + q_row * DQK + 8 * g4;
@@ -159,6 +157,46 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     for (int j = 0; j < QSTEPS; ++j)
       qf[j] = row_valid ? *(const u32x4_t*)(src + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
   }
+
+  // Copies key stage `st` into buffer SLOT.  Wave w moves key rows 4w .. 4w+3 of the stage
+  // for both K and V, straight from the pages into LDS (one instruction per 1 KB row, or
+  // one per two 512-byte rows); lane L fills chunk position L % chunks-per-row of its row
+  // with the logical chunk that the swizzle puts there.
+  const char* k_base = a.k + (int64_t)kvh * a.k_sh;
+  const char* v_base = a.v + (int64_t)kvh * a.v_sh;
+  const int my_row = RPW * w;
+  auto copy_stage = [&](int st, auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    int64_t koff[RPW], voff[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      int t = st * KS + my_row + i;
+      t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
+      int pg, sl;
+      uniform_page_slot<POW2>(pages, t, a.page_size, a.page_shift, pg, sl);
+      koff[i] = pg * a.k_sp + sl * a.k_st;
+      voff[i] = pg * a.v_sp + sl * a.v_st;
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; i += KRPI) {
+      const int sub = KRPI == 1 ? 0 : lane / KCH;
+      const int64_t off = KRPI == 1 ? koff[i] : (sub ? koff[i + 1] : koff[i]);
+      const int chunk = (lane % KCH) ^ k_swz(my_row + i + sub);
+      __builtin_amdgcn_global_load_lds((const void*)(k_base + off + 16 * chunk),
+          (__attribute__((address_space(3))) void*)(&k_lds[SLOT][(my_row + i) * DQK]), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; i += VRPI) {
+      const int sub = VRPI == 1 ? 0 : lane / VCH;
+      const int64_t off = VRPI == 1 ? voff[i] : (sub ? voff[i + 1] : voff[i]);
+      const int chunk = (lane % VCH) ^ v_swz(my_row + i + sub);
+      __builtin_amdgcn_global_load_lds((const void*)(v_base + off + 16 * chunk),
+          (__attribute__((address_space(3))) void*)(&v_lds[SLOT][(my_row + i) * DVO]), 16, 0, 0);
+    }
+  };
+  (void)CPW;
+
+  if (st_first < st_end) copy_stage(st_first, std::integral_constant<int, 0>{});
 
   f32x4_t o[OT];
 #pragma unroll
@@ -168,23 +206,24 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
 
   // Transpose-read source of this lane within its 16-lane block: key (n / 4) of the 4-key
   // group, dims 4*(n % 4) .. +3 of the 16-dim tile.
-  const int tr_row = n >> 2;
+  const int tr_row = 4 * g4 + (n >> 2);
   const int tr_half = (n & 3) >> 1;         // which 16-byte chunk of the 32-byte pair
   const int tr_off = 4 * (n & 1);           // element offset inside that chunk
 
-  int buf = 0;
-  for (int tile = tile_first; tile < tile_end; ++tile, buf ^= 1) {
-    const int t0 = tile * KT;
-    if (tile + 1 < tile_end) {
-      copy_tile(tile + 1, buf ^ 1);
-      wait_vmcnt<COPIES>();  // this tile's copies have landed; the next tile's may fly
-    } else {
-      wait_vmcnt<0>();
-    }
+  // One key stage in buffer SLOT: wait for its copies, barrier, refill the other buffer,
+  // then S^T = K Q^T, the online softmax and O^T += V^T P^T.
+  auto stage = [&](int st, auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    const int t0 = st * KS;
+    // This wave's copies of this stage have landed; after the barrier every wave's have,
+    // and every wave is done with the other buffer, which the next stage's copies refill.
+    wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
+    if (st + 1 < st_end) copy_stage(st + 1, std::integral_constant<int, SLOT ^ 1>{});
+    const bool full = st >= full_lo && st < full_hi;
 
-    const uint16_t* kt = k_lds[buf];
-    const uint16_t* vt = v_lds[buf];
+    const uint16_t* kt = k_lds[SLOT];
+    const uint16_t* vt = v_lds[SLOT];
     // ---- S^T = K Q^T for keys 0..15 (s0) and 16..31 (s1); lane holds keys 4*g4 + i.
     // Chunk 4j + g4 of row n (or 16 + n) sits at 4*(j ^ (n>>2)) + (g4 ^ (n&3)): four
     // per-lane bases (one per j % 4) plus compile-time offsets cover every step.
@@ -196,10 +235,9 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
         const uint16_t* kbl = kb + 32 * (jl ^ (n >> 2));
 #pragma unroll
         for (int jh = 0; jh < QSTEPS / 4; ++jh) {
-          const int j = 4 * jh + jl;
           const u32x4_t k0 = *(const u32x4_t*)(kbl + 128 * jh);
           const u32x4_t k1 = *(const u32x4_t*)(kbl + 128 * jh + 16 * DQK);
-          const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, qf[j]);
+          const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, qf[4 * jh + jl]);
           s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k0), qb, s0, 0, 0, 0);
           s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k1), qb, s1, 0, 0, 0);
         }
@@ -209,19 +247,21 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     // ---- masks and online softmax of row n (its 32 keys are spread over the 4 lanes g4).
     float sv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sv[i] = i < 4 ? s0[i] : s1[i - 4];
-    float mx = -INFINITY;
+    for (int i = 0; i < 8; ++i) sv[i] = (i < 4 ? s0[i] : s1[i - 4]) * a.scale_log2;
+    if (!full) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = t0 + 16 * (i >> 2) + 4 * g4 + (i & 3);
-      bool ok = row_valid && t >= kv_lo && t < kv_hi;
-      if (a.causal) ok = ok && t <= pos;
-      if (a.window > 0) ok = ok && t > pos - a.window;
-      sv[i] = ok ? sv[i] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sv[i]);
+      for (int i = 0; i < 8; ++i) {
+        const int t = t0 + 16 * (i >> 2) + 4 * g4 + (i & 3);
+        bool ok = row_valid && t >= kv_lo && t < kv_hi;
+        if (a.causal) ok = ok && t <= pos;
+        if (a.window > 0) ok = ok && t > pos - a.window;
+        sv[i] = ok ? sv[i] : -INFINITY;
+      }
     }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
     // Move the reference max only when the row max outgrows it by the threshold.
     const bool grow = mx > m_ref + kRescaleThreshold || (m_ref == -INFINITY && mx != -INFINITY);
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -252,11 +292,10 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     // swizzle, and the second is 16 rows below the first).  Chunk 2t + half of the row sits
     // at 2*(t ^ s) + half with s = row & 7: eight per-lane bases plus constant offsets.
     {
-      const int ra = 4 * g4 + tr_row;
-      const uint16_t* vb = vt + ra * DVO + tr_off + 8 * tr_half;
+      const uint16_t* vb = vt + tr_row * DVO + tr_off + 8 * tr_half;
 #pragma unroll
       for (int tl = 0; tl < 8; ++tl) {
-        const uint16_t* vbl = vb + 16 * (tl ^ (ra & 7));
+        const uint16_t* vbl = vb + 16 * (tl ^ (tr_row & 7));
 #pragma unroll
         for (int th = 0; th < OT / 8; ++th) {
           const int t = 8 * th + tl;
@@ -267,12 +306,15 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
         }
       }
     }
-    __builtin_amdgcn_s_barrier();  // every wave is done with this buffer before it is refilled
+  };
+
+  for (int st0 = st_first; st0 < st_end; st0 += 2) {
+    stage(st0, std::integral_constant<int, 0>{});
+    if (st0 + 1 < st_end) stage(st0 + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- normalise and write row n: O^T tile t, register i holds dim 16t + 4*g4 + i.
-  float l_tot = l_run + shfl_xor_f(l_run, 16);
-  l_tot += shfl_xor_f(l_tot, 32);
+  const float l_tot = sum_xor32(sum_xor16(l_run));
   if (!row_valid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t out_row = q_row * DVO;
@@ -288,6 +330,12 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   }
   if (a.lse && g4 == 0)
     a.lse[q_row] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+template <int DQK, int DVO>
+static void launch_prefill(const PrefillArgs& a, bool pow2, int grid, hipStream_t s) {
+  if (pow2) prefill_kernel<DQK, DVO, true><<<grid, 512, 0, s>>>(a);
+  else prefill_kernel<DQK, DVO, false><<<grid, 512, 0, s>>>(a);
 }
 
 }  // namespace pa
@@ -314,8 +362,8 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   a.q = (const uint16_t*)q;
   a.k = (const char*)cache->k;
   a.v = (const char*)cache->v;
-  a.k_sp = cache->k_stride_page; a.k_sh = cache->k_stride_head; a.k_st = cache->k_stride_token;
-  a.v_sp = cache->v_stride_page; a.v_sh = cache->v_stride_head; a.v_st = cache->v_stride_token;
+  a.k_sp = 2 * cache->k_stride_page; a.k_sh = 2 * cache->k_stride_head; a.k_st = 2 * cache->k_stride_token;
+  a.v_sp = 2 * cache->v_stride_page; a.v_sh = 2 * cache->v_stride_head; a.v_st = 2 * cache->v_stride_token;
   a.kv_indptr = table->kv_indptr;
   a.kv_indices = table->kv_indices;
   a.items = (const PrefillItem*)(ws + plan->items_offset);
@@ -325,6 +373,7 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   a.num_kv_heads = cache->num_kv_heads;
   a.group = params->num_qo_heads / cache->num_kv_heads;
   a.page_size = cache->page_size;
+  a.page_shift = __builtin_ctz(cache->page_size);  // used only when page_size is a power of two
   a.window = params->window > 0 ? params->window : 0;
   a.causal = params->causal ? 1 : 0;
   a.out_fp32 = params->out_dtype == PA_DTYPE_FP32;
@@ -332,9 +381,10 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   const int grid = plan->num_items * cache->num_kv_heads;
   hipStream_t s = (hipStream_t)stream;
   const int dqk = cache->head_dim_qk, dvo = cache->head_dim_vo;
-  if (dqk == 512 && dvo == 512) prefill_kernel<512, 512><<<grid, 512, 0, s>>>(a);
-  else if (dqk == 256 && dvo == 256) prefill_kernel<256, 256><<<grid, 512, 0, s>>>(a);
-  else prefill_kernel<512, 256><<<grid, 512, 0, s>>>(a);
+  const bool pow2 = (cache->page_size & (cache->page_size - 1)) == 0;
+  if (dqk == 512 && dvo == 512) launch_prefill<512, 512>(a, pow2, grid, s);
+  else if (dqk == 256 && dvo == 256) launch_prefill<256, 256>(a, pow2, grid, s);
+  else launch_prefill<512, 256>(a, pow2, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
   count_launches(1);
