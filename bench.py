@@ -2,11 +2,12 @@
 
 Prints ONE JSON line.  The headline is paged decode HBM throughput on the GQA decode
 workload (batch 32, 24 query / 4 KV heads, head_dim 512, page size 16, KV lengths
-uniform in [1024, 8192], split-K 8, bf16): ``value`` is algorithmic bytes per step divided
-by the measured step time, with the inputs resident in HBM.  A step is one pass of the
-decode hot path: the split-K partial kernel and the log-sum-exp merge kernel (the plan is
-host work, made and uploaded once before timing).  The other workloads (FP8 decode,
-sliding-window decode, causal prefill) are reported under ``secondary``.
+uniform in [1024, 8192], bf16), split by the balanced planner: ``value`` is algorithmic
+bytes per step divided by the measured step time, with the inputs resident in HBM.  A
+step is one pass of the decode hot path: the split-K partial kernel and the log-sum-exp
+merge kernel (the plan is host work, made and uploaded once before timing).  The other
+workloads (the same GQA inputs with a fixed split-K of 8, FP8 decode, sliding-window
+decode, causal prefill) are reported under ``secondary``.
 
 Algorithmic work:
   decode bytes  = sum_b Hkv * |visible keys_b| * (Dqk + Dvo) * bytes_per_kv_element
@@ -262,7 +263,8 @@ def decode_config(case):
     return {"workload": case.name, "batch": case.batch, "num_qo_heads": case.num_qo_heads,
             "num_kv_heads": case.num_kv_heads, "head_dim_qk": case.head_dim_qk,
             "head_dim_vo": case.head_dim_vo, "page_size": case.page_size,
-            "kv_dtype": case.kv_dtype, "window": case.window, "num_splits": case.num_splits,
+            "kv_dtype": case.kv_dtype, "window": case.window,
+            "split_k": case.num_splits if case.num_splits > 0 else "balanced",
             "kv_len_min": int(case.kv_lens.min()), "kv_len_max": int(case.kv_lens.max()),
             "kv_len_mean": float(case.kv_lens.mean()), "out_dtype": case.out_dtype}
 
@@ -271,7 +273,9 @@ def measure_decode(name, steps, warmup, variant=None):
     import torch
     from synth import decode_workload
     case = decode_workload(name, device="cuda", variant=variant)
-    if variant is not None:
+    if isinstance(variant, str):
+        case.name = f"{name}_{variant}"
+    elif variant is not None:
         case.name = f"{name}_d{variant[0]}_p{variant[1]}"
     step_ms, part_ms, merge_ms, wall_ms, plan = time_decode(case, steps, warmup)
     nbytes = decode_algorithmic_bytes(case)
@@ -285,8 +289,9 @@ def measure_decode(name, steps, warmup, variant=None):
                      "traffic": traffic_for(case.name), "kernel": "decode_partial_kernel",
                      "algorithmic_bytes_per_launch": nbytes,
                      "kernel_avg_ms": round(part_ms, 5)},
-        "plan": {"items": plan.num_items, "workgroups": plan.num_items * case.num_kv_heads,
-                 "merges": plan.num_merges, "chunk_blocks": plan.chunk_blocks},
+        "plan": {"segments": plan.num_items, "waves": plan.num_workers,
+                 "merged_pairs": plan.num_merges, "partial_slots": plan.num_slots,
+                 "max_wave_blocks": plan.chunk_blocks},
     }
     return res
 
@@ -327,7 +332,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa_decode",
-                    help="gqa_decode | fp8_decode | window_decode_d512_p1 | ... | "
+                    help="gqa_decode | gqa_decode_splitk8 | fp8_decode | "
+                         "window_decode_d512_p1 | ... | "
                          "causal_prefill_vo512 | causal_prefill_vo256")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -353,6 +359,9 @@ def main():
         if wl.startswith("causal_prefill_vo"):
             return measure_prefill("causal_prefill", args.steps, args.warmup,
                                    int(wl[len("causal_prefill_vo"):]))
+        if wl.startswith("gqa_decode_splitk"):
+            return measure_decode("gqa_decode", args.steps, args.warmup,
+                                  wl[len("gqa_decode_"):])
         return measure_decode(wl, args.steps, args.warmup)
 
     main_res = run_named(args.workload)
@@ -389,7 +398,8 @@ def main():
 
     if not args.no_secondary:
         sec = {}
-        names = ["gqa_decode", "fp8_decode", "window_decode_d512_p1", "window_decode_d512_p32",
+        names = ["gqa_decode", "gqa_decode_splitk8", "fp8_decode", "window_decode_d512_p1",
+                 "window_decode_d512_p32",
                  "window_decode_d256_p1", "window_decode_d256_p32", "causal_prefill_vo512",
                  "causal_prefill_vo256"]
         for wl in names:

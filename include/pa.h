@@ -117,19 +117,21 @@ typedef struct pa_plan {
   int32_t kv_dtype;
   int32_t window;
   int32_t causal;
-  int32_t num_items;               /* work items; one workgroup per (item, kv head)     */
+  int32_t num_items;               /* decode: key segments; prefill: tiles (one
+                                      workgroup per (tile, kv head))                    */
   int32_t num_slots;               /* decode: partial-result slots in the workspace     */
-  int32_t num_merges;              /* decode: requests whose partials are merged        */
+  int32_t num_merges;              /* decode: (request, kv head) pairs the merge writes  */
   int32_t block_tokens;            /* decode: key block of the partition (16)           */
-  int32_t chunk_blocks;            /* decode: adaptive chunk length in blocks, or 0     */
-  int32_t num_splits;              /* decode: requested splits (0 = adaptive)           */
+  int32_t chunk_blocks;            /* decode: longest wave, in blocks                   */
+  int32_t num_splits;              /* decode: requested splits (0 = balanced)           */
   int32_t tile_rows;               /* prefill: query rows (token, head) per tile        */
   int32_t total_q;                 /* prefill: number of query tokens                   */
   int32_t max_kv_len;
-  int32_t reserved0;
+  int32_t num_workers;             /* decode: waves the partial kernel launches         */
   int64_t plan_bytes;              /* bytes of the host plan buffer in use              */
   int64_t items_offset;            /* byte offset of the item array in the plan buffer  */
   int64_t merges_offset;           /* byte offset of the merge array in the plan buffer */
+  int64_t workers_offset;          /* decode: byte offset of the per-wave segment ranges */
   int64_t partial_o_offset;        /* byte offset of partial outputs in the workspace   */
   int64_t partial_lse_offset;      /* byte offset of partial lse in the workspace       */
   int64_t workspace_bytes;         /* device workspace the run call needs               */
@@ -158,12 +160,17 @@ pa_status pa_validate_page_table_host(const int32_t* kv_indptr_host,
                                       int32_t num_pages, int32_t page_size);
 
 /* Plans a decode batch from host copies of kv_indptr and kv_last_page_len (the device
- * copies passed to pa_paged_decode must hold the same values).  num_splits > 0 cuts each
- * request's visible keys into min(num_splits, blocks) near-equal chunks of 16-token
- * blocks; num_splits == 0 picks the chunk length so that the batch makes about 2048
- * workgroups (at least 8 blocks per chunk, at most 64 chunks per request).  Items run
- * longest first.  Call with plan_buf_host == NULL to learn plan->plan_bytes (and
- * plan->workspace_bytes); then call again with a buffer of at least that size.
+ * copies passed to pa_paged_decode must hold the same values).  The work is the set of
+ * (request, kv head, 16-token key block) units; each wave of the partial kernel runs one
+ * piece of them.  num_splits == 0 (balanced) cuts the units, flattened in (request,
+ * kv head, block) order, into min(2048, ceil(units / 8)) equal pieces, i.e. one wave per
+ * SIMD slot of the 256 CUs at two waves per SIMD, so every wave streams the same number
+ * of bytes.  num_splits > 0 instead cuts each (request, kv head) into
+ * min(num_splits, blocks) near-equal pieces.  A piece is cut at (request, kv head)
+ * boundaries into segments; a (request, kv head) with several segments is merged by
+ * log-sum-exp weights.  Waves run longest first.  Call with plan_buf_host == NULL to
+ * learn plan->plan_bytes (and plan->workspace_bytes); then call again with a buffer of
+ * at least that size.
  * Supported: head dims (512,512), (256,256), (512,256); kv bf16 or FP8 E4M3FN;
  * q bf16; out fp32 or bf16; 1 <= num_qo_heads / num_kv_heads <= 8; num_splits <= 64.
  * Never calls HIP. */

@@ -13,15 +13,20 @@ Decode rule (units of 16-token logical blocks, block j = tokens [16j, 16j+16)):
 
 * L_b from the page table; visible keys are [s_b, L_b) with s_b = max(0, L_b - W) when a
   window W > 0 is set, else 0.
-* Visible blocks: fb = s_b // 16, eb = ceil(L_b / 16), n_b = eb - fb.
-* Number of chunks: fixed ``num_splits`` S > 0 gives c_b = min(S, n_b); adaptive (S = 0)
-  uses ``chunk_blocks = max(MIN_CHUNK_BLOCKS, ceil(sum_b n_b / ceil(TARGET_WGS / Hkv)))``
-  and c_b = min(MAX_SPLITS, ceil(n_b / chunk_blocks)).  c_b is at least 1.
-* Chunk c of request b spans blocks [fb + n_b*c // c_b, fb + n_b*(c+1) // c_b), clipped to
-  the visible keys.
-* Requests with c_b > 1 own c_b consecutive workspace slots, in request order; a request
-  with a single chunk writes its output directly (slot -1).
-* Work items run longest first (token count descending), ties in (b, c) order.
+* Visible blocks: fb = s_b // 16, eb = ceil(L_b / 16), n_b = max(0, eb - fb).
+* Work units are the (request b, KV head h, block j) triples, flattened in (b, h, j)
+  order; the range of (b, h) is [o_bh, o_bh + n_b) and U is the total.
+* Pieces (one wave each): balanced (num_splits S = 0) cuts the flattened axis into
+  P = min(WAVE_SLOTS, ceil(U / MIN_PIECE_BLOCKS)) pieces [U p // P, U (p+1) // P); a
+  fixed split S > 0 cuts every (b, h) range on its own into c = min(S, n_b) pieces
+  [o_bh + n_b k // c, o_bh + n_b (k+1) // c).
+* A piece is cut at (b, h) boundaries into segments; blocks [j0, j1) of (b, h) cover the
+  keys [max(s_b, 16 (fb + j0)), min(L_b, 16 (fb + j1))).
+* A (b, h) with several segments owns that many consecutive workspace slots, in segment
+  order, slots numbered in (b, h) order, and gets a merge entry (b, h, first slot, count);
+  a (b, h) with one segment writes its output directly (slot -1); an empty request gets a
+  merge entry with no slots for each h (zero output, lse -inf).
+* Waves run by piece length descending, ties in piece order.
 
 Prefill rule: the query rows of one (request, KV head) are the q_len * G pairs
 (token i, head g) flattened as i * G + g; tiles of ``tile_rows`` consecutive rows;
@@ -31,8 +36,8 @@ Tiles run by key count descending, ties in (b, tile) order.
 """
 
 BLOCK_TOKENS = 16
-TARGET_WGS = 2048
-MIN_CHUNK_BLOCKS = 8
+WAVE_SLOTS = 2048
+MIN_PIECE_BLOCKS = 8
 MAX_SPLITS = 64
 
 
@@ -41,46 +46,78 @@ def _ceil_div(a, b):
 
 
 def decode_partition_ref(kv_lens, window, num_splits, num_kv_heads):
-    """Returns (items, merges).
+    """Returns (waves, merges).
 
-    items:  list of (b, t_begin, t_end, slot) in execution order.
-    merges: list of (b, slot_begin, num_chunks) for requests split into several chunks.
+    waves:  in launch order, each a list of segments (b, h, t_begin, t_end, slot).
+    merges: (b, h, slot_begin, num_slots) for every (request, KV head) that has several
+            segments or no keys at all, in (b, h) order.
     """
+    lens = [int(x) for x in kv_lens]
     starts, nblk = [], []
-    for length in kv_lens:
-        length = int(length)
+    for length in lens:
         s = max(0, length - window) if window > 0 else 0
-        fb = s // BLOCK_TOKENS
-        eb = _ceil_div(length, BLOCK_TOKENS)
         starts.append(s)
-        nblk.append(max(0, eb - fb))
-    if num_splits > 0:
-        chunks = [max(1, min(num_splits, n)) for n in nblk]
-    else:
-        target_chunks = _ceil_div(TARGET_WGS, num_kv_heads)
-        chunk_blocks = max(MIN_CHUNK_BLOCKS, _ceil_div(sum(nblk), target_chunks))
-        chunks = [max(1, min(MAX_SPLITS, _ceil_div(n, chunk_blocks))) for n in nblk]
+        nblk.append(max(0, _ceil_div(length, BLOCK_TOKENS) - s // BLOCK_TOKENS))
+    pairs = [(b, h) for b in range(len(lens)) for h in range(num_kv_heads)]
+    origin, total = [], 0
+    for b, h in pairs:
+        origin.append(total)
+        total += nblk[b]
 
-    items, merges, next_slot = [], [], 0
-    for b, length in enumerate(kv_lens):
-        length = int(length)
-        c_b, n_b, s_b = chunks[b], nblk[b], starts[b]
-        fb = s_b // BLOCK_TOKENS
-        slot0 = -1
-        if c_b > 1:
-            slot0 = next_slot
-            merges.append((b, next_slot, c_b))
-            next_slot += c_b
-        for c in range(c_b):
-            lo = fb + (n_b * c) // c_b
-            hi = fb + (n_b * (c + 1)) // c_b
-            t0 = max(s_b, lo * BLOCK_TOKENS)
-            t1 = min(length, hi * BLOCK_TOKENS)
-            if length == 0:
-                t0 = t1 = 0
-            items.append((b, t0, t1, -1 if c_b == 1 else slot0 + c, c))
-    items.sort(key=lambda it: (-(it[2] - it[1]), it[0], it[4]))
-    return [it[:4] for it in items], merges
+    if num_splits > 0:
+        pieces = []
+        for i, (b, h) in enumerate(pairs):
+            n = nblk[b]
+            c = min(num_splits, n)
+            pieces += [(origin[i] + n * k // c, origin[i] + n * (k + 1) // c) for k in range(c)]
+    else:
+        p = min(WAVE_SLOTS, _ceil_div(total, MIN_PIECE_BLOCKS))
+        pieces = [(total * k // p, total * (k + 1) // p) for k in range(p)]
+
+    def pair_of(u):  # the (b, h) whose range holds flattened unit u (empty ranges hold none)
+        for i in range(len(pairs)):
+            if origin[i] <= u < origin[i] + nblk[pairs[i][0]]:
+                return i
+        raise AssertionError(u)
+
+    piece_segs = []
+    for u0, u1 in pieces:
+        segs, u = [], u0
+        while u < u1:
+            i = pair_of(u)
+            b, h = pairs[i]
+            e = min(u1, origin[i] + nblk[b])
+            fb = starts[b] // BLOCK_TOKENS
+            t0 = max(starts[b], (fb + u - origin[i]) * BLOCK_TOKENS)
+            t1 = min(lens[b], (fb + e - origin[i]) * BLOCK_TOKENS)
+            segs.append([b, h, t0, t1, -1])
+            u = e
+        piece_segs.append(segs)
+
+    count = {}
+    for segs in piece_segs:
+        for sg in segs:
+            count[(sg[0], sg[1])] = count.get((sg[0], sg[1]), 0) + 1
+    first_slot, merges, next_slot = {}, [], 0
+    for b, h in pairs:
+        k = count.get((b, h), 0)
+        if k == 0:
+            merges.append((b, h, next_slot, 0))
+        elif k > 1:
+            first_slot[(b, h)] = next_slot
+            merges.append((b, h, next_slot, k))
+            next_slot += k
+    used = {}
+    for segs in piece_segs:
+        for sg in segs:
+            key = (sg[0], sg[1])
+            if key in first_slot:
+                sg[4] = first_slot[key] + used.get(key, 0)
+                used[key] = used.get(key, 0) + 1
+
+    order = sorted(range(len(pieces)), key=lambda k: (-(pieces[k][1] - pieces[k][0]), k))
+    waves = [[tuple(sg) for sg in piece_segs[k]] for k in order]
+    return waves, merges
 
 
 def prefill_tiles_ref(qo_lens, kv_lens, group, tile_rows, causal, window):

@@ -7,21 +7,26 @@
 // keys, read through the page table from the combined HND cache, with the key axis cut
 // into chunks whose partial results are merged by log-sum-exp weights (flash-decoding).
 //
-// Work decomposition.  The host planner cuts every request's visible keys into chunks of
-// 16-token blocks; one workgroup (4 waves) runs one (chunk, KV head).  The G query heads
-// that share the KV head are computed together, so each K/V byte is read from HBM once
-// for the whole group:
+// Work decomposition.  The host planner flattens the (request, KV head, 16-token block)
+// units and cuts them into equal pieces, one per wave (2048 on the 256 CUs at two waves
+// per SIMD), so every wave streams the same number of bytes and the whole grid is
+// resident from start to end: no second round of workgroups, no tail of stragglers.  A
+// piece is cut into segments at (request, KV head) boundaries; a segment's result goes to
+// the output directly when it covers the whole pair, else to a workspace slot that the
+// merge kernel combines.  The G query heads that share the KV head are computed together,
+// so each K/V byte is read from HBM once for the whole group:
 //   * S = K Q^T for a 16-key block is one 16x16 tile of v_mfma_f32_16x16x32_bf16 (keys
 //     on M, the G heads padded to 16 on N, head_dim on K).  Each lane loads its K operand
 //     straight from the page as 16-byte vectors (4 lanes cover 64 contiguous bytes of a key
 //     row); Q sits in LDS with the same head_dim order.
 //   * The online softmax keeps a running max and sum per head; the block max is a
 //     cross-lane reduction over the 4 lanes that share a head.
-//   * P V runs on the vector ALU: each V load instruction covers whole key rows (lane l
-//     holds 8 consecutive head_dim elements of one row), each lane keeps G x 8 fp32
-//     accumulators, and the block's probabilities come from LDS as broadcast reads.
-//   * The 4 waves take interleaved blocks and merge their states through LDS in a fixed
-//     order at the end, so results are deterministic.
+//   * P V runs on the vector ALU one block behind S: each V load instruction covers whole
+//     key rows (lane l holds 8 consecutive head_dim elements of one row), each lane keeps
+//     G x 8 fp32 accumulators, and the block's probabilities come from LDS as broadcast
+//     reads.  Block i's V rows are loaded while block i's scores are computed and used in
+//     the next iteration; block i+1's keys are loaded after block i's MFMAs.
+//   * Waves never synchronise with each other; each one's results are deterministic.
 // FP8 E4M3FN keys are widened to bf16 in registers (exact); k_scale is folded into the
 // score scale and v_scale into the output.
 
@@ -36,7 +41,7 @@
 
 namespace pa {
 
-constexpr int kDecodeWaves = 4;
+constexpr int kDecodeWavesPerGroup = 8;  // the two waves of every SIMD of a CU
 
 struct DecodeArgs {
   const uint16_t* q;           // [B, Hq, DQK] bf16 bits
@@ -46,13 +51,14 @@ struct DecodeArgs {
   int64_t v_sp, v_sh, v_st;
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
-  const DecodeItem* items;
+  const DecodeSegment* segs;
+  const int32_t* wave_begin;   // wave w runs segments [wave_begin[w], wave_begin[w + 1])
+  int32_t num_waves;
   void* out;                   // [B, Hq, DVO] fp32 or bf16
   float* lse;                  // [B, Hq] or null
-  float* part_o;               // [slots, Hq, DVO] fp32
-  float* part_lse;             // [slots, Hq], log2 domain
+  float* part_o;               // [slots, G, DVO] fp32
+  float* part_lse;             // [slots, G], log2 domain
   int32_t num_qo_heads;
-  int32_t num_kv_heads;
   int32_t group;
   int32_t page_size;
   int32_t out_fp32;
@@ -68,341 +74,305 @@ __device__ __forceinline__ int q_dim_of_step(int j, int g4) {
   else return 64 * (j >> 1) + 16 * g4 + 8 * (j & 1);
 }
 
+// Eight waves per workgroup, one workgroup per CU: each wave runs its own piece (its
+// segments one after the other) and never waits for the others.  They share LDS only to
+// publish how many blocks each has done: a wave behind the CU's average raises its issue
+// priority, because the hardware otherwise favours the older of the two waves on a SIMD,
+// which then finishes far ahead of its partner and leaves the SIMD half-occupied for the
+// rest of the kernel.
 template <int DQK, int DVO, int KVB, int GMAX>
-__global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
-  constexpr int NW = kDecodeWaves;
+__global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_kernel(DecodeArgs a) {
   constexpr int NSTEP = DQK / 32;                 // MFMA steps over head_dim
   constexpr int NKL = 16 * DQK * KVB / (64 * 16); // 16-byte K loads per lane per block
   constexpr int LPR = DVO / 8;                    // lanes per V row (8 elements per lane)
   constexpr int RPI = 64 / LPR;                   // V rows per load instruction (1 or 2)
   constexpr int NVL = 16 / RPI;                   // V load instructions per block
   constexpr int QPITCH = DQK + 8;                 // LDS row pitch of Q (bf16), padded
+  constexpr int QV = (GMAX * DQK / 8 + 63) / 64;  // 16-byte Q pieces per lane
   using vload_t = typename std::conditional<KVB == 2, u32x4_t, u32x2_t>::type;
 
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[16 * QPITCH];
-  __shared__ __attribute__((aligned(16))) float p_lds[NW][16][16];
-  __shared__ __attribute__((aligned(16))) float alpha_lds[NW][16];
-  __shared__ __attribute__((aligned(16))) float ml_lds[2][NW][16];
-  __shared__ __attribute__((aligned(16))) float merge_lds[2][GMAX][DVO];
+  constexpr int NWG = kDecodeWavesPerGroup;
+  __shared__ __attribute__((aligned(16))) uint16_t q_all[NWG][GMAX * QPITCH];
+  __shared__ __attribute__((aligned(16))) float p_all[NWG][2][16][16];  // P V runs one block behind
+  __shared__ __attribute__((aligned(16))) float alpha_all[NWG][2][16];
+  __shared__ __attribute__((aligned(16))) int progress[NWG];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g4 = lane >> 4;
   const int n = lane & 15;
-  const int hkv = a.num_kv_heads;
-  const int kvh = blockIdx.x % hkv;
-  const DecodeItem it = a.items[blockIdx.x / hkv];
   const int G = a.group;
-  const int t0 = it.t_begin, t1 = it.t_end;
-  const int32_t* __restrict__ pages = a.kv_indices + a.kv_indptr[it.b];
-
-  // Q of the head group -> LDS rows 0..G-1; rows G..15 are zero.
-  {
-    const uint16_t* qsrc = a.q + ((int64_t)it.b * a.num_qo_heads + (int64_t)kvh * G) * DQK;
-    for (int idx = tid; idx < 16 * (DQK / 8); idx += 256) {
-      const int row = idx / (DQK / 8), c8 = idx % (DQK / 8);
-      u32x4_t val = {0u, 0u, 0u, 0u};
-      if (row < G) val = *(const u32x4_t*)(qsrc + row * DQK + c8 * 8);
-      *(u32x4_t*)(q_lds + row * QPITCH + c8 * 8) = val;
-    }
-  }
-  __syncthreads();
-
-  float m_run = -INFINITY;  // per head n, log2 domain
-  float l_run = 0.f;        // this lane's share of the sum for head n
-  float acc[GMAX][8];
-#pragma unroll
-  for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-
-  const int blk_first = t0 / 16;
-  const int blk_end = (t1 + 15) / 16;
-  const int64_t k_head = (int64_t)kvh * a.k_sh;
-  const int64_t v_head = (int64_t)kvh * a.v_sh;
+  const int qrow = n < G ? n : G - 1;  // MFMA columns past the group repeat the last head
+  uint16_t* q_lds = q_all[wv];
+  float (*p_lds)[16][16] = p_all[wv];
+  float (*alpha_lds)[16] = alpha_all[wv];
+  const int wave = blockIdx.x * NWG + wv;
+  const int seg_first = wave < a.num_waves ? a.wave_begin[wave] : 0;
+  const int seg_last = wave < a.num_waves ? a.wave_begin[wave + 1] : 0;
+  if (lane == 0) progress[wv] = 0;
+  int done = 0;  // blocks this wave has finished
 
   u32x4_t kbuf[NKL];
   vload_t vbuf[NVL];
+  float acc[GMAX][8];
 
-  // Page and slot of key n of a block (clamped into the chunk, so that every load is of a
-  // key this chunk owns; clamped lanes are masked out of the softmax).
-  auto block_page = [&](int blk, int32_t& page, int32_t& slot) {
-    int t = blk * 16 + n;
-    t = t < t0 ? t0 : (t >= t1 ? t1 - 1 : t);
-    token_page_slot(pages, t, a.page_size, page, slot);
-  };
-  auto issue_k = [&](int32_t page, int32_t slot) {
-    const char* base = a.k + (row_elem_offset(page, 0, slot, a.k_sp, 0, a.k_st) + k_head) * KVB + 16 * g4;
+  for (int sgi = seg_first; sgi < seg_last; ++sgi) {
+    const DecodeSegment sg = a.segs[sgi];
+    const int t0 = sg.t_begin, t1 = sg.t_end;  // t1 > t0
+    const int32_t* __restrict__ pages = a.kv_indices + a.kv_indptr[sg.b];
+    const int64_t k_head = (int64_t)sg.kvh * a.k_sh;
+    const int64_t v_head = (int64_t)sg.kvh * a.v_sh;
+
+    // Page and slot of key n of a block, clamped into the segment: every load is of a key
+    // the segment owns, and clamped lanes are masked out of the softmax.  Block indices
+    // past the end (the prefetch after the last block) land on the segment's last key.
+    auto block_page = [&](int blk, int32_t& page, int32_t& slot) {
+      int t = blk * 16 + n;
+      t = t < t0 ? t0 : (t >= t1 ? t1 - 1 : t);
+      token_page_slot(pages, t, a.page_size, page, slot);
+    };
+    auto issue_k = [&](int32_t page, int32_t slot) {
+      const char* base = a.k + (row_elem_offset(page, 0, slot, a.k_sp, 0, a.k_st) + k_head) * KVB + 16 * g4;
 #pragma unroll
-    for (int l = 0; l < NKL; ++l) kbuf[l] = *(const u32x4_t*)(base + 64 * l);
-  };
-  auto issue_v = [&](int32_t page, int32_t slot) {
+      for (int l = 0; l < NKL; ++l) kbuf[l] = __builtin_nontemporal_load((const u32x4_t*)(base + 64 * l));
+    };
+    auto issue_v = [&](int32_t page, int32_t slot) {
 #pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-      const int src = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
-      int32_t pv, sv;
-      if constexpr (RPI == 1) {
-        pv = __builtin_amdgcn_readlane(page, src);
-        sv = __builtin_amdgcn_readlane(slot, src);
-      } else {
-        pv = shfl_i(page, src);
-        sv = shfl_i(slot, src);
+      for (int i = 0; i < NVL; ++i) {
+        const int src = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
+        int32_t pv, sv;
+        if constexpr (RPI == 1) {
+          pv = __builtin_amdgcn_readlane(page, src);
+          sv = __builtin_amdgcn_readlane(slot, src);
+        } else {
+          pv = shfl_i(page, src);
+          sv = shfl_i(slot, src);
+        }
+        const char* base = a.v + (row_elem_offset(pv, 0, sv, a.v_sp, 0, a.v_st) + v_head) * KVB +
+                           (lane % LPR) * 8 * KVB;
+        vbuf[i] = __builtin_nontemporal_load((const vload_t*)base);
       }
-      const char* base = a.v + (row_elem_offset(pv, 0, sv, a.v_sp, 0, a.v_st) + v_head) * KVB +
-                         (lane % LPR) * 8 * KVB;
-      vbuf[i] = *(const vload_t*)base;
-    }
-  };
+    };
+    // P V of one block: rescale the accumulators by the block's alpha, then add p * V with
+    // the probabilities from LDS buffer `pb` and the V rows in vbuf.
+    auto pv = [&](int pb) {
+      {
+        float al[GMAX];
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) al[h] = alpha_lds[pb][h];
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+      }
+#pragma unroll
+      for (int i = 0; i < NVL; ++i) {
+        const int tk = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
+        float p[GMAX];
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) p[h] = p_lds[pb][tk][h];
+        float vf[8];
+        if constexpr (KVB == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vf[2 * e] = bf16_lo(vbuf[i][e]);
+            vf[2 * e + 1] = bf16_hi(vbuf[i][e]);
+          }
+        } else {
+          fp8x4_to_f32(vbuf[i][0], vf);
+          fp8x4_to_f32(vbuf[i][1], vf + 4);
+        }
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+          if (GMAX == 1 || h < G) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p[h], vf[e], acc[h][e]);
+          }
+        }
+      }
+    };
 
-  int blk = blk_first + w;
-  int32_t page_c = 0, slot_c = 0, page_n = 0, slot_n = 0;
-  if (blk < blk_end) {
+    // ---- Q rows of the group, the first block's page lookup and its keys, all in flight
+    // together (the Q loads go first; their LDS store waits only for them).  No load
+    // below sits behind a branch: a load on one side of a branch makes the compiler wait
+    // for every outstanding load where the paths join, which would serialise the pipeline.
+    const uint16_t* qsrc = a.q + ((int64_t)sg.b * a.num_qo_heads + (int64_t)sg.kvh * G) * DQK;
+    u32x4_t qv_pre[QV];
+#pragma unroll
+    for (int r = 0; r < QV; ++r) {
+      const int idx = lane + 64 * r;
+      const int row = idx / (DQK / 8), c8 = idx % (DQK / 8);
+      qv_pre[r] = *(const u32x4_t*)(qsrc + (row < G ? row : G - 1) * DQK + c8 * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int blk = t0 / 16;
+    const int blk_end = (t1 + 15) / 16;
+    int32_t page_c, slot_c;
     block_page(blk, page_c, slot_c);
     issue_k(page_c, slot_c);
-    if (blk + NW < blk_end) block_page(blk + NW, page_n, slot_n);
-    issue_v(page_c, slot_c);
-  }
-
-  for (; blk < blk_end; blk += NW) {
-    const bool has_next = blk + NW < blk_end;
-    // ---- S^T = K Q^T for the 16 keys of this block (keys on rows, heads on columns).
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < NSTEP; ++j) {
-      bf16x8_t kf;
-      if constexpr (KVB == 2) {
-        kf = __builtin_bit_cast(bf16x8_t, kbuf[j]);
-      } else {
-        const u32x4_t raw = kbuf[j >> 1];
-        const u32x2_t lo = fp8x4_to_bf16x4(raw[(j & 1) * 2 + 0]);
-        const u32x2_t hi = fp8x4_to_bf16x4(raw[(j & 1) * 2 + 1]);
-        const u32x4_t packed = {lo[0], lo[1], hi[0], hi[1]};
-        kf = __builtin_bit_cast(bf16x8_t, packed);
-      }
-      const u32x4_t qv = *(const u32x4_t*)(q_lds + n * QPITCH + q_dim_of_step<KVB>(j, g4));
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, __builtin_bit_cast(bf16x8_t, qv), s, 0, 0, 0);
+    for (int r = 0; r < QV; ++r) {
+      const int idx = lane + 64 * r;
+      const int row = idx / (DQK / 8), c8 = idx % (DQK / 8);
+      if (row < G) *(u32x4_t*)(q_lds + row * QPITCH + c8 * 8) = qv_pre[r];
     }
-    // ---- prefetch: next block's keys (its page index was loaded one iteration ago) and
-    // the page index of the block after it.
-    if (has_next) issue_k(page_n, slot_n);
-    int32_t page_nn = 0, slot_nn = 0;
-    if (blk + 2 * NW < blk_end) block_page(blk + 2 * NW, page_nn, slot_nn);
-
-    // ---- online softmax over the block; lane (g4, n) holds keys 4*g4 + i of head n.
-    float sc[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = blk * 16 + 4 * g4 + i;
-      sc[i] = (t >= t0 && t < t1) ? s[i] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sc[i]);
-    }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = exp2f(sc[i] - m_use);
-      psum += p;
-      p_lds[w][4 * g4 + i][n] = p;
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (g4 == 0) alpha_lds[w][n] = alpha;
     wave_lds_sync();
 
-    // ---- rescale the accumulators, then O += P V.
-    {
-      float al[GMAX];
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h) al[h] = alpha_lds[w][h];
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
-    }
-#pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-      const int tk = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
-      float p[GMAX];
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h) p[h] = p_lds[w][tk][h];
-      float vf[8];
-      if constexpr (KVB == 2) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vf[2 * e] = bf16_lo(vbuf[i][e]);
-          vf[2 * e + 1] = bf16_hi(vbuf[i][e]);
-        }
-      } else {
-        fp8x4_to_f32(vbuf[i][0], vf);
-        fp8x4_to_f32(vbuf[i][1], vf + 4);
-      }
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h) {
-        if (GMAX == 1 || h < G) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p[h], vf[e], acc[h][e]);
-        }
-      }
-    }
-    wave_lds_sync();  // p_lds / alpha_lds are rewritten next iteration
-    if (has_next) issue_v(page_n, slot_n);
-    page_n = page_nn;
-    slot_n = slot_nn;
-  }
-
-  // ---- per-wave totals: the sum over the 4 lanes of a head, and (two rows per V load)
-  // the accumulator halves.
-  l_run += shfl_xor_f(l_run, 16);
-  l_run += shfl_xor_f(l_run, 32);
-  if constexpr (RPI == 2) {
+    float m_run = -INFINITY;  // per head n, log2 domain
+    float l_run = 0.f;        // this lane's share of the sum for head n
 #pragma unroll
     for (int h = 0; h < GMAX; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += shfl_xor_f(acc[h][e], 32);
-  }
-  if (g4 == 0) {
-    ml_lds[0][w][n] = m_run;
-    ml_lds[1][w][n] = l_run;
-  }
-  __syncthreads();
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
-  // ---- merge the 4 waves: common max per head, rescale, then a fixed-order tree sum.
-  float mtot[GMAX], ltot[GMAX];
-#pragma unroll
-  for (int h = 0; h < GMAX; ++h) {
-    float mm = -INFINITY;
-#pragma unroll
-    for (int x = 0; x < NW; ++x) mm = fmaxf(mm, ml_lds[0][x][h]);
-    const float mu = mm == -INFINITY ? 0.f : mm;
-    float ll = 0.f;
-#pragma unroll
-    for (int x = 0; x < NW; ++x) ll += ml_lds[1][x][h] * exp2f(ml_lds[0][x][h] - mu);
-    const float f = exp2f(ml_lds[0][w][h] - mu);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] *= f;
-    mtot[h] = mm;
-    ltot[h] = ll;
-  }
-  const bool writer = lane < LPR;
-  auto publish = [&](int slot) {
-    if (writer) {
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h) {
-        *(f32x4_t*)&merge_lds[slot][h][lane * 8] = f32x4_t{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-        *(f32x4_t*)&merge_lds[slot][h][lane * 8 + 4] = f32x4_t{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+    int iter = 0;
+    for (; blk < blk_end; ++blk, ++iter) {
+      const int cur = iter & 1;
+      // ---- page index of the next block, which this iteration's key prefetch needs.
+      int32_t page_n, slot_n;
+      block_page(blk + 1, page_n, slot_n);
+      // ---- P V of the previous block, then this block's V rows (used next iteration).
+      if (iter > 0) {
+        pv(cur ^ 1);
+        wave_lds_sync();
       }
-    }
-  };
-  auto absorb = [&](int slot) {
-    if (writer) {
+      issue_v(page_c, slot_c);
+      // ---- S^T = K Q^T for the 16 keys of this block (keys on rows, heads on columns).
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < GMAX; ++h) {
-        const f32x4_t x0 = *(const f32x4_t*)&merge_lds[slot][h][lane * 8];
-        const f32x4_t x1 = *(const f32x4_t*)&merge_lds[slot][h][lane * 8 + 4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[h][e] += x0[e];
-          acc[h][e + 4] += x1[e];
-        }
-      }
-    }
-  };
-  if (w >= 2) publish(w - 2);
-  __syncthreads();
-  if (w < 2) absorb(w);
-  __syncthreads();
-  if (w == 1) publish(0);
-  __syncthreads();
-  if (w != 0) return;
-  absorb(0);
-
-  // ---- wave 0 writes the chunk result: final output, or a partial for the merge.
-  const int h0 = kvh * G;
-  if (it.slot < 0) {
-    if (writer) {
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h) {
-        if (h >= G) continue;
-        const float inv = ltot[h] > 0.f ? a.v_scale / ltot[h] : 0.f;
-        const int64_t off = ((int64_t)it.b * a.num_qo_heads + h0 + h) * DVO + lane * 8;
-        if (a.out_fp32) {
-          float* o = (float*)a.out + off;
-          *(f32x4_t*)o = f32x4_t{acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv};
-          *(f32x4_t*)(o + 4) = f32x4_t{acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv};
+      for (int j = 0; j < NSTEP; ++j) {
+        bf16x8_t kf;
+        if constexpr (KVB == 2) {
+          kf = __builtin_bit_cast(bf16x8_t, kbuf[j]);
         } else {
-          u32x4_t pk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pk[e] = pack_bf16(acc[h][2 * e] * inv, acc[h][2 * e + 1] * inv);
-          *(u32x4_t*)((uint16_t*)a.out + off) = pk;
+          const u32x4_t raw = kbuf[j >> 1];
+          const u32x2_t lo = fp8x4_to_bf16x4(raw[(j & 1) * 2 + 0]);
+          const u32x2_t hi = fp8x4_to_bf16x4(raw[(j & 1) * 2 + 1]);
+          const u32x4_t packed = {lo[0], lo[1], hi[0], hi[1]};
+          kf = __builtin_bit_cast(bf16x8_t, packed);
         }
+        const u32x4_t qv = *(const u32x4_t*)(q_lds + qrow * QPITCH + q_dim_of_step<KVB>(j, g4));
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, __builtin_bit_cast(bf16x8_t, qv), s, 0, 0, 0);
       }
+      // ---- prefetch the next block's keys.
+      issue_k(page_n, slot_n);
+
+      // ---- online softmax over the block; lane (g4, n) holds keys 4*g4 + i of head n.
+      float sc[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = blk * 16 + 4 * g4 + i;
+        sc[i] = (t >= t0 && t < t1) ? s[i] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[i]);
+      }
+      mx = max_xor16(mx);
+      mx = max_xor32(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f(m_run - m_new);  // every block holds a visible key
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(sc[i] - m_new);
+        psum += p;
+        p_lds[cur][4 * g4 + i][n] = p;
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      if (g4 == 0) alpha_lds[cur][n] = alpha;
+      wave_lds_sync();
+      page_c = page_n;
+      slot_c = slot_n;
+      // ---- issue priority from the workgroup's progress (plain LDS words; a stale value
+      // only delays the adjustment by an iteration).
+      ++done;
+      if (lane == 0) progress[wv] = done;
+      int sum = 0;
+#pragma unroll
+      for (int x = 0; x < NWG; ++x) sum += progress[x];
+      if (done * NWG < sum) __builtin_amdgcn_s_setprio(3);
+      else __builtin_amdgcn_s_setprio(0);
     }
-    if (a.lse && lane < G) {
-      float lv = -INFINITY;
+    pv((iter - 1) & 1);
+
+    // ---- segment result: the sum over the 4 lanes of a head, and (two rows per V load)
+    // the accumulator halves.  Lane h < 16 then holds head h's max and sum.
+    l_run = sum_xor32(sum_xor16(l_run));
+    if constexpr (RPI == 2) {
 #pragma unroll
       for (int h = 0; h < GMAX; ++h)
-        if (h == lane && ltot[h] > 0.f) lv = (mtot[h] + log2f(ltot[h])) * kLn2;
-      a.lse[(int64_t)it.b * a.num_qo_heads + h0 + lane] = lv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] += shfl_xor_f(acc[h][e], 32);
     }
-  } else {
-    if (writer) {
+    const int h0 = sg.kvh * G;
+    if (lane < LPR) {
 #pragma unroll
       for (int h = 0; h < GMAX; ++h) {
         if (h >= G) continue;
-        const float inv = ltot[h] > 0.f ? a.v_scale / ltot[h] : 0.f;
-        float* o = a.part_o + ((int64_t)it.slot * a.num_qo_heads + h0 + h) * DVO + lane * 8;
-        *(f32x4_t*)o = f32x4_t{acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv};
-        *(f32x4_t*)(o + 4) = f32x4_t{acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv};
+        const float lh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_run), h));
+        const float inv = lh > 0.f ? a.v_scale / lh : 0.f;
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = acc[h][e] * inv;
+        if (sg.slot >= 0) {
+          float* dst = a.part_o + ((int64_t)sg.slot * G + h) * DVO + lane * 8;
+          *(f32x4_t*)dst = f32x4_t{o[0], o[1], o[2], o[3]};
+          *(f32x4_t*)(dst + 4) = f32x4_t{o[4], o[5], o[6], o[7]};
+        } else {
+          const int64_t off = ((int64_t)sg.b * a.num_qo_heads + h0 + h) * DVO + lane * 8;
+          if (a.out_fp32) {
+            float* dst = (float*)a.out + off;
+            *(f32x4_t*)dst = f32x4_t{o[0], o[1], o[2], o[3]};
+            *(f32x4_t*)(dst + 4) = f32x4_t{o[4], o[5], o[6], o[7]};
+          } else {
+            u32x4_t pk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pk[e] = pack_bf16(o[2 * e], o[2 * e + 1]);
+            *(u32x4_t*)((uint16_t*)a.out + off) = pk;
+          }
+        }
       }
     }
     if (lane < G) {
-      float lv = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h)
-        if (h == lane && ltot[h] > 0.f) lv = mtot[h] + log2f(ltot[h]);
-      a.part_lse[(int64_t)it.slot * a.num_qo_heads + h0 + lane] = lv;
+      const float lg = m_run + log2f(l_run);  // log2 domain; l_run > 0 here
+      if (sg.slot >= 0) a.part_lse[(int64_t)sg.slot * G + lane] = lg;
+      else if (a.lse) a.lse[(int64_t)sg.b * a.num_qo_heads + h0 + lane] = lg * kLn2;
     }
   }
 }
 
 struct MergeArgs {
   const MergeItem* merges;
-  const float* part_o;
-  const float* part_lse;   // log2 domain
+  const float* part_o;     // [slots, G, DVO]
+  const float* part_lse;   // [slots, G], log2 domain
   void* out;
   float* lse;
   int32_t num_qo_heads;
+  int32_t group;
   int32_t out_fp32;
 };
 
-// One wave per (split request, query head): log-sum-exp weights over the chunks, in chunk
-// order, then the weighted sum of the chunk outputs.
+// One wave per (merged (request, KV head), head of the group): log-sum-exp weights over
+// the segments, in segment order, then the weighted sum of the segment outputs.  A pair
+// with no segments (no keys) gets a zero output and lse -inf.
 template <int DVO>
 __global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a) {
   constexpr int EPT = DVO / 64;
   const MergeItem mi = a.merges[blockIdx.x];
   const int h = blockIdx.y;
   const int lane = threadIdx.x;
-  const int hq = a.num_qo_heads;
+  const int G = a.group;
   float mx = -INFINITY;
-  for (int c = 0; c < mi.num_chunks; ++c)
-    mx = fmaxf(mx, a.part_lse[(int64_t)(mi.slot_begin + c) * hq + h]);
+  for (int c = 0; c < mi.num_slots; ++c)
+    mx = fmaxf(mx, a.part_lse[(int64_t)(mi.slot_begin + c) * G + h]);
   const float mu = mx == -INFINITY ? 0.f : mx;
   float o[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) o[e] = 0.f;
   float wsum = 0.f;
-  for (int c = 0; c < mi.num_chunks; ++c) {
-    const int64_t row = (int64_t)(mi.slot_begin + c) * hq + h;
-    const float lc = a.part_lse[row];
-    if (lc == -INFINITY) continue;
-    const float wgt = exp2f(lc - mu);
+  for (int c = 0; c < mi.num_slots; ++c) {
+    const int64_t row = (int64_t)(mi.slot_begin + c) * G + h;
+    const float wgt = exp2f(a.part_lse[row] - mu);
     wsum += wgt;
     const float* src = a.part_o + row * DVO + lane * EPT;
 #pragma unroll
@@ -413,7 +383,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a) {
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const int64_t off = ((int64_t)mi.b * hq + h) * DVO + lane * EPT;
+  const int hq = a.num_qo_heads;
+  const int64_t off = ((int64_t)mi.b * hq + mi.kvh * G + h) * DVO + lane * EPT;
   if (a.out_fp32) {
     float* dst = (float*)a.out + off;
 #pragma unroll
@@ -425,7 +396,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a) {
     for (int e = 0; e < EPT; e += 2) dst[e / 2] = pack_bf16(o[e] * inv, o[e + 1] * inv);
   }
   if (a.lse && lane == 0)
-    a.lse[(int64_t)mi.b * hq + h] = wsum > 0.f ? (mx + log2f(wsum)) * kLn2 : -INFINITY;
+    a.lse[(int64_t)mi.b * hq + mi.kvh * G + h] = wsum > 0.f ? (mx + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
 // Copies the rows of one (request, KV head) in logical order, through the same address
@@ -462,10 +433,12 @@ __global__ void fp8_to_f32_kernel(const uint8_t* codes, float* out, int n) {
 template <int DQK, int DVO, int KVB>
 static hipError_t launch_decode_dims(const DecodeArgs& a, int gmax, int grid, hipStream_t s) {
   switch (gmax) {
-    case 1: decode_partial_kernel<DQK, DVO, KVB, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: decode_partial_kernel<DQK, DVO, KVB, 2><<<grid, 256, 0, s>>>(a); break;
-    case 4: decode_partial_kernel<DQK, DVO, KVB, 4><<<grid, 256, 0, s>>>(a); break;
-    default: decode_partial_kernel<DQK, DVO, KVB, 8><<<grid, 256, 0, s>>>(a); break;
+    case 1: decode_partial_kernel<DQK, DVO, KVB, 1><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
+    case 2: decode_partial_kernel<DQK, DVO, KVB, 2><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
+    case 3: decode_partial_kernel<DQK, DVO, KVB, 3><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
+    case 4: decode_partial_kernel<DQK, DVO, KVB, 4><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
+    case 6: decode_partial_kernel<DQK, DVO, KVB, 6><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
+    default: decode_partial_kernel<DQK, DVO, KVB, 8><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }
@@ -510,7 +483,7 @@ static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_
   if (st != PA_OK) return st;
   if ((st = check_params(params, cache, kMaxDecodeGroup)) != PA_OK) return st;
   if ((st = check_plan_matches(plan, 1, params, cache, table, workspace_bytes)) != PA_OK) return st;
-  if (plan->num_items == 0) return PA_OK;
+  if (plan->num_items == 0 && plan->num_merges == 0) return PA_OK;
   if (!q || !out) return fail(PA_ERR_INVALID_ARG, "q or out is NULL");
   if (!workspace) return fail(PA_ERR_INVALID_ARG, "workspace is NULL");
   if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)workspace) & 15)
@@ -518,13 +491,13 @@ static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_
   if ((uintptr_t)lse & 3) return fail(PA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
 
   const int group = params->num_qo_heads / cache->num_kv_heads;
-  const int gmax = group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8;
+  const int gmax = group <= 4 ? group : group <= 6 ? 6 : 8;
   char* ws = (char*)workspace;
   hipStream_t s = (hipStream_t)stream;
   const bool out_fp32 = params->out_dtype == PA_DTYPE_FP32;
   float* part_o = (float*)(ws + plan->partial_o_offset);
   float* part_lse = (float*)(ws + plan->partial_lse_offset);
-  if (run_partial) {
+  if (run_partial && plan->num_workers > 0) {
     DecodeArgs a;
     a.q = (const uint16_t*)q;
     a.k = (const char*)cache->k;
@@ -533,20 +506,21 @@ static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_
     a.v_sp = cache->v_stride_page; a.v_sh = cache->v_stride_head; a.v_st = cache->v_stride_token;
     a.kv_indptr = table->kv_indptr;
     a.kv_indices = table->kv_indices;
-    a.items = (const DecodeItem*)(ws + plan->items_offset);
+    a.segs = (const DecodeSegment*)(ws + plan->items_offset);
+    a.wave_begin = (const int32_t*)(ws + plan->workers_offset);
+    a.num_waves = plan->num_workers;
     a.out = out;
     a.lse = lse;
     a.part_o = part_o;
     a.part_lse = part_lse;
     a.num_qo_heads = params->num_qo_heads;
-    a.num_kv_heads = cache->num_kv_heads;
     a.group = group;
     a.page_size = cache->page_size;
     a.out_fp32 = out_fp32;
     a.scale_log2 = params->sm_scale * cache->k_scale * kLog2e;
     a.v_scale = cache->v_scale;
     const int kvb = cache->kv_dtype == PA_DTYPE_FP8_E4M3FN ? 1 : 2;
-    const int grid = plan->num_items * cache->num_kv_heads;
+    const int grid = (plan->num_workers + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup;
     hipError_t e = launch_decode(a, cache->head_dim_qk, cache->head_dim_vo, kvb, gmax, grid, s);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
     count_launches(1);
@@ -559,8 +533,9 @@ static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_
     m.out = out;
     m.lse = lse;
     m.num_qo_heads = params->num_qo_heads;
+    m.group = group;
     m.out_fp32 = out_fp32;
-    dim3 mg(plan->num_merges, params->num_qo_heads);
+    dim3 mg(plan->num_merges, group);
     if (cache->head_dim_vo == 512) decode_merge_kernel<512><<<mg, 64, 0, s>>>(m);
     else decode_merge_kernel<256><<<mg, 64, 0, s>>>(m);
     hipError_t e = hipGetLastError();

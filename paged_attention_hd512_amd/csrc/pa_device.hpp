@@ -121,6 +121,14 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads in flight stay in flight
+// (a full __syncthreads would first wait for every outstanding vector memory load).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Cross-lane max / sum with the lane 32 (or 16) apart, on the VALU: each swap returns, per
 // lane, the lane's own value in one result and its partner's in the other.
 __device__ __forceinline__ float max_xor32(float v) {

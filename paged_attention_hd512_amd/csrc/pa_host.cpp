@@ -248,74 +248,107 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
 
   const int window = params->window > 0 ? params->window : 0;
   const int P = cache->page_size;
+  const int32_t hkv = cache->num_kv_heads;
   std::vector<int64_t> len(batch), start(batch), nblk(batch);
-  int64_t total_blocks = 0, max_len = 0;
+  int64_t max_len = 0;
   for (int32_t b = 0; b < batch; ++b) {
     len[b] = kv_len_of(kv_indptr_host, kv_last_page_len_host, b, P);
     start[b] = window > 0 ? std::max<int64_t>(0, len[b] - window) : 0;
     const int64_t fb = start[b] / kBlockTokens;
     const int64_t eb = (len[b] + kBlockTokens - 1) / kBlockTokens;
     nblk[b] = std::max<int64_t>(0, eb - fb);
-    total_blocks += nblk[b];
     max_len = std::max(max_len, len[b]);
   }
-  std::vector<int32_t> chunks(batch);
-  int64_t chunk_blocks = 0;
+  // Flattened units: (b, h, block) in that order; pair i = b * hkv + h starts at origin[i].
+  const int64_t npairs = (int64_t)batch * hkv;
+  std::vector<int64_t> origin(npairs + 1);
+  origin[0] = 0;
+  for (int64_t i = 0; i < npairs; ++i) origin[i + 1] = origin[i] + nblk[i / hkv];
+  const int64_t total = origin[npairs];
+
+  std::vector<std::pair<int64_t, int64_t>> pieces;
   if (num_splits > 0) {
-    for (int32_t b = 0; b < batch; ++b)
-      chunks[b] = (int32_t)std::max<int64_t>(1, std::min<int64_t>(num_splits, nblk[b]));
+    for (int64_t i = 0; i < npairs; ++i) {
+      const int64_t n = nblk[i / hkv];
+      const int64_t c = std::min<int64_t>(num_splits, n);
+      for (int64_t k = 0; k < c; ++k)
+        pieces.emplace_back(origin[i] + n * k / c, origin[i] + n * (k + 1) / c);
+    }
   } else {
-    const int64_t target_chunks =
-        (kTargetWorkgroups + cache->num_kv_heads - 1) / cache->num_kv_heads;
-    chunk_blocks = std::max<int64_t>(kMinChunkBlocks, (total_blocks + target_chunks - 1) / target_chunks);
-    for (int32_t b = 0; b < batch; ++b)
-      chunks[b] = (int32_t)std::max<int64_t>(
-          1, std::min<int64_t>(kMaxSplits, (nblk[b] + chunk_blocks - 1) / chunk_blocks));
+    const int64_t np = std::min<int64_t>(kDecodeWaveSlots, (total + kMinPieceBlocks - 1) / kMinPieceBlocks);
+    for (int64_t k = 0; k < np; ++k) pieces.emplace_back(total * k / np, total * (k + 1) / np);
   }
 
-  struct Tmp { DecodeItem it; int32_t c; };
-  std::vector<Tmp> items;
+  // Cut each piece into segments at (b, h) boundaries; pieces run in flattened order, so
+  // the pair index only moves forward.
+  std::vector<std::vector<DecodeSegment>> piece_segs(pieces.size());
+  std::vector<int32_t> seg_count(npairs, 0);
+  int64_t pair = 0;
+  for (size_t k = 0; k < pieces.size(); ++k) {
+    int64_t u = pieces[k].first;
+    const int64_t u1 = pieces[k].second;
+    while (u < u1) {
+      while (origin[pair + 1] <= u) ++pair;  // skips empty ranges too
+      const int32_t b = (int32_t)(pair / hkv), h = (int32_t)(pair % hkv);
+      const int64_t e = std::min<int64_t>(u1, origin[pair + 1]);
+      const int64_t fb = start[b] / kBlockTokens;
+      const int64_t t0 = std::max<int64_t>(start[b], (fb + u - origin[pair]) * kBlockTokens);
+      const int64_t t1 = std::min<int64_t>(len[b], (fb + e - origin[pair]) * kBlockTokens);
+      DecodeSegment sg;
+      memset(&sg, 0, sizeof(sg));
+      sg.b = b; sg.kvh = h; sg.t_begin = (int32_t)t0; sg.t_end = (int32_t)t1; sg.slot = -1;
+      piece_segs[k].push_back(sg);
+      ++seg_count[pair];
+      u = e;
+    }
+  }
+  // Slots, numbered in (b, h) order; merge entries for split and for empty pairs.
+  std::vector<int32_t> first_slot(npairs, -1);
   std::vector<MergeItem> merges;
   int32_t next_slot = 0;
-  for (int32_t b = 0; b < batch; ++b) {
-    const int32_t cb = chunks[b];
-    const int64_t fb = start[b] / kBlockTokens;
-    int32_t slot0 = -1;
-    if (cb > 1) {
-      slot0 = next_slot;
-      merges.push_back(MergeItem{b, next_slot, cb, 0});
-      next_slot += cb;
-    }
-    for (int32_t c = 0; c < cb; ++c) {
-      const int64_t lo = fb + (nblk[b] * c) / cb;
-      const int64_t hi = fb + (nblk[b] * (c + 1)) / cb;
-      int64_t t0 = std::max<int64_t>(start[b], lo * kBlockTokens);
-      int64_t t1 = std::min<int64_t>(len[b], hi * kBlockTokens);
-      if (len[b] == 0) t0 = t1 = 0;
-      items.push_back(Tmp{DecodeItem{b, (int32_t)t0, (int32_t)t1, cb == 1 ? -1 : slot0 + c}, c});
+  for (int64_t i = 0; i < npairs; ++i) {
+    const int32_t b = (int32_t)(i / hkv), h = (int32_t)(i % hkv);
+    if (seg_count[i] == 0) {
+      merges.push_back(MergeItem{b, h, next_slot, 0});
+    } else if (seg_count[i] > 1) {
+      first_slot[i] = next_slot;
+      merges.push_back(MergeItem{b, h, next_slot, seg_count[i]});
+      next_slot += seg_count[i];
     }
   }
-  // Longest first; the generation order (b, c) breaks ties.
-  std::stable_sort(items.begin(), items.end(), [](const Tmp& a, const Tmp& b) {
-    return (a.it.t_end - a.it.t_begin) > (b.it.t_end - b.it.t_begin);
+  std::vector<int32_t> used(npairs, 0);
+  for (auto& segs : piece_segs)
+    for (auto& sg : segs) {
+      const int64_t i = (int64_t)sg.b * hkv + sg.kvh;
+      if (first_slot[i] >= 0) sg.slot = first_slot[i] + used[i]++;
+    }
+  // Launch order: longest piece first, ties in piece order.
+  std::vector<int32_t> order(pieces.size());
+  for (size_t k = 0; k < order.size(); ++k) order[k] = (int32_t)k;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    return pieces[x].second - pieces[x].first > pieces[y].second - pieces[y].first;
   });
+  int64_t num_segs = 0;
+  for (auto& segs : piece_segs) num_segs += (int64_t)segs.size();
 
   plan_header(plan, 1, params, cache, batch);
-  plan->num_items = (int32_t)items.size();
+  plan->num_items = (int32_t)num_segs;
+  plan->num_workers = (int32_t)pieces.size();
   plan->num_slots = next_slot;
   plan->num_merges = (int32_t)merges.size();
   plan->block_tokens = kBlockTokens;
-  plan->chunk_blocks = (int32_t)chunk_blocks;
+  plan->chunk_blocks = pieces.empty() ? 0 : (int32_t)(pieces[order[0]].second - pieces[order[0]].first);
   plan->num_splits = num_splits;
   plan->max_kv_len = (int32_t)max_len;
   plan->items_offset = 0;
-  plan->merges_offset = align_up((int64_t)items.size() * sizeof(DecodeItem), 16);
+  plan->workers_offset = align_up(num_segs * (int64_t)sizeof(DecodeSegment), 16);
+  plan->merges_offset = align_up(plan->workers_offset + ((int64_t)pieces.size() + 1) * 4, 16);
   plan->plan_bytes = align_up(plan->merges_offset + (int64_t)merges.size() * sizeof(MergeItem), 256);
   plan->partial_o_offset = plan->plan_bytes;
-  const int64_t o_bytes = (int64_t)next_slot * params->num_qo_heads * cache->head_dim_vo * 4;
+  const int32_t group = params->num_qo_heads / hkv;
+  const int64_t o_bytes = (int64_t)next_slot * group * cache->head_dim_vo * 4;
   plan->partial_lse_offset = align_up(plan->partial_o_offset + o_bytes, 256);
-  plan->workspace_bytes =
-      align_up(plan->partial_lse_offset + (int64_t)next_slot * params->num_qo_heads * 4, 256);
+  plan->workspace_bytes = align_up(plan->partial_lse_offset + (int64_t)next_slot * group * 4, 256);
 
   if (!plan_buf_host) return PA_OK;  // sizing call
   if ((int64_t)plan_buf_bytes < plan->plan_bytes)
@@ -323,8 +356,14 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
                 plan_buf_bytes, (long long)plan->plan_bytes);
   char* buf = (char*)plan_buf_host;
   memset(buf, 0, (size_t)plan->plan_bytes);
-  DecodeItem* out_items = (DecodeItem*)(buf + plan->items_offset);
-  for (size_t i = 0; i < items.size(); ++i) out_items[i] = items[i].it;
+  DecodeSegment* out_segs = (DecodeSegment*)(buf + plan->items_offset);
+  int32_t* wave_begin = (int32_t*)(buf + plan->workers_offset);
+  int32_t n = 0;
+  for (size_t w = 0; w < order.size(); ++w) {
+    wave_begin[w] = n;
+    for (const DecodeSegment& sg : piece_segs[order[w]]) out_segs[n++] = sg;
+  }
+  wave_begin[order.size()] = n;
   memcpy(buf + plan->merges_offset, merges.data(), merges.size() * sizeof(MergeItem));
   return PA_OK;
 }

@@ -8,10 +8,11 @@
 namespace pa {
 
 // Decode partition: keys are grouped in logical blocks of 16 tokens (one MFMA tile of
-// keys); a work item is a contiguous run of blocks of one request.
+// keys); the work units are (request, KV head, block) triples, and each wave of the
+// partial kernel runs a contiguous piece of them.
 constexpr int kBlockTokens = 16;
-constexpr int kTargetWorkgroups = 2048;  // adaptive split aims at about this many
-constexpr int kMinChunkBlocks = 8;
+constexpr int kDecodeWaveSlots = 2048;   // 256 CUs x 4 SIMDs x 2 waves (register-bound)
+constexpr int kMinPieceBlocks = 8;       // balanced pieces hold at least this many blocks
 constexpr int kMaxSplits = 64;
 constexpr int kMaxDecodeGroup = 8;       // query heads per KV head in decode
 constexpr int kMaxPrefillGroup = 16;
@@ -19,18 +20,20 @@ constexpr int kMaxPrefillGroup = 16;
 // Prefill: query rows per tile ((token, head) pairs of one head group).
 constexpr int kPrefillTileRows = 128;
 
-struct DecodeItem {   // 16 bytes
-  int32_t b;          // request
-  int32_t t_begin;    // first visible key of the chunk
-  int32_t t_end;      // one past the last key of the chunk
-  int32_t slot;       // partial slot, or -1: write the final output directly
+struct DecodeSegment {  // 32 bytes: blocks of one (request, KV head) run by one wave
+  int32_t b;             // request
+  int32_t kvh;           // KV head
+  int32_t t_begin;       // first key of the segment
+  int32_t t_end;         // one past the last key (t_end > t_begin)
+  int32_t slot;          // partial slot, or -1: write the final output directly
+  int32_t pad[3];
 };
 
-struct MergeItem {    // 16 bytes
+struct MergeItem {       // 16 bytes
   int32_t b;
+  int32_t kvh;
   int32_t slot_begin;
-  int32_t num_chunks;
-  int32_t pad;
+  int32_t num_slots;     // 0: the request has no keys (zero output, lse -inf)
 };
 
 struct PrefillItem {  // 32 bytes

@@ -60,8 +60,9 @@ class pa_plan(Structure):
                 ("causal", c_int32), ("num_items", c_int32), ("num_slots", c_int32),
                 ("num_merges", c_int32), ("block_tokens", c_int32), ("chunk_blocks", c_int32),
                 ("num_splits", c_int32), ("tile_rows", c_int32), ("total_q", c_int32),
-                ("max_kv_len", c_int32), ("reserved0", c_int32), ("plan_bytes", c_int64),
+                ("max_kv_len", c_int32), ("num_workers", c_int32), ("plan_bytes", c_int64),
                 ("items_offset", c_int64), ("merges_offset", c_int64),
+                ("workers_offset", c_int64),
                 ("partial_o_offset", c_int64), ("partial_lse_offset", c_int64),
                 ("workspace_bytes", c_int64)]
 
@@ -374,15 +375,21 @@ class PagedPrefill:
         return out, lse
 
 
-def decode_items(plan, plan_buf):
-    """Work items of a decode plan as a [num_items, 4] int32 array (b, t0, t1, slot)."""
-    off = plan.items_offset
-    return plan_buf[off:off + 16 * plan.num_items].view(np.int32).reshape(-1, 4)
+def decode_waves(plan, plan_buf):
+    """Segments of a decode plan per wave, in launch order: a list of [k, 5] int32 arrays
+    of (b, kv_head, t_begin, t_end, slot)."""
+    segs = plan_buf[plan.items_offset:plan.items_offset + 32 * plan.num_items]
+    segs = segs.view(np.int32).reshape(-1, 8)[:, :5]
+    off = plan.workers_offset
+    begin = plan_buf[off:off + 4 * (plan.num_workers + 1)].view(np.int32)
+    return [segs[begin[w]:begin[w + 1]] for w in range(plan.num_workers)]
 
 
 def decode_merges(plan, plan_buf):
+    """Merge entries of a decode plan as a [num_merges, 4] int32 array
+    (b, kv_head, slot_begin, num_slots)."""
     off = plan.merges_offset
-    return plan_buf[off:off + 16 * plan.num_merges].view(np.int32).reshape(-1, 4)[:, :3]
+    return plan_buf[off:off + 16 * plan.num_merges].view(np.int32).reshape(-1, 4)
 
 
 def prefill_items(plan, plan_buf):

@@ -262,8 +262,10 @@ WORKLOADS = {
     "tiny_decode": dict(kind="decode", kv_lens=[37, 64], num_qo_heads=8, num_kv_heads=1,
                         head_dim_qk=512, page_size=16, out_dtype="fp32", num_splits=1,
                         slack_pages=9, seed=1001),
+    # The GQA decode runs the balanced partition (num_splits 0); variant "splitk8" runs the
+    # same inputs with every request cut into exactly 8 key chunks.
     "gqa_decode": dict(kind="decode", batch=32, len_range=(1024, 8192), num_qo_heads=24,
-                       num_kv_heads=4, head_dim_qk=512, page_size=16, num_splits=8,
+                       num_kv_heads=4, head_dim_qk=512, page_size=16, num_splits=0,
                        seed=1002),
     "fp8_decode": dict(kind="decode", batch=64, len_range=(4096, 32768), num_qo_heads=12,
                        num_kv_heads=4, head_dim_qk=512, page_size=64, kv_dtype="fp8",
@@ -290,7 +292,10 @@ def decode_workload(name, device="cpu", variant=None):
     else:
         kv_lens = w.pop("kv_lens")
     variants = w.pop("variants", None)
-    if variants is not None:
+    if isinstance(variant, str):
+        assert variant.startswith("splitk"), variant
+        w["num_splits"] = int(variant[len("splitk"):])
+    elif variants is not None:
         dim, page = variants[0] if variant is None else variant
         w["head_dim_qk"], w["page_size"] = dim, page
     return make_decode_case(kv_lens, seed=seed, device=device, name=name, **w)

@@ -132,8 +132,25 @@ def test_page_relabeling_gives_bit_identical_output_and_runs_are_deterministic()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_waves_that_run_several_segments():
+    """Short requests: balanced pieces of 8 blocks span several (request, KV head) pairs,
+    so waves run several segments, some pairs are merged and some are written directly."""
+    say("waves with several segments")
+    lens = list(np.random.default_rng(11).integers(1, 70, size=40)) + [0, 700]
+    c = make_decode_case(lens, 12, 3, 512, 16, num_splits=0, out_dtype="fp32", seed=12,
+                         device=dev())
+    runner, o, lse = gpu_decode(c)
+    waves = pa.decode_waves(runner.plan, runner.plan_buf)
+    assert max(len(w) for w in waves) >= 3
+    slots = np.concatenate([w[:, 4] for w in waves])
+    assert (slots < 0).any() and (slots >= 0).any()
+    ref, ref_lse = oracle_decode(c)
+    compare("several segments per wave", out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("name,variant", [("gqa_decode", None), ("fp8_decode", None),
+@pytest.mark.parametrize("name,variant", [("gqa_decode", None), ("gqa_decode", "splitk8"),
+                                          ("fp8_decode", None),
                                           ("window_decode", (512, 1)),
                                           ("window_decode", (512, 32)),
                                           ("window_decode", (256, 1)),

@@ -84,39 +84,64 @@ def test_decode_plan_matches_reference_partition(lens, P, window, splits, hkv):
     indptr, last = lens_to_table(lens, P)
     cache = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, int(indptr[-1]) + 1, hkv, P, 512)
     plan, buf = pa.pa_decode_plan(params(hq=hkv * 2, window=window), cache, indptr, last, splits)
-    items = pa.decode_items(plan, buf)
+    waves = pa.decode_waves(plan, buf)
     merges = pa.decode_merges(plan, buf)
-    ref_items, ref_merges = decode_partition_ref(lens, window, splits, hkv)
-    assert [tuple(r) for r in items.tolist()] == [tuple(r) for r in ref_items]
-    assert [tuple(r) for r in merges.tolist()] == [tuple(r) for r in ref_merges]
-    assert plan.num_items == len(ref_items) and plan.num_merges == len(ref_merges)
-    assert plan.num_slots == sum(m[2] for m in ref_merges)
-    hq, dvo = hkv * 2, 512
-    assert plan.partial_lse_offset - plan.partial_o_offset >= plan.num_slots * hq * dvo * 4
-    assert plan.workspace_bytes >= plan.partial_lse_offset + plan.num_slots * hq * 4
+    ref_waves, ref_merges = decode_partition_ref(lens, window, splits, hkv)
+    assert [[tuple(r) for r in w.tolist()] for w in waves] == ref_waves
+    assert [tuple(r) for r in merges.tolist()] == ref_merges
+    assert plan.num_workers == len(ref_waves) and plan.num_merges == len(ref_merges)
+    assert plan.num_items == sum(len(w) for w in ref_waves)
+    assert plan.num_slots == sum(m[3] for m in ref_merges)
+    group, dvo = 2, 512
+    assert plan.partial_lse_offset - plan.partial_o_offset >= plan.num_slots * group * dvo * 4
+    assert plan.workspace_bytes >= plan.partial_lse_offset + plan.num_slots * group * 4
 
 
 @pytest.mark.parametrize("lens,P,window,splits,hkv", DECODE_CASES)
 def test_reference_partition_covers_visible_keys_exactly(lens, P, window, splits, hkv):
-    items, merges = decode_partition_ref(lens, window, splits, hkv)
-    per_req = {}
-    for b, t0, t1, slot in items:
-        per_req.setdefault(b, []).append((t0, t1, slot))
+    """Every visible key of every (request, KV head) lies in exactly one segment; inner
+    cuts fall on 16-key blocks; balanced waves differ by at most one block; slots of a
+    merged pair are consecutive in key order; single-segment pairs write directly."""
+    waves, merges = decode_partition_ref(lens, window, splits, hkv)
+    per_pair = {}
+    for w in waves:
+        for b, h, t0, t1, slot in w:
+            per_pair.setdefault((b, h), []).append((t0, t1, slot))
+    merged = {(b, h): (s0, k) for b, h, s0, k in merges}
     for b, L in enumerate(lens):
         L = int(L)
-        chunks = sorted(per_req[b])
         start = max(0, L - window) if window > 0 else 0
-        if L == 0:
-            assert chunks == [(0, 0, -1)]
-            continue
-        assert chunks[0][0] == start and chunks[-1][1] == L
-        for (a0, a1, _), (b0, b1, _) in zip(chunks, chunks[1:]):
-            assert a1 == b0 and b0 % 16 == 0  # contiguous, inner cuts on 16-key blocks
-        assert all(t1 > t0 for t0, t1, _ in chunks)
-        if splits > 0:
-            assert len(chunks) <= splits
-    counts = [t1 - t0 for _, t0, t1, _ in items]
-    assert counts == sorted(counts, reverse=True)  # longest first
+        for h in range(hkv):
+            segs = sorted(per_pair.get((b, h), []))
+            if L == 0:
+                assert segs == [] and merged[(b, h)][1] == 0
+                continue
+            assert segs[0][0] == start and segs[-1][1] == L
+            for (a0, a1, _), (b0, b1, _) in zip(segs, segs[1:]):
+                assert a1 == b0 and b0 % 16 == 0
+            assert all(t1 > t0 for t0, t1, _ in segs)
+            if len(segs) == 1:
+                assert segs[0][2] == -1 and (b, h) not in merged
+            else:
+                s0, k = merged[(b, h)]
+                assert k == len(segs) and [s for _, _, s in segs] == list(range(s0, s0 + k))
+            if splits > 0:
+                assert len(segs) == min(splits, -(-L // 16) - start // 16)
+    blocks = [sum(-(-t1 // 16) - t0 // 16 for _, _, t0, t1, _ in w) for w in waves]
+    assert blocks == sorted(blocks, reverse=True)  # longest first
+    if splits == 0 and waves:
+        assert max(blocks) - min(blocks) <= 1 and len(waves) <= 2048
+    slots = sorted(s for w in waves for *_, s in w if s >= 0)
+    assert slots == list(range(len(slots)))  # every slot written once
+
+
+def test_balanced_partition_of_the_gqa_decode_shape_fills_every_wave_slot():
+    lens = list(np.random.default_rng(5).integers(1024, 8193, size=32))
+    waves, merges = decode_partition_ref(lens, 0, 0, 4)
+    total = 4 * sum(-(-int(L) // 16) for L in lens)
+    assert len(waves) == 2048
+    assert sum(sum(-(-t1 // 16) - t0 // 16 for _, _, t0, t1, _ in w) for w in waves) == total
+    assert all(1 <= len(w) <= 2 for w in waves)  # pieces of ~36 blocks vs pairs of >= 64
 
 
 PREFILL_CASES = [
