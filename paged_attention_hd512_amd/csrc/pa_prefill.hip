@@ -39,6 +39,11 @@ constexpr int kPrefillWaves = 8;          // 16 query rows each: 128 rows per ti
 constexpr int kKeyStage = 32;             // keys per LDS stage (double-buffered)
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
+// How a stage's key rows are found in the pages.
+constexpr int kPagesAny = 0;    // any page size: one page-table lookup per key row
+constexpr int kPagesPow2 = 1;   // power-of-two page size below 32: same, with shifts
+constexpr int kPagesStage = 2;  // page size a multiple of 32: a stage lies in one page
+
 struct PrefillArgs {
   const uint16_t* q;          // [total_q, Hq, DQK] bf16
   const char* k;
@@ -92,7 +97,13 @@ __device__ __forceinline__ void uniform_page_slot(const int32_t* pages, int t, i
   page = cp[j];
 }
 
-template <int DQK, int DVO, bool POW2>
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <int DQK, int DVO, int PM>
 __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = kPrefillWaves;
   constexpr int KS = kKeyStage;
@@ -121,10 +132,13 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   const int32_t* __restrict__ pages = a.kv_indices + a.kv_indptr[it.b];
 
   // This lane's query row: (token, head) pair r of the group.
+  // Rows past the tile's end repeat its last row (every row is computed independently;
+  // they are not stored).
   const int r = it.row_begin + 16 * w + n;
   const bool row_valid = r < it.row_end;
-  const int tok = row_valid ? r / G : 0;
-  const int head = kvh * G + (row_valid ? r % G : 0);
+  const int re = row_valid ? r : it.row_end - 1;
+  const int tok = re / G;
+  const int head = kvh * G + re % G;
   const int pos = it.kv_len - it.q_len + tok;
   const int64_t q_row = (int64_t)(it.q_begin + tok) * a.num_qo_heads + head;
 
@@ -132,11 +146,19 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   const int st_first = kv_lo / KS;
   const int st_end = (kv_hi + KS - 1) / KS;
 
+  // Keys row n sees: [vis_lo, vis_lo + vis_len) (the tile's range, the causal bound, the
+  // window).
+  int vis_lo = kv_lo, vis_hi = kv_hi;
+  if (a.causal) vis_hi = min(vis_hi, pos + 1);
+  if (a.window > 0) vis_lo = max(vis_lo, pos - a.window + 1);
+  const uint32_t vis_len = vis_hi > vis_lo ? (uint32_t)(vis_hi - vis_lo) : 0u;
+  const float c = a.scale_log2;
+
   // Stages [full_lo, full_hi) are visible to every row of this wave without a mask.
   int full_lo, full_hi;
   {
-    const int w_row0 = it.row_begin + 16 * w;
-    const int w_row1 = min(w_row0 + 15, it.row_end - 1);
+    const int w_row0 = min(it.row_begin + 16 * w, it.row_end - 1);
+    const int w_row1 = min(it.row_begin + 16 * w + 15, it.row_end - 1);
     const int p_first = it.kv_len - it.q_len + w_row0 / G;
     const int p_last = it.kv_len - it.q_len + w_row1 / G;
     int hi = kv_hi;                                   // keys < hi are below every bound
@@ -145,7 +167,6 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     if (a.window > 0) lo = max(lo, p_last - a.window + 1);
     full_lo = (lo + KS - 1) / KS;
     full_hi = hi / KS;
-    if (w_row0 + 15 >= it.row_end) full_hi = full_lo;  // a wave with unused rows: masked path
   }
 
   // Q^T operand for the whole tile: step j holds dims 32j + 8*g4 .. +7 of row n.  Loaded
@@ -155,7 +176,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     const uint16_t* src = a.q + q_row * DQK + 8 * g4;
 #pragma unroll
     for (int j = 0; j < QSTEPS; ++j)
-      qf[j] = row_valid ? *(const u32x4_t*)(src + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
+      qf[j] = *(const u32x4_t*)(src + 32 * j);
   }
 
   // Copies key stage `st` into buffer SLOT.  Wave w moves key rows 4w .. 4w+3 of the stage
@@ -165,33 +186,67 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   const char* k_base = a.k + (int64_t)kvh * a.k_sh;
   const char* v_base = a.v + (int64_t)kvh * a.v_sh;
   const int my_row = RPW * w;
-  auto copy_stage = [&](int st, auto slot_c) {
+  auto issue_rows = [&](auto slot_c, auto k_row_off, auto v_row_off) {
     constexpr int SLOT = decltype(slot_c)::value;
-    int64_t koff[RPW], voff[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      int t = st * KS + my_row + i;
-      t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
-      int pg, sl;
-      uniform_page_slot<POW2>(pages, t, a.page_size, a.page_shift, pg, sl);
-      koff[i] = pg * a.k_sp + sl * a.k_st;
-      voff[i] = pg * a.v_sp + sl * a.v_st;
-    }
 #pragma unroll
     for (int i = 0; i < RPW; i += KRPI) {
       const int sub = KRPI == 1 ? 0 : lane / KCH;
-      const int64_t off = KRPI == 1 ? koff[i] : (sub ? koff[i + 1] : koff[i]);
       const int chunk = (lane % KCH) ^ k_swz(my_row + i + sub);
-      __builtin_amdgcn_global_load_lds((const void*)(k_base + off + 16 * chunk),
+      __builtin_amdgcn_global_load_lds((const void*)(k_base + k_row_off(i, sub) + 16 * chunk),
           (__attribute__((address_space(3))) void*)(&k_lds[SLOT][(my_row + i) * DQK]), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < RPW; i += VRPI) {
       const int sub = VRPI == 1 ? 0 : lane / VCH;
-      const int64_t off = VRPI == 1 ? voff[i] : (sub ? voff[i + 1] : voff[i]);
       const int chunk = (lane % VCH) ^ v_swz(my_row + i + sub);
-      __builtin_amdgcn_global_load_lds((const void*)(v_base + off + 16 * chunk),
+      __builtin_amdgcn_global_load_lds((const void*)(v_base + v_row_off(i, sub) + 16 * chunk),
           (__attribute__((address_space(3))) void*)(&v_lds[SLOT][(my_row + i) * DVO]), 16, 0, 0);
+    }
+  };
+  // A stage inside one page (page size a multiple of 32): one lookup, then rows at a fixed
+  // stride.  The page index and the stage within the page of the next copy are tracked
+  // incrementally (copies run in stage order).
+  const int stages_per_page = a.page_size / KS;
+  int nxt_j = 0, nxt_r = 0;
+  if constexpr (PM == kPagesStage) {
+    nxt_j = __builtin_amdgcn_readfirstlane(st_first / stages_per_page);
+    nxt_r = __builtin_amdgcn_readfirstlane(st_first - nxt_j * stages_per_page);
+  }
+  auto copy_stage = [&](int st, auto slot_c) {
+    if constexpr (PM == kPagesStage) {
+      // Rows at or past the request's length would read slots past its last page's end
+      // (not keys of the request); they re-read the request's last key instead, which
+      // sits in the same page.  They are masked out.
+      const int pg = ((const_i32_ptr)pages)[nxt_j];
+      const int last_row = it.kv_len - 1 - st * KS;  // >= 0: the stage holds a key < kv_len
+      const int64_t kb = uniform_i64(pg * a.k_sp + (int64_t)nxt_r * KS * a.k_st);
+      const int64_t vb = uniform_i64(pg * a.v_sp + (int64_t)nxt_r * KS * a.v_st);
+      issue_rows(slot_c,
+          [&](int i, int sub) { return kb + (int64_t)min(my_row + i + sub, last_row) * a.k_st; },
+          [&](int i, int sub) { return vb + (int64_t)min(my_row + i + sub, last_row) * a.v_st; });
+      if (++nxt_r == stages_per_page) {
+        nxt_r = 0;
+        ++nxt_j;
+      }
+    } else {
+      // One page-table lookup per key row (keys clamped into the tile's range, so every
+      // row read is a key of the request; clamped keys are masked out).
+      auto one = [&](int row, int64_t sp, int64_t stt) {
+        int t = st * KS + my_row + row;
+        t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
+        int pg, sl;
+        uniform_page_slot<PM == kPagesPow2>(pages, t, a.page_size, a.page_shift, pg, sl);
+        return uniform_i64(pg * sp + sl * stt);
+      };
+      issue_rows(slot_c,
+          [&](int i, int sub) -> int64_t {
+            if constexpr (KRPI == 1) return one(i, a.k_sp, a.k_st);
+            else return sub ? one(i + 1, a.k_sp, a.k_st) : one(i, a.k_sp, a.k_st);
+          },
+          [&](int i, int sub) -> int64_t {
+            if constexpr (VRPI == 1) return one(i, a.v_sp, a.v_st);
+            else return sub ? one(i + 1, a.v_sp, a.v_st) : one(i, a.v_sp, a.v_st);
+          });
     }
   };
   (void)CPW;
@@ -203,6 +258,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   for (int t = 0; t < OT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY;  // reference max of row n (log2 domain)
   float l_run = 0.f;        // this lane's share of the row sum
+  float l_bf = 0.f;         // the same over the bf16-rounded weights
 
   // Transpose-read source of this lane within its 16-lane block: key (n / 4) of the 4-key
   // group, dims 4*(n % 4) .. +3 of the 16-dim tile.
@@ -245,29 +301,31 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- masks and online softmax of row n (its 32 keys are spread over the 4 lanes g4).
+    // The scale is positive: masks and the max work on raw scores, and the scale folds
+    // into one FMA per key in the exponent.
     float sv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sv[i] = (i < 4 ? s0[i] : s1[i - 4]) * a.scale_log2;
+    for (int i = 0; i < 8; ++i) sv[i] = i < 4 ? s0[i] : s1[i - 4];
     if (!full) {
+      // Key t is visible to row n iff t - vis_lo < vis_len (unsigned): one compare a key.
+      const uint32_t base = (uint32_t)(t0 + 4 * g4 - vis_lo);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int t = t0 + 16 * (i >> 2) + 4 * g4 + (i & 3);
-        bool ok = row_valid && t >= kv_lo && t < kv_hi;
-        if (a.causal) ok = ok && t <= pos;
-        if (a.window > 0) ok = ok && t > pos - a.window;
+        const bool ok = base + (uint32_t)(16 * (i >> 2) + (i & 3)) < vis_len;
         sv[i] = ok ? sv[i] : -INFINITY;
       }
     }
     float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     mx = max_xor16(mx);
-    mx = max_xor32(mx);
+    mx = max_xor32(mx) * c;
     // Move the reference max only when the row max outgrows it by the threshold.
     const bool grow = mx > m_ref + kRescaleThreshold || (m_ref == -INFINITY && mx != -INFINITY);
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = grow ? mx : m_ref;
-      const float alpha = grow ? (m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new)) : 1.f;
+      const float alpha = grow ? (m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new)) : 1.f;
       l_run *= alpha;
+      l_bf *= alpha;
 #pragma unroll
       for (int t = 0; t < OT; ++t) o[t] *= alpha;
       m_ref = m_new;
@@ -279,11 +337,17 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = exp2f(sv[i] - m_use);
+        p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], c, -m_use));
         l_run += p[i];
       }
+      // The output is normalised by the sum of the bf16 weights the MFMA uses, so the
+      // applied weights sum to one (this matters when one key dominates the row); the lse
+      // uses the fp32 sum.
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pf[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+      for (int e = 0; e < 4; ++e) {
+        pf[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+        l_bf += bf16_lo(pf[e]) + bf16_hi(pf[e]);
+      }
     }
     const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pf);
 
@@ -315,8 +379,9 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
 
   // ---- normalise and write row n: O^T tile t, register i holds dim 16t + 4*g4 + i.
   const float l_tot = sum_xor32(sum_xor16(l_run));
+  const float l_bf_tot = sum_xor32(sum_xor16(l_bf));
   if (!row_valid) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_bf_tot > 0.f ? 1.f / l_bf_tot : 0.f;
   const int64_t out_row = q_row * DVO;
 #pragma unroll
   for (int t = 0; t < OT; ++t) {
@@ -333,9 +398,10 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
 }
 
 template <int DQK, int DVO>
-static void launch_prefill(const PrefillArgs& a, bool pow2, int grid, hipStream_t s) {
-  if (pow2) prefill_kernel<DQK, DVO, true><<<grid, 512, 0, s>>>(a);
-  else prefill_kernel<DQK, DVO, false><<<grid, 512, 0, s>>>(a);
+static void launch_prefill(const PrefillArgs& a, int pm, int grid, hipStream_t s) {
+  if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage><<<grid, 512, 0, s>>>(a);
+  else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2><<<grid, 512, 0, s>>>(a);
+  else prefill_kernel<DQK, DVO, kPagesAny><<<grid, 512, 0, s>>>(a);
 }
 
 }  // namespace pa
@@ -381,10 +447,11 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   const int grid = plan->num_items * cache->num_kv_heads;
   hipStream_t s = (hipStream_t)stream;
   const int dqk = cache->head_dim_qk, dvo = cache->head_dim_vo;
-  const bool pow2 = (cache->page_size & (cache->page_size - 1)) == 0;
-  if (dqk == 512 && dvo == 512) launch_prefill<512, 512>(a, pow2, grid, s);
-  else if (dqk == 256 && dvo == 256) launch_prefill<256, 256>(a, pow2, grid, s);
-  else launch_prefill<512, 256>(a, pow2, grid, s);
+  const int P = cache->page_size;
+  const int pm = P % kKeyStage == 0 ? kPagesStage : ((P & (P - 1)) == 0 ? kPagesPow2 : kPagesAny);
+  if (dqk == 512 && dvo == 512) launch_prefill<512, 512>(a, pm, grid, s);
+  else if (dqk == 256 && dvo == 256) launch_prefill<256, 256>(a, pm, grid, s);
+  else launch_prefill<512, 256>(a, pm, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
   count_launches(1);

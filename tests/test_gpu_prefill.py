@@ -46,6 +46,25 @@ def test_prefill_sweep(qo, kv, hq, hkv, dqk, dvo, page, causal, window, out):
     compare(name, out_to_np(o), ref, lse.cpu().numpy(), ref_lse, out_dtype=out)
 
 
+@pytest.mark.parametrize("dqk,dvo,page", [(512, 512, 64), (512, 256, 16), (256, 256, 3)])
+def test_scores_far_above_the_first_stage_max(dqk, dvo, page):
+    """Keys from position 100 on get 40x larger K rows, so their scores exceed every
+    row's running max by far more than the kernel's rescale threshold: the accumulators
+    must be rescaled and the result still match the oracle."""
+    say(f"large later scores dims={dqk}/{dvo} page={page}")
+    c = make_prefill_case([150, 40], [400, 40], 8, 2, dqk, page, head_dim_vo=dvo,
+                          out_dtype="fp32", seed=31, device=dev())
+    P = c.page_size
+    for b in range(c.batch):
+        for t in range(100, int(c.kv_lens[b])):
+            pg = int(c.kv_indices[c.kv_indptr[b] + t // P])
+            c.k_pool[pg, :, t % P, :] *= 40
+    _, o, lse = gpu_prefill(c)
+    ref, ref_lse = oracle_prefill(c)
+    assert np.isfinite(ref).all()
+    compare(f"large later scores {dqk}/{dvo}", out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
+
+
 def test_prefill_with_one_new_token_equals_decode():
     say("prefill q_len 1 vs decode")
     from parity import gpu_decode
