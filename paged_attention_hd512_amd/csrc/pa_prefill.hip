@@ -116,6 +116,10 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int RPW = KS / NW;              // key rows each wave copies per stage
   constexpr int CPW = RPW / KRPI + RPW / VRPI;  // copy instructions per wave per stage
   static_assert(RPW == 4, "each wave copies four key rows per stage");
+  // Read-ahead of the software pipelines (steps of S^T, tiles of O^T), bounded by the
+  // registers left beside Q (DQK / 8 per lane) and O (DVO / 4 per lane).
+  constexpr int KD = DVO == 512 ? 1 : 4;
+  constexpr int VD = DVO == 512 ? 2 : 4;
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KS * DQK];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][KS * DVO];
@@ -283,20 +287,26 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     // ---- S^T = K Q^T for keys 0..15 (s0) and 16..31 (s1); lane holds keys 4*g4 + i.
     // Chunk 4j + g4 of row n (or 16 + n) sits at 4*(j ^ (n>>2)) + (g4 ^ (n&3)): four
     // per-lane bases (one per j % 4) plus compile-time offsets cover every step.
+    // Software-pipelined: the K operands of step j + KD are read before step j's MFMAs, so
+    // KD steps of LDS reads are in flight behind the MFMAs (the fences keep that order).
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     {
       const uint16_t* kb = kt + n * DQK + 8 * (g4 ^ (n & 3));
+      auto ld = [&](int j, u32x4_t& k0, u32x4_t& k1) {
+        const uint16_t* src = kb + 32 * ((j & 3) ^ (n >> 2)) + 128 * (j >> 2);
+        k0 = *(const u32x4_t*)src;
+        k1 = *(const u32x4_t*)(src + 16 * DQK);
+      };
+      u32x4_t kr0[KD + 1], kr1[KD + 1];
 #pragma unroll
-      for (int jl = 0; jl < 4; ++jl) {
-        const uint16_t* kbl = kb + 32 * (jl ^ (n >> 2));
+      for (int j = 0; j < KD; ++j) ld(j, kr0[j], kr1[j]);
 #pragma unroll
-        for (int jh = 0; jh < QSTEPS / 4; ++jh) {
-          const u32x4_t k0 = *(const u32x4_t*)(kbl + 128 * jh);
-          const u32x4_t k1 = *(const u32x4_t*)(kbl + 128 * jh + 16 * DQK);
-          const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, qf[4 * jh + jl]);
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k0), qb, s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k1), qb, s1, 0, 0, 0);
-        }
+      for (int j = 0; j < QSTEPS; ++j) {
+        if (j + KD < QSTEPS) ld(j + KD, kr0[(j + KD) % (KD + 1)], kr1[(j + KD) % (KD + 1)]);
+        const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, qf[j]);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr0[j % (KD + 1)]), qb, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr1[j % (KD + 1)]), qb, s1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -355,19 +365,23 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     // two transpose reads (keys 4*g4 + 0..3 and 16 + 4*g4 + 0..3; both rows have the same
     // swizzle, and the second is 16 rows below the first).  Chunk 2t + half of the row sits
     // at 2*(t ^ s) + half with s = row & 7: eight per-lane bases plus constant offsets.
+    // Software-pipelined like S^T: tile t + VD's reads are issued before tile t's MFMA.
     {
       const uint16_t* vb = vt + tr_row * DVO + tr_off + 8 * tr_half;
+      auto ld = [&](int t) {
+        const uint16_t* src = vb + 16 * ((t & 7) ^ (tr_row & 7)) + 128 * (t >> 3);
+        const u32x2_t lo = lds_read_tr16(src);
+        const u32x2_t hi = lds_read_tr16(src + 16 * DVO);
+        return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      };
+      u32x4_t vr[VD + 1];
 #pragma unroll
-      for (int tl = 0; tl < 8; ++tl) {
-        const uint16_t* vbl = vb + 16 * (tl ^ (tr_row & 7));
+      for (int t = 0; t < VD; ++t) vr[t] = ld(t);
 #pragma unroll
-        for (int th = 0; th < OT / 8; ++th) {
-          const int t = 8 * th + tl;
-          const u32x2_t lo = lds_read_tr16(vbl + 128 * th);
-          const u32x2_t hi = lds_read_tr16(vbl + 128 * th + 16 * DVO);
-          const u32x4_t vf = {lo[0], lo[1], hi[0], hi[1]};
-          o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf), pb, o[t], 0, 0, 0);
-        }
+      for (int t = 0; t < OT; ++t) {
+        if (t + VD < OT) vr[(t + VD) % (VD + 1)] = ld(t + VD);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vr[t % (VD + 1)]), pb, o[t], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
