@@ -114,15 +114,18 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int KRPI = 64 / KCH;            // K rows per copy instruction (1 or 2)
   constexpr int VRPI = 64 / VCH;
   constexpr int RPW = KS / NW;              // key rows each wave copies per stage
-  constexpr int CPW = RPW / KRPI + RPW / VRPI;  // copy instructions per wave per stage
   static_assert(RPW == 4, "each wave copies four key rows per stage");
   // Read-ahead of the software pipelines (steps of S^T, tiles of O^T), bounded by the
   // registers left beside Q (DQK / 8 per lane) and O (DVO / 4 per lane).
   constexpr int KD = DVO == 512 ? 1 : 4;
   constexpr int VD = DVO == 512 ? 2 : 4;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KS * DQK];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][KS * DVO];
+  // One array per buffer: the compiler then sees that reads of one buffer do not alias the
+  // direct-to-LDS copies into the other, and does not make them wait for those copies.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[KS * DQK], k_lds1[KS * DQK];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[KS * DVO], v_lds1[KS * DVO];
+  auto k_buf = [&](auto slot_c) -> uint16_t* { if constexpr (decltype(slot_c)::value == 0) return k_lds0; else return k_lds1; };
+  auto v_buf = [&](auto slot_c) -> uint16_t* { if constexpr (decltype(slot_c)::value == 0) return v_lds0; else return v_lds1; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -186,74 +189,93 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   // Copies key stage `st` into buffer SLOT.  Wave w moves key rows 4w .. 4w+3 of the stage
   // for both K and V, straight from the pages into LDS (one instruction per 1 KB row, or
   // one per two 512-byte rows); lane L fills chunk position L % chunks-per-row of its row
-  // with the logical chunk that the swizzle puts there.
+  // with the logical chunk that the swizzle puts there.  Each instruction takes a
+  // wave-uniform 64-bit base and a 32-bit per-lane offset.
   const char* k_base = a.k + (int64_t)kvh * a.k_sh;
   const char* v_base = a.v + (int64_t)kvh * a.v_sh;
   const int my_row = RPW * w;
-  auto issue_rows = [&](auto slot_c, auto k_row_off, auto v_row_off) {
-    constexpr int SLOT = decltype(slot_c)::value;
-#pragma unroll
-    for (int i = 0; i < RPW; i += KRPI) {
-      const int sub = KRPI == 1 ? 0 : lane / KCH;
-      const int chunk = (lane % KCH) ^ k_swz(my_row + i + sub);
-      __builtin_amdgcn_global_load_lds((const void*)(k_base + k_row_off(i, sub) + 16 * chunk),
-          (__attribute__((address_space(3))) void*)(&k_lds[SLOT][(my_row + i) * DQK]), 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < RPW; i += VRPI) {
-      const int sub = VRPI == 1 ? 0 : lane / VCH;
-      const int chunk = (lane % VCH) ^ v_swz(my_row + i + sub);
-      __builtin_amdgcn_global_load_lds((const void*)(v_base + v_row_off(i, sub) + 16 * chunk),
-          (__attribute__((address_space(3))) void*)(&v_lds[SLOT][(my_row + i) * DVO]), 16, 0, 0);
-    }
-  };
   // A stage inside one page (page size a multiple of 32): one lookup, then rows at a fixed
   // stride.  The page index and the stage within the page of the next copy are tracked
   // incrementally (copies run in stage order).
   const int stages_per_page = a.page_size / KS;
   int nxt_j = 0, nxt_r = 0;
+  uint32_t k_roff = 0, v_roff = 0;  // byte offsets of the next copy's stage inside its page
   if constexpr (PM == kPagesStage) {
     nxt_j = __builtin_amdgcn_readfirstlane(st_first / stages_per_page);
     nxt_r = __builtin_amdgcn_readfirstlane(st_first - nxt_j * stages_per_page);
+    k_roff = (uint32_t)nxt_r * KS * (uint32_t)a.k_st;
+    v_roff = (uint32_t)nxt_r * KS * (uint32_t)a.v_st;
   }
   auto copy_stage = [&](int st, auto slot_c) {
     if constexpr (PM == kPagesStage) {
       // Rows at or past the request's length would read slots past its last page's end
       // (not keys of the request); they re-read the request's last key instead, which
-      // sits in the same page.  They are masked out.
+      // sits in the same page.  They are masked out.  The stage base is one 64-bit scalar
+      // sum; a row's offset from it fits 32 bits (the host checks 32 token strides do), so
+      // each copy instruction takes a scalar base plus a 32-bit per-lane offset.
       const int pg = ((const_i32_ptr)pages)[nxt_j];
       const int last_row = it.kv_len - 1 - st * KS;  // >= 0: the stage holds a key < kv_len
-      const int64_t kb = uniform_i64(pg * a.k_sp + (int64_t)nxt_r * KS * a.k_st);
-      const int64_t vb = uniform_i64(pg * a.v_sp + (int64_t)nxt_r * KS * a.v_st);
-      issue_rows(slot_c,
-          [&](int i, int sub) { return kb + (int64_t)min(my_row + i + sub, last_row) * a.k_st; },
-          [&](int i, int sub) { return vb + (int64_t)min(my_row + i + sub, last_row) * a.v_st; });
+      const char* ks = (const char*)uniform_i64((int64_t)(k_base + pg * a.k_sp + k_roff));
+      const char* vs = (const char*)uniform_i64((int64_t)(v_base + pg * a.v_sp + v_roff));
+      const uint32_t kst = (uint32_t)a.k_st, vst = (uint32_t)a.v_st;
+      // The lane terms are rebuilt each stage from one register (the empty asm hides the
+      // value from loop-invariant hoisting, which would hold one register per instruction).
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int i = 0; i < RPW; i += KRPI) {
+        const int row = my_row + i + (KRPI == 1 ? 0 : (int)((uint32_t)ln / KCH));
+        const uint32_t off = (uint32_t)min(row, last_row) * kst + 16u * (((uint32_t)ln % KCH) ^ k_swz(row));
+        __builtin_amdgcn_global_load_lds((const void*)(ks + off),
+            (__attribute__((address_space(3))) void*)(k_buf(slot_c) + (my_row + i) * DQK), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < RPW; i += VRPI) {
+        const int row = my_row + i + (VRPI == 1 ? 0 : (int)((uint32_t)ln / VCH));
+        const uint32_t off = (uint32_t)min(row, last_row) * vst + 16u * (((uint32_t)ln % VCH) ^ v_swz(row));
+        __builtin_amdgcn_global_load_lds((const void*)(vs + off),
+            (__attribute__((address_space(3))) void*)(v_buf(slot_c) + (my_row + i) * DVO), 16, 0, 0);
+      }
+      k_roff += KS * kst;
+      v_roff += KS * vst;
       if (++nxt_r == stages_per_page) {
         nxt_r = 0;
         ++nxt_j;
+        k_roff = 0;
+        v_roff = 0;
       }
     } else {
       // One page-table lookup per key row (keys clamped into the tile's range, so every
       // row read is a key of the request; clamped keys are masked out).
-      auto one = [&](int row, int64_t sp, int64_t stt) {
+      auto row_base = [&](int row, const char* base, int64_t sp, int64_t stt) {
         int t = st * KS + my_row + row;
         t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
         int pg, sl;
         uniform_page_slot<PM == kPagesPow2>(pages, t, a.page_size, a.page_shift, pg, sl);
-        return uniform_i64(pg * sp + sl * stt);
+        return (const char*)uniform_i64((int64_t)(base + pg * sp + sl * stt));
       };
-      issue_rows(slot_c,
-          [&](int i, int sub) -> int64_t {
-            if constexpr (KRPI == 1) return one(i, a.k_sp, a.k_st);
-            else return sub ? one(i + 1, a.k_sp, a.k_st) : one(i, a.k_sp, a.k_st);
-          },
-          [&](int i, int sub) -> int64_t {
-            if constexpr (VRPI == 1) return one(i, a.v_sp, a.v_st);
-            else return sub ? one(i + 1, a.v_sp, a.v_st) : one(i, a.v_sp, a.v_st);
-          });
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int i = 0; i < RPW; i += KRPI) {
+        const uint32_t sub = KRPI == 1 ? 0u : (uint32_t)ln / KCH;
+        const char* rb = row_base(i, k_base, a.k_sp, a.k_st);
+        if constexpr (KRPI == 2) rb = sub ? row_base(i + 1, k_base, a.k_sp, a.k_st) : rb;
+        const uint32_t off = 16u * (((uint32_t)ln % KCH) ^ k_swz(my_row + i + (int)sub));
+        __builtin_amdgcn_global_load_lds((const void*)(rb + off),
+            (__attribute__((address_space(3))) void*)(k_buf(slot_c) + (my_row + i) * DQK), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < RPW; i += VRPI) {
+        const uint32_t sub = VRPI == 1 ? 0u : (uint32_t)ln / VCH;
+        const char* rb = row_base(i, v_base, a.v_sp, a.v_st);
+        if constexpr (VRPI == 2) rb = sub ? row_base(i + 1, v_base, a.v_sp, a.v_st) : rb;
+        const uint32_t off = 16u * (((uint32_t)ln % VCH) ^ v_swz(my_row + i + (int)sub));
+        __builtin_amdgcn_global_load_lds((const void*)(rb + off),
+            (__attribute__((address_space(3))) void*)(v_buf(slot_c) + (my_row + i) * DVO), 16, 0, 0);
+      }
     }
   };
-  (void)CPW;
 
   if (st_first < st_end) copy_stage(st_first, std::integral_constant<int, 0>{});
 
@@ -282,8 +304,8 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     if (st + 1 < st_end) copy_stage(st + 1, std::integral_constant<int, SLOT ^ 1>{});
     const bool full = st >= full_lo && st < full_hi;
 
-    const uint16_t* kt = k_lds[SLOT];
-    const uint16_t* vt = v_lds[SLOT];
+    const uint16_t* kt = k_buf(slot_c);
+    const uint16_t* vt = v_buf(slot_c);
     // ---- S^T = K Q^T for keys 0..15 (s0) and 16..31 (s1); lane holds keys 4*g4 + i.
     // Chunk 4j + g4 of row n (or 16 + n) sits at 4*(j ^ (n>>2)) + (g4 ^ (n&3)): four
     // per-lane bases (one per j % 4) plus compile-time offsets cover every step.
@@ -462,7 +484,12 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   hipStream_t s = (hipStream_t)stream;
   const int dqk = cache->head_dim_qk, dvo = cache->head_dim_vo;
   const int P = cache->page_size;
-  const int pm = P % kKeyStage == 0 ? kPagesStage : ((P & (P - 1)) == 0 ? kPagesPow2 : kPagesAny);
+  // The one-lookup-per-stage path forms byte offsets inside a page in 32 bits.
+  const bool page_fits_u32 = (int64_t)P * a.k_st + 2 * dqk < (int64_t(1) << 32) &&
+                             (int64_t)P * a.v_st + 2 * dvo < (int64_t(1) << 32);
+  const int pm = P % kKeyStage == 0 && page_fits_u32
+                     ? kPagesStage
+                     : ((P & (P - 1)) == 0 ? kPagesPow2 : kPagesAny);
   if (dqk == 512 && dvo == 512) launch_prefill<512, 512>(a, pm, grid, s);
   else if (dqk == 256 && dvo == 256) launch_prefill<256, 256>(a, pm, grid, s);
   else launch_prefill<512, 256>(a, pm, grid, s);
