@@ -29,6 +29,7 @@
 #include <math.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
@@ -80,6 +81,35 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Calls f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
+template <int... I, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+// ds_read_b64_tr_b16 at LDS byte address addr + OFF, as inline assembly: the compiler does
+// not count it, so the caller waits for it with lds_wait<N>.  (Issued through the builtin,
+// the compiler cannot tell which LDS buffer the read touches and makes it wait for every
+// direct-to-LDS copy in flight, including the next stage's.)
+template <int OFF>
+__device__ __forceinline__ u32x2_t lds_read_tr16_at(uint32_t addr) {
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+// Waits until at most N LDS (or scalar memory) operations of this wave are outstanding.
+// The registers that the awaited reads fill pass through the statement, so the compiler
+// cannot use or copy them before it.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2_t& a, u32x2_t& b) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+
 // Page and slot of a wave-uniform logical token, through a scalar load.
 template <bool POW2>
 __device__ __forceinline__ void uniform_page_slot(const int32_t* pages, int t, int page_size,
@@ -95,6 +125,12 @@ __device__ __forceinline__ void uniform_page_slot(const int32_t* pages, int t, i
     slot = t - j * page_size;
   }
   page = cp[j];
+}
+
+// Raw buffer resource at base p: no stride, no bound (every offset the kernel forms stays
+// inside the page it addresses), 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* p) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, -1, 0x00020000);
 }
 
 __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
@@ -122,8 +158,10 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
 
   // One array per buffer: the compiler then sees that reads of one buffer do not alias the
   // direct-to-LDS copies into the other, and does not make them wait for those copies.
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[KS * DQK], k_lds1[KS * DQK];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[KS * DVO], v_lds1[KS * DVO];
+  // 1 KB alignment: the swizzled read addresses below differ from a per-lane base only in
+  // bits the base leaves zero, so one XOR forms each of them.
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[KS * DQK], k_lds1[KS * DQK];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[KS * DVO], v_lds1[KS * DVO];
   auto k_buf = [&](auto slot_c) -> uint16_t* { if constexpr (decltype(slot_c)::value == 0) return k_lds0; else return k_lds1; };
   auto v_buf = [&](auto slot_c) -> uint16_t* { if constexpr (decltype(slot_c)::value == 0) return v_lds0; else return v_lds1; };
 
@@ -206,44 +244,63 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     k_roff = (uint32_t)nxt_r * KS * (uint32_t)a.k_st;
     v_roff = (uint32_t)nxt_r * KS * (uint32_t)a.v_st;
   }
+  // Rows at or past the request's length would read slots past its last page's end (not
+  // keys of the request); they re-read the request's last key instead, which sits in the
+  // same page.  They are masked out.  The stage base is one 64-bit scalar sum; a row's
+  // offset from it fits 32 bits (the host checks that a page's bytes do), so each copy
+  // instruction takes a scalar base plus a 32-bit per-lane offset.  copy_prep does the
+  // scalar work of a stage once; copy_one issues copy instruction IDX (K rows first, then
+  // V rows), so the instructions can be spread over the stage's MFMA steps.  The copies are
+  // buffer loads to LDS over a resource at the stage base (the global-memory form would make
+  // the compiler drain every LDS read at each later LDS wait, as it counts that form as a
+  // pending LDS access).
+  constexpr int NKC = RPW / KRPI, NVC = RPW / VRPI, NCOPY = NKC + NVC;
+  // The next copy's resources and last in-range row (plain locals, so they stay in
+  // scalar registers).  A prep past the last stage (no copy follows it) clamps to the
+  // request's last page and row 0 of the stage, so its addresses stay valid.
+  __amdgpu_buffer_rsrc_t c_kr = make_rsrc(a.k), c_vr = make_rsrc(a.v);
+  int c_last_row = 0;
+  const int last_j = (it.kv_len - 1) / a.page_size;
+  auto copy_prep = [&](int st) {
+    const int pg = ((const_i32_ptr)pages)[min(nxt_j, last_j)];
+    c_last_row = max(it.kv_len - 1 - st * KS, 0);  // a stage that is copied holds a key < kv_len
+    c_kr = make_rsrc((const char*)uniform_i64((int64_t)(k_base + pg * a.k_sp + k_roff)));
+    c_vr = make_rsrc((const char*)uniform_i64((int64_t)(v_base + pg * a.v_sp + v_roff)));
+    k_roff += KS * (uint32_t)a.k_st;
+    v_roff += KS * (uint32_t)a.v_st;
+    if (++nxt_r == stages_per_page) {
+      nxt_r = 0;
+      ++nxt_j;
+      k_roff = 0;
+      v_roff = 0;
+    }
+  };
+  auto copy_one = [&](auto idx_c, auto slot_c) {
+    constexpr int IDX = decltype(idx_c)::value;
+    // The lane terms are rebuilt from one register each time (the empty asm hides the value
+    // from loop-invariant hoisting, which would hold one register per instruction).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if constexpr (IDX < NKC) {
+      constexpr int i = IDX * KRPI;
+      const int row = my_row + i + (KRPI == 1 ? 0 : (int)((uint32_t)ln / KCH));
+      const uint32_t off = (uint32_t)min(row, c_last_row) * (uint32_t)a.k_st +
+                           16u * (((uint32_t)ln % KCH) ^ k_swz(row));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c_kr,
+          (__attribute__((address_space(3))) void*)(k_buf(slot_c) + (my_row + i) * DQK), 16, off, 0, 0, 0);
+    } else {
+      constexpr int i = (IDX - NKC) * VRPI;
+      const int row = my_row + i + (VRPI == 1 ? 0 : (int)((uint32_t)ln / VCH));
+      const uint32_t off = (uint32_t)min(row, c_last_row) * (uint32_t)a.v_st +
+                           16u * (((uint32_t)ln % VCH) ^ v_swz(row));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c_vr,
+          (__attribute__((address_space(3))) void*)(v_buf(slot_c) + (my_row + i) * DVO), 16, off, 0, 0, 0);
+    }
+  };
   auto copy_stage = [&](int st, auto slot_c) {
     if constexpr (PM == kPagesStage) {
-      // Rows at or past the request's length would read slots past its last page's end
-      // (not keys of the request); they re-read the request's last key instead, which
-      // sits in the same page.  They are masked out.  The stage base is one 64-bit scalar
-      // sum; a row's offset from it fits 32 bits (the host checks 32 token strides do), so
-      // each copy instruction takes a scalar base plus a 32-bit per-lane offset.
-      const int pg = ((const_i32_ptr)pages)[nxt_j];
-      const int last_row = it.kv_len - 1 - st * KS;  // >= 0: the stage holds a key < kv_len
-      const char* ks = (const char*)uniform_i64((int64_t)(k_base + pg * a.k_sp + k_roff));
-      const char* vs = (const char*)uniform_i64((int64_t)(v_base + pg * a.v_sp + v_roff));
-      const uint32_t kst = (uint32_t)a.k_st, vst = (uint32_t)a.v_st;
-      // The lane terms are rebuilt each stage from one register (the empty asm hides the
-      // value from loop-invariant hoisting, which would hold one register per instruction).
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-#pragma unroll
-      for (int i = 0; i < RPW; i += KRPI) {
-        const int row = my_row + i + (KRPI == 1 ? 0 : (int)((uint32_t)ln / KCH));
-        const uint32_t off = (uint32_t)min(row, last_row) * kst + 16u * (((uint32_t)ln % KCH) ^ k_swz(row));
-        __builtin_amdgcn_global_load_lds((const void*)(ks + off),
-            (__attribute__((address_space(3))) void*)(k_buf(slot_c) + (my_row + i) * DQK), 16, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < RPW; i += VRPI) {
-        const int row = my_row + i + (VRPI == 1 ? 0 : (int)((uint32_t)ln / VCH));
-        const uint32_t off = (uint32_t)min(row, last_row) * vst + 16u * (((uint32_t)ln % VCH) ^ v_swz(row));
-        __builtin_amdgcn_global_load_lds((const void*)(vs + off),
-            (__attribute__((address_space(3))) void*)(v_buf(slot_c) + (my_row + i) * DVO), 16, 0, 0);
-      }
-      k_roff += KS * kst;
-      v_roff += KS * vst;
-      if (++nxt_r == stages_per_page) {
-        nxt_r = 0;
-        ++nxt_j;
-        k_roff = 0;
-        v_roff = 0;
-      }
+      copy_prep(st);
+      static_for<NCOPY>([&](auto idx_c) { copy_one(idx_c, slot_c); });
     } else {
       // One page-table lookup per key row (keys clamped into the tile's range, so every
       // row read is a key of the request; clamped keys are masked out).
@@ -301,7 +358,19 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     // and every wave is done with the other buffer, which the next stage's copies refill.
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (st + 1 < st_end) copy_stage(st + 1, std::integral_constant<int, SLOT ^ 1>{});
+    const bool has_next = st + 1 < st_end;
+    constexpr auto next_slot = std::integral_constant<int, SLOT ^ 1>{};
+    // One-lookup pages at head_dim_vo 512: the next stage's copy instructions are spread
+    // over the S^T steps below, so the vector memory pipe streams them while the MFMAs run
+    // (as one burst here they stall the issuing waves).  The shorter head_dim_vo 256 stage
+    // leaves too little time behind late copies, so there, and for other page sizes, they
+    // are all issued here.
+    constexpr bool SPREAD = PM == kPagesStage && DVO == 512;
+    if constexpr (SPREAD) {
+      copy_prep(st + 1);
+    } else {
+      if (has_next) copy_stage(st + 1, next_slot);
+    }
     const bool full = st >= full_lo && st < full_hi;
 
     const uint16_t* kt = k_buf(slot_c);
@@ -312,25 +381,35 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     // Software-pipelined: the K operands of step j + KD are read before step j's MFMAs, so
     // KD steps of LDS reads are in flight behind the MFMAs (the fences keep that order).
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    {
-      const uint16_t* kb = kt + n * DQK + 8 * (g4 ^ (n & 3));
+    auto qk = [&](auto copy_c) {
+      constexpr bool COPY = decltype(copy_c)::value;
+      constexpr int CSTEP = QSTEPS / NCOPY > 0 ? QSTEPS / NCOPY : 1;
+      static_assert(!COPY || (QSTEPS + CSTEP - 1) / CSTEP >= NCOPY, "copy slots");
+      // Element index of the step-j chunk: kb ^ 32*(j & 3) (bits 5-6 of kb hold n >> 2 and
+      // nothing else does), plus 128*(j >> 2).
+      int kb = n * DQK + 8 * (g4 ^ (n & 3)) + 32 * (n >> 2);
+      asm volatile("" : "+v"(kb));
       auto ld = [&](int j, u32x4_t& k0, u32x4_t& k1) {
-        const uint16_t* src = kb + 32 * ((j & 3) ^ (n >> 2)) + 128 * (j >> 2);
+        const uint16_t* src = kt + ((kb ^ (32 * (j & 3))) + 128 * (j >> 2));
         k0 = *(const u32x4_t*)src;
         k1 = *(const u32x4_t*)(src + 16 * DQK);
       };
       u32x4_t kr0[KD + 1], kr1[KD + 1];
 #pragma unroll
       for (int j = 0; j < KD; ++j) ld(j, kr0[j], kr1[j]);
-#pragma unroll
-      for (int j = 0; j < QSTEPS; ++j) {
-        if (j + KD < QSTEPS) ld(j + KD, kr0[(j + KD) % (KD + 1)], kr1[(j + KD) % (KD + 1)]);
+      static_for<QSTEPS>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        if constexpr (j + KD < QSTEPS) ld(j + KD, kr0[(j + KD) % (KD + 1)], kr1[(j + KD) % (KD + 1)]);
+        if constexpr (COPY && j % CSTEP == 0 && j / CSTEP < NCOPY)
+          copy_one(std::integral_constant<int, j / CSTEP>{}, next_slot);
         const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, qf[j]);
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr0[j % (KD + 1)]), qb, s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr1[j % (KD + 1)]), qb, s1, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+      });
+    };
+    if (SPREAD && has_next) qk(std::true_type{});
+    else qk(std::false_type{});
 
     // ---- masks and online softmax of row n (its 32 keys are spread over the 4 lanes g4).
     // The scale is positive: masks and the max work on raw scores, and the scale folds
@@ -388,23 +467,31 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     // swizzle, and the second is 16 rows below the first).  Chunk 2t + half of the row sits
     // at 2*(t ^ s) + half with s = row & 7: eight per-lane bases plus constant offsets.
     // Software-pipelined like S^T: tile t + VD's reads are issued before tile t's MFMA.
+    // The reads are inline assembly (see lds_read_tr16_at), so each MFMA first waits for
+    // its own tile's two reads: at most 2 * (tiles issued after it) reads may be pending.
     {
-      const uint16_t* vb = vt + tr_row * DVO + tr_off + 8 * tr_half;
-      auto ld = [&](int t) {
-        const uint16_t* src = vb + 16 * ((t & 7) ^ (tr_row & 7)) + 128 * (t >> 3);
-        const u32x2_t lo = lds_read_tr16(src);
-        const u32x2_t hi = lds_read_tr16(src + 16 * DVO);
-        return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      // Byte address of tile t's chunk: vb ^ 32*(t & 7) (bits 5-7 of vb hold the row
+      // swizzle and nothing else does), plus 256*(t >> 3) as the instruction offset.
+      uint32_t vb = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)(
+                        vt + tr_row * DVO + tr_off + 8 * tr_half) + 32u * (uint32_t)(tr_row & 7);
+      asm volatile("" : "+v"(vb));
+      u32x2_t vlo[VD + 1], vhi[VD + 1];
+      auto ld = [&](auto t_c) {
+        constexpr int t = decltype(t_c)::value;
+        const uint32_t src = vb ^ (32u * (t & 7));
+        vlo[t % (VD + 1)] = lds_read_tr16_at<256 * (t >> 3)>(src);
+        vhi[t % (VD + 1)] = lds_read_tr16_at<256 * (t >> 3) + 32 * DVO>(src);
       };
-      u32x4_t vr[VD + 1];
-#pragma unroll
-      for (int t = 0; t < VD; ++t) vr[t] = ld(t);
-#pragma unroll
-      for (int t = 0; t < OT; ++t) {
-        if (t + VD < OT) vr[(t + VD) % (VD + 1)] = ld(t + VD);
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vr[t % (VD + 1)]), pb, o[t], 0, 0, 0);
+      static_for<VD>([&](auto t_c) { ld(t_c); });
+      static_for<OT>([&](auto t_c) {
+        constexpr int t = decltype(t_c)::value;
+        constexpr int r = t % (VD + 1);
+        if constexpr (t + VD < OT) ld(std::integral_constant<int, t + VD>{});
+        lds_wait<2 * (t + VD < OT ? VD : OT - 1 - t)>(vlo[r], vhi[r]);
+        const u32x4_t vf = {vlo[r][0], vlo[r][1], vhi[r][0], vhi[r][1]};
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf), pb, o[t], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     }
   };
 
