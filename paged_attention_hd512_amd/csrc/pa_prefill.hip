@@ -261,11 +261,27 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   __amdgpu_buffer_rsrc_t c_kr = make_rsrc(a.k), c_vr = make_rsrc(a.v);
   int c_last_row = 0;
   const int last_j = (it.kv_len - 1) / a.page_size;
+  // Page indices come from a window of 64 consecutive entries held one per lane and read
+  // with v_readlane, so a stage's lookup has no memory latency; the window moves (one
+  // vector load) every 64 pages.
+  int pwin_base = 0, pwin = 0;
+  if constexpr (PM == kPagesStage) {
+    pwin_base = min(nxt_j, last_j);
+    pwin = pages[min(pwin_base + lane, last_j)];
+  }
   auto copy_prep = [&](int st) {
-    const int pg = ((const_i32_ptr)pages)[min(nxt_j, last_j)];
+    const int jj = min(nxt_j, last_j);
+    if (jj - pwin_base >= 64) {
+      pwin_base = jj;
+      pwin = pages[min(pwin_base + lane, last_j)];
+    }
+    const int pg = __builtin_amdgcn_readlane(pwin, jj - pwin_base);
     c_last_row = max(it.kv_len - 1 - st * KS, 0);  // a stage that is copied holds a key < kv_len
-    c_kr = make_rsrc((const char*)uniform_i64((int64_t)(k_base + pg * a.k_sp + k_roff)));
-    c_vr = make_rsrc((const char*)uniform_i64((int64_t)(v_base + pg * a.v_sp + v_roff)));
+    // Page strides fit 32 bits on this path (host-checked): one 32x32->64-bit product each.
+    c_kr = make_rsrc((const char*)uniform_i64(
+        (int64_t)(k_base + (uint64_t)(uint32_t)pg * (uint32_t)a.k_sp + k_roff)));
+    c_vr = make_rsrc((const char*)uniform_i64(
+        (int64_t)(v_base + (uint64_t)(uint32_t)pg * (uint32_t)a.v_sp + v_roff)));
     k_roff += KS * (uint32_t)a.k_st;
     v_roff += KS * (uint32_t)a.v_st;
     if (++nxt_r == stages_per_page) {
@@ -430,11 +446,13 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     mx = max_xor16(mx);
     mx = max_xor32(mx) * c;
-    // Move the reference max only when the row max outgrows it by the threshold.
-    const bool grow = mx > m_ref + kRescaleThreshold || (m_ref == -INFINITY && mx != -INFINITY);
+    // Move the reference max only when the row max outgrows it by the threshold.  While
+    // m_ref is -inf (no visible key yet) any finite max outgrows it, and the factor
+    // exp2(-inf) = 0 clears the (zero) state.
+    const bool grow = mx > m_ref + kRescaleThreshold;
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = grow ? mx : m_ref;
-      const float alpha = grow ? (m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new)) : 1.f;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
       l_run *= alpha;
       l_bf *= alpha;
 #pragma unroll
@@ -571,9 +589,11 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   hipStream_t s = (hipStream_t)stream;
   const int dqk = cache->head_dim_qk, dvo = cache->head_dim_vo;
   const int P = cache->page_size;
-  // The one-lookup-per-stage path forms byte offsets inside a page in 32 bits.
+  // The one-lookup-per-stage path forms byte offsets inside a page, and page strides, in
+  // 32 bits.
   const bool page_fits_u32 = (int64_t)P * a.k_st + 2 * dqk < (int64_t(1) << 32) &&
-                             (int64_t)P * a.v_st + 2 * dvo < (int64_t(1) << 32);
+                             (int64_t)P * a.v_st + 2 * dvo < (int64_t(1) << 32) &&
+                             a.k_sp < (int64_t(1) << 32) && a.v_sp < (int64_t(1) << 32);
   const int pm = P % kKeyStage == 0 && page_fits_u32
                      ? kPagesStage
                      : ((P & (P - 1)) == 0 ? kPagesPow2 : kPagesAny);
