@@ -156,14 +156,16 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int KD = DVO == 512 ? 1 : 4;
   constexpr int VD = DVO == 512 ? 2 : 4;
 
-  // One array per buffer: the compiler then sees that reads of one buffer do not alias the
-  // direct-to-LDS copies into the other, and does not make them wait for those copies.
-  // 1 KB alignment: the swizzled read addresses below differ from a per-lane base only in
-  // bits the base leaves zero, so one XOR forms each of them.
+  // K stages are double-buffered, V stages triple-buffered: half of the waves use a stage's
+  // V one interval after its K (see the stage loop below).  One array per K buffer: the
+  // compiler then sees that K reads of one buffer do not alias the direct-to-LDS copies into
+  // the other, and does not make them wait for those copies (V is read by inline assembly,
+  // which the compiler does not track).  1 KB alignment: the swizzled read addresses below
+  // differ from a per-lane base only in bits the base leaves zero, so one XOR forms each.
+  constexpr int VSTAGE = KS * DVO;  // elements of one V buffer
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[KS * DQK], k_lds1[KS * DQK];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[KS * DVO], v_lds1[KS * DVO];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[3 * VSTAGE];
   auto k_buf = [&](auto slot_c) -> uint16_t* { if constexpr (decltype(slot_c)::value == 0) return k_lds0; else return k_lds1; };
-  auto v_buf = [&](auto slot_c) -> uint16_t* { if constexpr (decltype(slot_c)::value == 0) return v_lds0; else return v_lds1; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -291,8 +293,11 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
       v_roff = 0;
     }
   };
-  auto copy_one = [&](auto idx_c, auto slot_c) {
-    constexpr int IDX = decltype(idx_c)::value;
+  // Instruction IDX % NCOPY of the rows of wave w (IDX < NCOPY) or of wave w + NW/2 (the
+  // wave sharing this SIMD, IDX >= NCOPY).
+  auto copy_one = [&](auto idx_c, auto slot_c, int vo) {
+    constexpr int IDX = decltype(idx_c)::value % NCOPY;
+    const int my_row = RPW * w + (decltype(idx_c)::value / NCOPY) * RPW * (NW / 2);
     // The lane terms are rebuilt from one register each time (the empty asm hides the value
     // from loop-invariant hoisting, which would hold one register per instruction).
     int ln = lane;
@@ -310,13 +315,14 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
       const uint32_t off = (uint32_t)min(row, c_last_row) * (uint32_t)a.v_st +
                            16u * (((uint32_t)ln % VCH) ^ v_swz(row));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c_vr,
-          (__attribute__((address_space(3))) void*)(v_buf(slot_c) + (my_row + i) * DVO), 16, off, 0, 0, 0);
+          (__attribute__((address_space(3))) void*)(v_lds + vo + (my_row + i) * DVO), 16, off, 0, 0, 0);
     }
   };
-  auto copy_stage = [&](int st, auto slot_c) {
+  // Copies stage st: K into buffer slot_c, V into v_lds + vo.
+  auto copy_stage = [&](int st, auto slot_c, int vo) {
     if constexpr (PM == kPagesStage) {
       copy_prep(st);
-      static_for<NCOPY>([&](auto idx_c) { copy_one(idx_c, slot_c); });
+      static_for<NCOPY>([&](auto idx_c) { copy_one(idx_c, slot_c, vo); });
     } else {
       // One page-table lookup per key row (keys clamped into the tile's range, so every
       // row read is a key of the request; clamped keys are masked out).
@@ -345,12 +351,10 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
         if constexpr (VRPI == 2) rb = sub ? row_base(i + 1, v_base, a.v_sp, a.v_st) : rb;
         const uint32_t off = 16u * (((uint32_t)ln % VCH) ^ v_swz(my_row + i + (int)sub));
         __builtin_amdgcn_global_load_lds((const void*)(rb + off),
-            (__attribute__((address_space(3))) void*)(v_buf(slot_c) + (my_row + i) * DVO), 16, 0, 0);
+            (__attribute__((address_space(3))) void*)(v_lds + vo + (my_row + i) * DVO), 16, 0, 0);
       }
     }
   };
-
-  if (st_first < st_end) copy_stage(st_first, std::integral_constant<int, 0>{});
 
   f32x4_t o[OT];
 #pragma unroll
@@ -359,77 +363,59 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   float l_run = 0.f;        // this lane's share of the row sum
   float l_bf = 0.f;         // the same over the bf16-rounded weights
 
-  // Transpose-read source of this lane within its 16-lane block: key (n / 4) of the 4-key
-  // group, dims 4*(n % 4) .. +3 of the 16-dim tile.
-  const int tr_row = 4 * g4 + (n >> 2);
-  const int tr_half = (n & 3) >> 1;         // which 16-byte chunk of the 32-byte pair
-  const int tr_off = 4 * (n & 1);           // element offset inside that chunk
-
-  // One key stage in buffer SLOT: wait for its copies, barrier, refill the other buffer,
-  // then S^T = K Q^T, the online softmax and O^T += V^T P^T.
-  auto stage = [&](int st, auto slot_c) {
-    constexpr int SLOT = decltype(slot_c)::value;
-    const int t0 = st * KS;
-    // This wave's copies of this stage have landed; after the barrier every wave's have,
-    // and every wave is done with the other buffer, which the next stage's copies refill.
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    const bool has_next = st + 1 < st_end;
-    constexpr auto next_slot = std::integral_constant<int, SLOT ^ 1>{};
-    // One-lookup pages at head_dim_vo 512: the next stage's copy instructions are spread
-    // over the S^T steps below, so the vector memory pipe streams them while the MFMAs run
-    // (as one burst here they stall the issuing waves).  The shorter head_dim_vo 256 stage
-    // leaves too little time behind late copies, so there, and for other page sizes, they
-    // are all issued here.
-    constexpr bool SPREAD = PM == kPagesStage && DVO == 512;
-    if constexpr (SPREAD) {
-      copy_prep(st + 1);
-    } else {
-      if (has_next) copy_stage(st + 1, next_slot);
-    }
-    const bool full = st >= full_lo && st < full_hi;
-
-    const uint16_t* kt = k_buf(slot_c);
-    const uint16_t* vt = v_buf(slot_c);
-    // ---- S^T = K Q^T for keys 0..15 (s0) and 16..31 (s1); lane holds keys 4*g4 + i.
-    // Chunk 4j + g4 of row n (or 16 + n) sits at 4*(j ^ (n>>2)) + (g4 ^ (n&3)): four
-    // per-lane bases (one per j % 4) plus compile-time offsets cover every step.
-    // Software-pipelined: the K operands of step j + KD are read before step j's MFMAs, so
-    // KD steps of LDS reads are in flight behind the MFMAs (the fences keep that order).
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    auto qk = [&](auto copy_c) {
-      constexpr bool COPY = decltype(copy_c)::value;
-      constexpr int CSTEP = QSTEPS / NCOPY > 0 ? QSTEPS / NCOPY : 1;
-      static_assert(!COPY || (QSTEPS + CSTEP - 1) / CSTEP >= NCOPY, "copy slots");
-      // Element index of the step-j chunk: kb ^ 32*(j & 3) (bits 5-6 of kb hold n >> 2 and
-      // nothing else does), plus 128*(j >> 2).
-      int kb = n * DQK + 8 * (g4 ^ (n & 3)) + 32 * (n >> 2);
-      asm volatile("" : "+v"(kb));
-      auto ld = [&](int j, u32x4_t& k0, u32x4_t& k1) {
-        const uint16_t* src = kt + ((kb ^ (32 * (j & 3))) + 128 * (j >> 2));
-        k0 = *(const u32x4_t*)src;
-        k1 = *(const u32x4_t*)(src + 16 * DQK);
-      };
-      u32x4_t kr0[KD + 1], kr1[KD + 1];
-#pragma unroll
-      for (int j = 0; j < KD; ++j) ld(j, kr0[j], kr1[j]);
-      static_for<QSTEPS>([&](auto j_c) {
-        constexpr int j = decltype(j_c)::value;
-        if constexpr (j + KD < QSTEPS) ld(j + KD, kr0[(j + KD) % (KD + 1)], kr1[(j + KD) % (KD + 1)]);
-        if constexpr (COPY && j % CSTEP == 0 && j / CSTEP < NCOPY)
-          copy_one(std::integral_constant<int, j / CSTEP>{}, next_slot);
-        const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, qf[j]);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr0[j % (KD + 1)]), qb, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr1[j % (KD + 1)]), qb, s1, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      });
+  // One-lookup pages: the first wave group issues all of the next stage's copies (its rows
+  // and its SIMD partner's), one per S^T step, so the vector memory pipe streams them while
+  // the MFMAs run; the second group issues none (as bursts at the interval start they stall
+  // the issuing waves).  Other page sizes: every wave copies its own rows at the interval
+  // start.
+  constexpr bool SPREAD = PM == kPagesStage;
+  // ---- S^T = K Q^T from K buffer kslot_c into s0 (keys 0..15) and s1 (keys 16..31); lane
+  // holds keys 4*g4 + i.  With COPY the next stage's copies (K into the other buffer, V into
+  // v_lds + vo_next) are issued among the steps.
+  f32x4_t s0, s1;
+  auto qk = [&](auto kslot_c, auto copy_c, int vo_next) {
+    constexpr bool COPY = decltype(copy_c)::value;
+    const uint16_t* kt = k_buf(kslot_c);
+    s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // With COPY this wave issues the copies of its own rows and of its SIMD partner's.
+    constexpr int NQC = 2 * NCOPY;
+    constexpr int CSTEP = QSTEPS / NQC > 0 ? QSTEPS / NQC : 1;
+    static_assert(!COPY || (QSTEPS + CSTEP - 1) / CSTEP >= NQC, "copy slots");
+    // Element index of the step-j chunk: kb ^ 32*(j & 3) (bits 5-6 of kb hold n >> 2 and
+    // nothing else does), plus 128*(j >> 2).
+    int kb = n * DQK + 8 * (g4 ^ (n & 3)) + 32 * (n >> 2);
+    asm volatile("" : "+v"(kb));
+    auto ld = [&](int j, u32x4_t& k0, u32x4_t& k1) {
+      const uint16_t* src = kt + ((kb ^ (32 * (j & 3))) + 128 * (j >> 2));
+      k0 = *(const u32x4_t*)src;
+      k1 = *(const u32x4_t*)(src + 16 * DQK);
     };
-    if (SPREAD && has_next) qk(std::true_type{});
-    else qk(std::false_type{});
+    u32x4_t kr0[KD + 1], kr1[KD + 1];
+#pragma unroll
+    for (int j = 0; j < KD; ++j) ld(j, kr0[j], kr1[j]);
+    static_for<QSTEPS>([&](auto j_c) {
+      constexpr int j = decltype(j_c)::value;
+      if constexpr (j + KD < QSTEPS) ld(j + KD, kr0[(j + KD) % (KD + 1)], kr1[(j + KD) % (KD + 1)]);
+      if constexpr (COPY && j % CSTEP == 0 && j / CSTEP < NQC)
+        copy_one(std::integral_constant<int, j / CSTEP>{},
+                 std::integral_constant<int, decltype(kslot_c)::value ^ 1>{}, vo_next);
+      const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, qf[j]);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr0[j % (KD + 1)]), qb, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr1[j % (KD + 1)]), qb, s1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
 
-    // ---- masks and online softmax of row n (its 32 keys are spread over the 4 lanes g4).
-    // The scale is positive: masks and the max work on raw scores, and the scale folds
-    // into one FMA per key in the exponent.
+  // ---- online softmax of stage stp's scores (s0, s1) into the P^T operand pf, with the
+  // lazy rescale of the running state.
+  u32x4_t pf;
+  // Masks and online softmax of row n (its 32 keys are spread over the 4 lanes g4).  The
+  // scale is positive: masks and the max work on raw scores, and the scale folds into one
+  // FMA per key in the exponent.
+  auto softmax = [&](int stp) {
+    const int t0 = stp * KS;
+    const bool full = stp >= full_lo && stp < full_hi;
     float sv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) sv[i] = i < 4 ? s0[i] : s1[i - 4];
@@ -461,62 +447,122 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     }
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     // P^T operand: k-slot e of lane group g4 is key 4*g4 + e (e < 4) or 16 + 4*g4 + e - 4.
-    u32x4_t pf;
-    {
-      float p[8];
+    float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], c, -m_use));
-        l_run += p[i];
-      }
-      // The output is normalised by the sum of the bf16 weights the MFMA uses, so the
-      // applied weights sum to one (this matters when one key dominates the row); the lse
-      // uses the fp32 sum.
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pf[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
-        l_bf += bf16_lo(pf[e]) + bf16_hi(pf[e]);
-      }
+    for (int i = 0; i < 8; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], c, -m_use));
+      l_run += p[i];
     }
-    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pf);
-
-    // ---- O^T += V^T P^T.  A operand of lane (g4, m=n): V[k-slot keys][dim 16t + m], from
-    // two transpose reads (keys 4*g4 + 0..3 and 16 + 4*g4 + 0..3; both rows have the same
-    // swizzle, and the second is 16 rows below the first).  Chunk 2t + half of the row sits
-    // at 2*(t ^ s) + half with s = row & 7: eight per-lane bases plus constant offsets.
-    // Software-pipelined like S^T: tile t + VD's reads are issued before tile t's MFMA.
-    // The reads are inline assembly (see lds_read_tr16_at), so each MFMA first waits for
-    // its own tile's two reads: at most 2 * (tiles issued after it) reads may be pending.
-    {
-      // Byte address of tile t's chunk: vb ^ 32*(t & 7) (bits 5-7 of vb hold the row
-      // swizzle and nothing else does), plus 256*(t >> 3) as the instruction offset.
-      uint32_t vb = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)(
-                        vt + tr_row * DVO + tr_off + 8 * tr_half) + 32u * (uint32_t)(tr_row & 7);
-      asm volatile("" : "+v"(vb));
-      u32x2_t vlo[VD + 1], vhi[VD + 1];
-      auto ld = [&](auto t_c) {
-        constexpr int t = decltype(t_c)::value;
-        const uint32_t src = vb ^ (32u * (t & 7));
-        vlo[t % (VD + 1)] = lds_read_tr16_at<256 * (t >> 3)>(src);
-        vhi[t % (VD + 1)] = lds_read_tr16_at<256 * (t >> 3) + 32 * DVO>(src);
-      };
-      static_for<VD>([&](auto t_c) { ld(t_c); });
-      static_for<OT>([&](auto t_c) {
-        constexpr int t = decltype(t_c)::value;
-        constexpr int r = t % (VD + 1);
-        if constexpr (t + VD < OT) ld(std::integral_constant<int, t + VD>{});
-        lds_wait<2 * (t + VD < OT ? VD : OT - 1 - t)>(vlo[r], vhi[r]);
-        const u32x4_t vf = {vlo[r][0], vlo[r][1], vhi[r][0], vhi[r][1]};
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf), pb, o[t], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      });
+    // The output is normalised by the sum of the bf16 weights the MFMA uses, so the applied
+    // weights sum to one (this matters when one key dominates the row); the lse uses the
+    // fp32 sum.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pf[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+      l_bf += bf16_lo(pf[e]) + bf16_hi(pf[e]);
     }
   };
 
-  for (int st0 = st_first; st0 < st_end; st0 += 2) {
-    stage(st0, std::integral_constant<int, 0>{});
-    if (st0 + 1 < st_end) stage(st0 + 1, std::integral_constant<int, 1>{});
-  }
+  // ---- O^T += V^T P^T from the V buffer at v_lds + vo.  A operand of lane (g4, m=n):
+  // V[k-slot keys][dim 16t + m], from two transpose reads (keys 4*g4 + 0..3 and
+  // 16 + 4*g4 + 0..3; both rows have the same swizzle, and the second is 16 rows below the
+  // first).  Software-pipelined like S^T: tile t + VD's reads are issued before tile t's
+  // MFMA.  The reads are inline assembly (see lds_read_tr16_at), so each MFMA first waits
+  // for its own tile's two reads: at most 2 * (tiles issued after it) reads may be pending.
+  // Transpose-read source of this lane within its 16-lane block: key (n / 4) of the 4-key
+  // group, dims 4*(n % 4) .. +3 of the 16-dim tile.  Byte address of tile t's chunk:
+  // vb ^ 32*(t & 7) (bits 5-7 of vb hold the row swizzle and nothing else does), plus
+  // 256*(t >> 3) as the instruction offset.
+  const int tr_row = 4 * g4 + (n >> 2);
+  const uint32_t vb_lane =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)(
+          v_lds + tr_row * DVO + 4 * (n & 1) + 8 * ((n & 3) >> 1)) +
+      32u * (uint32_t)(tr_row & 7);
+  auto pv = [&](int vo) {
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pf);
+    uint32_t vb = vb_lane + 2u * (uint32_t)vo;
+    asm volatile("" : "+v"(vb));
+    u32x2_t vlo[VD + 1], vhi[VD + 1];
+    auto ld = [&](auto t_c) {
+      constexpr int t = decltype(t_c)::value;
+      const uint32_t src = vb ^ (32u * (t & 7));
+      vlo[t % (VD + 1)] = lds_read_tr16_at<256 * (t >> 3)>(src);
+      vhi[t % (VD + 1)] = lds_read_tr16_at<256 * (t >> 3) + 32 * DVO>(src);
+    };
+    static_for<VD>([&](auto t_c) { ld(t_c); });
+    static_for<OT>([&](auto t_c) {
+      constexpr int t = decltype(t_c)::value;
+      constexpr int r = t % (VD + 1);
+      if constexpr (t + VD < OT) ld(std::integral_constant<int, t + VD>{});
+      lds_wait<2 * (t + VD < OT ? VD : OT - 1 - t)>(vlo[r], vhi[r]);
+      const u32x4_t vf = {vlo[r][0], vlo[r][1], vhi[r][0], vhi[r][1]};
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf), pb, o[t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // ---- the stage loop, one interval per stage.  Stage st's K sits in K buffer
+  // (st - st_first) % 2, its V at v_lds + (st - st_first) % 3 * VSTAGE.  Interval st waits
+  // for stage st's copies and meets the other waves at the barrier, then copies stage
+  // st + 1.  The two waves sharing a SIMD (w and w + 4) work in rotated order, so that one's
+  // softmax runs while the other's MFMAs do: the first group does S^T(st), softmax(st) and
+  // O += V P^T(st); the second does softmax(st - 1) and O += V P^T(st - 1) (with stage st -
+  // 1's scores kept from the previous interval), then S^T(st), and after the last interval
+  // the last stage's softmax and O update.  After barrier st every wave is done with stage
+  // st - 1's K buffer (read in interval st - 1 by both groups) and with stage st - 2's V
+  // buffer (read in interval st - 2 by the first group and st - 1 by the second), which the
+  // copies of stage st + 1 refill.
+  const bool second = w >= NW / 2;
+  int vo_prev = 2 * VSTAGE, vo_cur = 0, vo_next = VSTAGE;
+  if (st_first < st_end) copy_stage(st_first, std::integral_constant<int, 0>{}, 0);
+  auto interval = [&](int st, auto kslot_c, auto second_c) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    const bool has_next = st + 1 < st_end;
+    constexpr auto other_c = std::integral_constant<int, decltype(kslot_c)::value ^ 1>{};
+    if constexpr (decltype(second_c)::value) {
+      if (!SPREAD && has_next) copy_stage(st + 1, other_c, vo_next);
+      if (st > st_first) {
+        softmax(st - 1);
+        pv(vo_prev);
+      }
+      qk(kslot_c, std::false_type{}, vo_next);
+    } else {
+      if constexpr (SPREAD) {
+        if (has_next) {
+          copy_prep(st + 1);
+          qk(kslot_c, std::true_type{}, vo_next);
+        } else {
+          qk(kslot_c, std::false_type{}, vo_next);
+        }
+      } else {
+        if (has_next) copy_stage(st + 1, other_c, vo_next);
+        qk(kslot_c, std::false_type{}, vo_next);
+      }
+      softmax(st);
+      pv(vo_cur);
+    }
+    const int t = vo_prev;
+    vo_prev = vo_cur;
+    vo_cur = vo_next;
+    vo_next = t;
+  };
+  // Separate loops per group (one loop holding both orders made the register allocator
+  // spill); both meet the same barriers, one per interval.
+  auto run = [&](auto second_c) {
+    for (int st = st_first; st < st_end; st += 2) {
+      interval(st, std::integral_constant<int, 0>{}, second_c);
+      if (st + 1 < st_end) interval(st + 1, std::integral_constant<int, 1>{}, second_c);
+    }
+    if constexpr (decltype(second_c)::value) {
+      if (st_first < st_end) {
+        softmax(st_end - 1);
+        pv(vo_prev);
+      }
+    }
+  };
+  if (second) run(std::true_type{});
+  else run(std::false_type{});
 
   // ---- normalise and write row n: O^T tile t, register i holds dim 16t + 4*g4 + i.
   const float l_tot = sum_xor32(sum_xor16(l_run));
