@@ -123,7 +123,7 @@ typedef struct pa_plan {
   int32_t num_merges;              /* decode: (request, kv head) pairs the merge writes  */
   int32_t block_tokens;            /* decode: key block of the partition (16)           */
   int32_t chunk_blocks;            /* decode: longest wave, in blocks                   */
-  int32_t num_splits;              /* decode: requested splits (0 = balanced)           */
+  int32_t num_splits;              /* decode: split-K chunk count (0 = no chunk cuts)    */
   int32_t tile_rows;               /* prefill: query rows (token, head) per tile        */
   int32_t total_q;                 /* prefill: number of query tokens                   */
   int32_t max_kv_len;
@@ -162,13 +162,14 @@ pa_status pa_validate_page_table_host(const int32_t* kv_indptr_host,
 /* Plans a decode batch from host copies of kv_indptr and kv_last_page_len (the device
  * copies passed to pa_paged_decode must hold the same values).  The work is the set of
  * (request, kv head, 16-token key block) units; each wave of the partial kernel runs one
- * piece of them.  num_splits == 0 (balanced) cuts the units, flattened in (request,
- * kv head, block) order, into min(2048, ceil(units / 8)) equal pieces, i.e. one wave per
- * SIMD slot of the 256 CUs at two waves per SIMD, so every wave streams the same number
- * of bytes.  num_splits > 0 instead cuts each (request, kv head) into
- * min(num_splits, blocks) near-equal pieces.  A piece is cut at (request, kv head)
- * boundaries into segments; a (request, kv head) with several segments is merged by
- * log-sum-exp weights.  Waves run longest first.  Call with plan_buf_host == NULL to
+ * piece of them: the units, flattened in (request, kv head, block) order, are cut into
+ * min(2048, ceil(units / 8)) equal pieces, i.e. one wave per SIMD slot of the 256 CUs at
+ * two waves per SIMD, so every wave streams the same number of bytes.  A piece is cut at
+ * (request, kv head) boundaries into segments.  num_splits S > 0 (split-K S) also cuts
+ * each (request, kv head) at the boundaries of its min(S, blocks) near-equal chunks, so
+ * every chunk is computed by whole segments; S == 0 adds no cuts.  A (request, kv head)
+ * with several segments is merged by log-sum-exp weights (the result does not depend on
+ * the cuts).  Waves run longest first.  Call with plan_buf_host == NULL to
  * learn plan->plan_bytes (and plan->workspace_bytes); then call again with a buffer of
  * at least that size.
  * Supported: head dims (512,512), (256,256), (512,256); kv bf16 or FP8 E4M3FN;

@@ -16,11 +16,12 @@ Decode rule (units of 16-token logical blocks, block j = tokens [16j, 16j+16)):
 * Visible blocks: fb = s_b // 16, eb = ceil(L_b / 16), n_b = max(0, eb - fb).
 * Work units are the (request b, KV head h, block j) triples, flattened in (b, h, j)
   order; the range of (b, h) is [o_bh, o_bh + n_b) and U is the total.
-* Pieces (one wave each): balanced (num_splits S = 0) cuts the flattened axis into
-  P = min(WAVE_SLOTS, ceil(U / MIN_PIECE_BLOCKS)) pieces [U p // P, U (p+1) // P); a
-  fixed split S > 0 cuts every (b, h) range on its own into c = min(S, n_b) pieces
-  [o_bh + n_b k // c, o_bh + n_b (k+1) // c).
-* A piece is cut at (b, h) boundaries into segments; blocks [j0, j1) of (b, h) cover the
+* Pieces (one wave each) cut the flattened axis into P = min(WAVE_SLOTS,
+  ceil(U / MIN_PIECE_BLOCKS)) near-equal parts [U p // P, U (p+1) // P).
+* A fixed split S > 0 (split-K S) cuts every (b, h) range into c = min(S, n_b) chunks
+  [o_bh + n_b k // c, o_bh + n_b (k+1) // c); S = 0 adds no cuts.
+* A piece is cut at (b, h) boundaries and at chunk boundaries into segments, so every
+  chunk is computed by one or more whole segments; blocks [j0, j1) of (b, h) cover the
   keys [max(s_b, 16 (fb + j0)), min(L_b, 16 (fb + j1))).
 * A (b, h) with several segments owns that many consecutive workspace slots, in segment
   order, slots numbered in (b, h) order, and gets a merge entry (b, h, first slot, count);
@@ -64,15 +65,17 @@ def decode_partition_ref(kv_lens, window, num_splits, num_kv_heads):
         origin.append(total)
         total += nblk[b]
 
-    if num_splits > 0:
-        pieces = []
-        for i, (b, h) in enumerate(pairs):
-            n = nblk[b]
+    p = min(WAVE_SLOTS, _ceil_div(total, MIN_PIECE_BLOCKS))
+    pieces = [(total * k // p, total * (k + 1) // p) for k in range(p)]
+
+    def cuts_of(i):  # unit positions that end a segment inside pair i's range
+        b = pairs[i][0]
+        n = nblk[b]
+        ends = {origin[i] + n}
+        if num_splits > 0 and n > 0:
             c = min(num_splits, n)
-            pieces += [(origin[i] + n * k // c, origin[i] + n * (k + 1) // c) for k in range(c)]
-    else:
-        p = min(WAVE_SLOTS, _ceil_div(total, MIN_PIECE_BLOCKS))
-        pieces = [(total * k // p, total * (k + 1) // p) for k in range(p)]
+            ends |= {origin[i] + n * k // c for k in range(1, c)}
+        return sorted(ends)
 
     def pair_of(u):  # the (b, h) whose range holds flattened unit u (empty ranges hold none)
         for i in range(len(pairs)):
@@ -86,7 +89,7 @@ def decode_partition_ref(kv_lens, window, num_splits, num_kv_heads):
         while u < u1:
             i = pair_of(u)
             b, h = pairs[i]
-            e = min(u1, origin[i] + nblk[b])
+            e = min([u1] + [x for x in cuts_of(i) if x > u])
             fb = starts[b] // BLOCK_TOKENS
             t0 = max(starts[b], (fb + u - origin[i]) * BLOCK_TOKENS)
             t1 = min(lens[b], (fb + e - origin[i]) * BLOCK_TOKENS)

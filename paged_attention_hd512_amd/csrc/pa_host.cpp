@@ -266,21 +266,32 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
   for (int64_t i = 0; i < npairs; ++i) origin[i + 1] = origin[i] + nblk[i / hkv];
   const int64_t total = origin[npairs];
 
+  // Pieces (one wave each): the flattened axis in near-equal parts.
   std::vector<std::pair<int64_t, int64_t>> pieces;
-  if (num_splits > 0) {
-    for (int64_t i = 0; i < npairs; ++i) {
-      const int64_t n = nblk[i / hkv];
-      const int64_t c = std::min<int64_t>(num_splits, n);
-      for (int64_t k = 0; k < c; ++k)
-        pieces.emplace_back(origin[i] + n * k / c, origin[i] + n * (k + 1) / c);
-    }
-  } else {
+  {
     const int64_t np = std::min<int64_t>(kDecodeWaveSlots, (total + kMinPieceBlocks - 1) / kMinPieceBlocks);
     for (int64_t k = 0; k < np; ++k) pieces.emplace_back(total * k / np, total * (k + 1) / np);
   }
+  // End of the segment that starts at unit u of pair i: the pair's end, or with a fixed
+  // split S the next of the S chunk boundaries of the pair, [o + n k / c) with c = min(S, n).
+  auto segment_end = [&](int64_t i, int64_t u) {
+    int64_t e = origin[i + 1];
+    if (num_splits > 0) {
+      const int64_t n = origin[i + 1] - origin[i];
+      const int64_t c = std::min<int64_t>(num_splits, n);
+      for (int64_t k = 1; k < c; ++k) {
+        const int64_t cut = origin[i] + n * k / c;
+        if (cut > u) {
+          e = cut;
+          break;
+        }
+      }
+    }
+    return e;
+  };
 
-  // Cut each piece into segments at (b, h) boundaries; pieces run in flattened order, so
-  // the pair index only moves forward.
+  // Cut each piece into segments at (b, h) boundaries (and fixed-split chunk boundaries);
+  // pieces run in flattened order, so the pair index only moves forward.
   std::vector<std::vector<DecodeSegment>> piece_segs(pieces.size());
   std::vector<int32_t> seg_count(npairs, 0);
   int64_t pair = 0;
@@ -290,7 +301,7 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
     while (u < u1) {
       while (origin[pair + 1] <= u) ++pair;  // skips empty ranges too
       const int32_t b = (int32_t)(pair / hkv), h = (int32_t)(pair % hkv);
-      const int64_t e = std::min<int64_t>(u1, origin[pair + 1]);
+      const int64_t e = std::min<int64_t>(u1, segment_end(pair, u));
       const int64_t fb = start[b] / kBlockTokens;
       const int64_t t0 = std::max<int64_t>(start[b], (fb + u - origin[pair]) * kBlockTokens);
       const int64_t t1 = std::min<int64_t>(len[b], (fb + e - origin[pair]) * kBlockTokens);

@@ -100,8 +100,9 @@ def test_decode_plan_matches_reference_partition(lens, P, window, splits, hkv):
 @pytest.mark.parametrize("lens,P,window,splits,hkv", DECODE_CASES)
 def test_reference_partition_covers_visible_keys_exactly(lens, P, window, splits, hkv):
     """Every visible key of every (request, KV head) lies in exactly one segment; inner
-    cuts fall on 16-key blocks; balanced waves differ by at most one block; slots of a
-    merged pair are consecutive in key order; single-segment pairs write directly."""
+    cuts fall on 16-key blocks; waves differ by at most one block; a fixed split's chunk
+    boundaries are segment boundaries; slots of a merged pair are consecutive in key
+    order; single-segment pairs write directly."""
     waves, merges = decode_partition_ref(lens, window, splits, hkv)
     per_pair = {}
     for w in waves:
@@ -126,10 +127,16 @@ def test_reference_partition_covers_visible_keys_exactly(lens, P, window, splits
                 s0, k = merged[(b, h)]
                 assert k == len(segs) and [s for _, _, s in segs] == list(range(s0, s0 + k))
             if splits > 0:
-                assert len(segs) == min(splits, -(-L // 16) - start // 16)
+                # split-K S: the S near-equal chunk boundaries of the pair's blocks are
+                # segment boundaries (each chunk is one or more whole segments).
+                fb, n = start // 16, -(-L // 16) - start // 16
+                c = min(splits, n)
+                starts = {t0 for t0, _, _ in segs}
+                assert {16 * (fb + n * k // c) for k in range(1, c)} <= starts
+                assert len(segs) >= c
     blocks = [sum(-(-t1 // 16) - t0 // 16 for _, _, t0, t1, _ in w) for w in waves]
     assert blocks == sorted(blocks, reverse=True)  # longest first
-    if splits == 0 and waves:
+    if waves:
         assert max(blocks) - min(blocks) <= 1 and len(waves) <= 2048
     slots = sorted(s for w in waves for *_, s in w if s >= 0)
     assert slots == list(range(len(slots)))  # every slot written once
