@@ -79,6 +79,21 @@ def prefill_algorithmic_flops(case, requests=None):
     return int(total)
 
 
+def extend_algorithmic_bytes(case):
+    """HBM bytes a short-query prefill must move: for each (request, KV head) the K and V
+    rows of every key some row of the request sees, plus Q and the output."""
+    total = 0
+    for b in range(case.batch):
+        q_len, L = int(case.qo_lens[b]), int(case.kv_lens[b])
+        if q_len == 0:
+            continue
+        lo = max(0, L - q_len - case.window + 1) if case.window > 0 else 0
+        hi = L if case.causal else L
+        total += case.num_kv_heads * max(0, hi - lo) * (case.head_dim_qk + case.head_dim_vo) * 2
+        total += q_len * case.num_qo_heads * (case.head_dim_qk * 2 + case.head_dim_vo * 2)
+    return int(total)
+
+
 # ----------------------------------------------------------------------------- timing
 
 def time_decode(case, steps, warmup):
@@ -314,6 +329,26 @@ def measure_prefill(name, steps, warmup, head_dim_vo):
     }
 
 
+def measure_extend(name, steps, warmup):
+    """Short-query extend: the whole call (prefill kernel over key chunks + merge) against
+    the algorithmic HBM bytes."""
+    from synth import prefill_workload
+    case = prefill_workload(name, device="cuda", head_dim_vo=512)
+    step_ms, kern_ms, wall_ms, plan = time_prefill(case, steps, warmup)
+    nbytes = extend_algorithmic_bytes(case)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    return {
+        "case": case, "bytes": nbytes, "step_ms": step_ms, "wall_ms": wall_ms,
+        "kernel_ms": kern_ms, "value": nbytes / (step_ms * 1e-3) / 1e9,
+        "plan": {"items": plan.num_items, "split_tiles": plan.num_merges,
+                 "partial_slots": plan.num_slots, "chunk_stages": plan.chunk_blocks},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "prefill_kernel + prefill_merge_kernel",
+                     "algorithmic_bytes_per_launch": nbytes, "kernel_avg_ms": round(kern_ms, 5)},
+    }
+
+
 def copy_calibration(nbytes=1 << 30, steps=5):
     """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -334,7 +369,7 @@ def main():
     ap.add_argument("--workload", default="gqa_decode",
                     help="gqa_decode | gqa_decode_splitk8 | fp8_decode | "
                          "window_decode_d512_p1 | ... | "
-                         "causal_prefill_vo512 | causal_prefill_vo256")
+                         "causal_prefill_vo512 | causal_prefill_vo256 | extend_prefill")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -359,6 +394,8 @@ def main():
         if wl.startswith("causal_prefill_vo"):
             return measure_prefill("causal_prefill", args.steps, args.warmup,
                                    int(wl[len("causal_prefill_vo"):]))
+        if wl == "extend_prefill":
+            return measure_extend(wl, args.steps, args.warmup)
         if wl.startswith("gqa_decode_splitk"):
             return measure_decode("gqa_decode", args.steps, args.warmup,
                                   wl[len("gqa_decode_"):])
@@ -366,11 +403,11 @@ def main():
 
     main_res = run_named(args.workload)
     case = main_res["case"]
-    is_prefill = "flops" in main_res
+    is_prefill = "flops" in main_res or args.workload == "extend_prefill"
     line = {
         "metric": METRIC,
         "value": round(main_res["value"], 3),
-        "unit": "TFLOP/s" if is_prefill else "GB/s",
+        "unit": "TFLOP/s" if "flops" in main_res else "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(main_res["step_ms"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -385,8 +422,9 @@ def main():
         "wall_ms_per_step": round(main_res["wall_ms"], 5),
         "kernel_source_hash": kernel_source_hash(),
     }
-    if not is_prefill:
+    if "merge_ms" in main_res:
         line["merge_ms"] = round(main_res["merge_ms"], 5)
+    if "plan" in main_res:
         line["plan"] = main_res["plan"]
     if not args.no_cpu_baseline:
         if is_prefill:
@@ -401,7 +439,7 @@ def main():
         names = ["gqa_decode", "gqa_decode_splitk8", "fp8_decode", "window_decode_d512_p1",
                  "window_decode_d512_p32",
                  "window_decode_d256_p1", "window_decode_d256_p32", "causal_prefill_vo512",
-                 "causal_prefill_vo256"]
+                 "causal_prefill_vo256", "extend_prefill"]
         for wl in names:
             if wl == args.workload:
                 continue
@@ -413,6 +451,8 @@ def main():
             unit = "TFLOP/s" if "flops" in r else "GB/s"
             sec[wl] = {"value": round(r["value"], 3), "unit": unit,
                        "ms_per_step": round(r["step_ms"], 5), "roofline": r["roofline"]}
+            if "plan" in r and wl == "extend_prefill":
+                sec[wl]["plan"] = r["plan"]
             del r
             torch.cuda.empty_cache()
         line["secondary"] = sec

@@ -117,12 +117,14 @@ typedef struct pa_plan {
   int32_t kv_dtype;
   int32_t window;
   int32_t causal;
-  int32_t num_items;               /* decode: key segments; prefill: tiles (one
-                                      workgroup per (tile, kv head))                    */
-  int32_t num_slots;               /* decode: partial-result slots in the workspace     */
-  int32_t num_merges;              /* decode: (request, kv head) pairs the merge writes  */
+  int32_t num_items;               /* decode: key segments; prefill: tiles and key chunks
+                                      (one workgroup per (item, kv head))               */
+  int32_t num_slots;               /* partial-result slots in the workspace             */
+  int32_t num_merges;              /* decode: (request, kv head) pairs the merge writes;
+                                      prefill: split tiles                              */
   int32_t block_tokens;            /* decode: key block of the partition (16)           */
-  int32_t chunk_blocks;            /* decode: longest wave, in blocks                   */
+  int32_t chunk_blocks;            /* decode: longest wave, in blocks; prefill: chunk
+                                      length in 32-key stages (0: no split)             */
   int32_t num_splits;              /* decode: split-K chunk count (0 = no chunk cuts)    */
   int32_t tile_rows;               /* prefill: query rows (token, head) per tile        */
   int32_t total_q;                 /* prefill: number of query tokens                   */
@@ -183,9 +185,16 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
 /* Plans a prefill batch.  qo_indptr_host [batch + 1] gives each request's new tokens,
  * which must not outnumber its KV tokens; row i of request b sits at key position
  * L_b - q_len_b + i.  Query rows of one (request, KV head) are the (token, head) pairs of
- * its head group, tiled in plan->tile_rows; tiles run longest first.  Same two-call
- * sizing as pa_decode_plan.  Supported: head dims (512,512), (256,256), (512,256); kv
- * bf16; q bf16; out fp32 or bf16; num_qo_heads / num_kv_heads <= 16.  Never calls HIP. */
+ * its head group, tiled in plan->tile_rows; a tile sees the keys some of its rows see.
+ * Split-K for short queries over long KV: when tiles x num_kv_heads < 512, every tile
+ * whose keys span more than C 32-key stages, C = max(8, ceil(total stages x num_kv_heads
+ * / 512)), is cut into ceil(stages / C) near-equal runs of whole stages; each such chunk
+ * writes a partial (normalised output and log-sum-exps) to its own workspace slot and a
+ * merge combines them (plan->num_merges split tiles, plan->num_slots slots,
+ * plan->chunk_blocks = C, 0 without splitting).  Items run by key count, longest first.
+ * The result does not depend on the split.  Same two-call sizing as pa_decode_plan.
+ * Supported: head dims (512,512), (256,256), (512,256); kv bf16; q bf16; out fp32 or bf16;
+ * num_qo_heads / num_kv_heads <= 16.  Never calls HIP. */
 pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache,
                           const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
                           const int32_t* kv_last_page_len_host, int32_t batch,
@@ -226,7 +235,8 @@ pa_status pa_paged_decode_merge(const pa_plan* plan, const void* q, const pa_kv_
 /* Enqueues one prefill: q [total_q, num_qo_heads, head_dim_qk] bf16 (contiguous, ragged
  * by qo_indptr) -> out [total_q, num_qo_heads, head_dim_vo] in params->out_dtype and
  * optional lse [total_q, num_qo_heads] fp32.  qo_indptr is the device copy of the array
- * given to pa_prefill_plan. */
+ * given to pa_prefill_plan.  One kernel launch, or two when the plan splits tiles (the
+ * chunk partials go to the workspace, then a merge kernel writes their rows). */
 pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const int32_t* qo_indptr,
                            const pa_kv_cache* cache, const pa_page_table* table,
                            const pa_attn_params* params, void* out, float* lse,

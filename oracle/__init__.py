@@ -32,7 +32,7 @@ from .attention import (
     chunk_partial_ref,
     merge_ref,
 )
-from .partition import decode_partition_ref, prefill_tiles_ref
+from .partition import decode_partition_ref, prefill_plan_ref
 
 __all__ = [
     "bf16_bits_to_f64",
@@ -48,5 +48,5 @@ __all__ = [
     "chunk_partial_ref",
     "merge_ref",
     "decode_partition_ref",
-    "prefill_tiles_ref",
+    "prefill_plan_ref",
 ]

@@ -33,13 +33,24 @@ Prefill rule: the query rows of one (request, KV head) are the q_len * G pairs
 (token i, head g) flattened as i * G + g; tiles of ``tile_rows`` consecutive rows;
 a tile sees keys [kv_begin, kv_end) with kv_end = pos(last token) + 1 under the causal
 mask (L_b without it) and kv_begin = max(0, pos(first token) - W + 1) with a window.
-Tiles run by key count descending, ties in (b, tile) order.
+Split-K (a short query over a long KV; the split-KV geometry of [VO-split] section "NVFP4
+split-KV correctness (added)"): a tile's stages are the 32-key blocks it touches,
+S = ceil(kv_end / 32) - kv_begin // 32.  When tiles x H_kv < SPLIT_ITEMS, with
+C = max(MIN_CHUNK_STAGES, ceil(total S x H_kv / SPLIT_ITEMS)), every tile with S > C is cut
+into c = ceil(S / C) chunks covering keys [max(kv_begin, 32 (s0 + S k // c)),
+min(kv_end, 32 (s0 + S (k+1) // c))), s0 = kv_begin // 32; chunks take consecutive
+partial slots in (b, tile, chunk) order and the tile a merge entry (b, row_begin, row_end,
+q_begin, first slot, c).  Items run by key count descending, ties in (b, tile, chunk)
+order.
 """
 
 BLOCK_TOKENS = 16
 WAVE_SLOTS = 2048
 MIN_PIECE_BLOCKS = 8
 MAX_SPLITS = 64
+PREFILL_STAGE = 32
+SPLIT_ITEMS = 512
+MIN_CHUNK_STAGES = 8
 
 
 def _ceil_div(a, b):
@@ -123,9 +134,14 @@ def decode_partition_ref(kv_lens, window, num_splits, num_kv_heads):
     return waves, merges
 
 
-def prefill_tiles_ref(qo_lens, kv_lens, group, tile_rows, causal, window):
-    """Returns the list of (b, row_begin, row_end, kv_begin, kv_end) in execution order."""
-    tiles = []
+def prefill_plan_ref(qo_lens, kv_lens, group, tile_rows, causal, window, num_kv_heads):
+    """Returns (items, merges).
+
+    items:  in execution order, each (b, row_begin, row_end, kv_begin, kv_end, slot), slot
+            -1 for a tile computed whole.
+    merges: (b, row_begin, row_end, q_begin, slot_begin, num_slots) per split tile.
+    """
+    tiles, q_begin = [], 0
     for b, (q_len, length) in enumerate(zip(qo_lens, kv_lens)):
         q_len, length = int(q_len), int(length)
         rows = q_len * group
@@ -135,6 +151,29 @@ def prefill_tiles_ref(qo_lens, kv_lens, group, tile_rows, causal, window):
             pos_last = length - q_len + (r1 - 1) // group
             kv_end = pos_last + 1 if causal else length
             kv_begin = max(0, pos_first - window + 1) if window > 0 else 0
-            tiles.append((b, r0, r1, kv_begin, kv_end, j))
-    tiles.sort(key=lambda t: (-(t[4] - t[3]), t[0], t[5]))
-    return [t[:5] for t in tiles]
+            tiles.append((b, r0, r1, kv_begin, kv_end, q_begin))
+        q_begin += q_len
+
+    def stages(t):
+        return _ceil_div(t[4], PREFILL_STAGE) - t[3] // PREFILL_STAGE if t[4] > t[3] else 0
+
+    chunk = 0
+    if len(tiles) * num_kv_heads < SPLIT_ITEMS:
+        chunk = max(MIN_CHUNK_STAGES,
+                    _ceil_div(sum(stages(t) for t in tiles) * num_kv_heads, SPLIT_ITEMS))
+    items, merges, slots = [], [], 0
+    for t in tiles:
+        b, r0, r1, kb, ke, qb = t
+        s = stages(t)
+        if chunk == 0 or s <= chunk:
+            items.append((b, r0, r1, kb, ke, -1))
+            continue
+        c = _ceil_div(s, chunk)
+        merges.append((b, r0, r1, qb, slots, c))
+        s0 = kb // PREFILL_STAGE
+        for k in range(c):
+            items.append((b, r0, r1, max(kb, PREFILL_STAGE * (s0 + s * k // c)),
+                          min(ke, PREFILL_STAGE * (s0 + s * (k + 1) // c)), slots))
+            slots += 1
+    order = sorted(range(len(items)), key=lambda i: (-(items[i][4] - items[i][3]), i))
+    return [items[i] for i in order], merges

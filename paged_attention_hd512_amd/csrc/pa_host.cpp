@@ -419,25 +419,77 @@ pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache
       const int64_t pos_last = L - q_len + (r1 - 1) / group;
       const int64_t kv_end = causal ? pos_last + 1 : L;
       const int64_t kv_begin = window > 0 ? std::max<int64_t>(0, pos_first - window + 1) : 0;
-      tiles.push_back(Tmp{PrefillItem{b, (int32_t)r0, (int32_t)r1, (int32_t)kv_begin,
-                                      (int32_t)kv_end, qo_indptr_host[b], (int32_t)L,
-                                      (int32_t)q_len},
-                          j});
+      PrefillItem it;
+      memset(&it, 0, sizeof(it));
+      it.b = b; it.row_begin = (int32_t)r0; it.row_end = (int32_t)r1;
+      it.kv_begin = (int32_t)kv_begin; it.kv_end = (int32_t)kv_end;
+      it.q_begin = qo_indptr_host[b]; it.kv_len = (int32_t)L; it.q_len = (int32_t)q_len;
+      it.slot = -1;
+      tiles.push_back(Tmp{it, j});
     }
   }
-  std::stable_sort(tiles.begin(), tiles.end(), [](const Tmp& a, const Tmp& b) {
+  // Split-K (a short query over a long KV): with fewer than kPrefillSplitItems workgroups,
+  // tile key ranges longer than `chunk` stages are cut into ceil(stages / chunk) near-equal
+  // runs of whole stages; each chunk writes a partial to its own slot (slots numbered in
+  // tile order) and the tile gets a merge entry.
+  const int64_t hkv = cache->num_kv_heads;
+  auto stages_of = [](const PrefillItem& it) -> int64_t {
+    return it.kv_end > it.kv_begin
+               ? (it.kv_end + kPrefillKeyStage - 1) / kPrefillKeyStage - it.kv_begin / kPrefillKeyStage
+               : 0;
+  };
+  int64_t chunk = 0;
+  if ((int64_t)tiles.size() * hkv < kPrefillSplitItems) {
+    int64_t total = 0;
+    for (const Tmp& t : tiles) total += stages_of(t.it);
+    chunk = std::max<int64_t>(kPrefillMinChunkStages,
+                              (total * hkv + kPrefillSplitItems - 1) / kPrefillSplitItems);
+  }
+  std::vector<Tmp> items;
+  std::vector<PrefillMerge> merges;
+  int64_t num_slots = 0;
+  for (const Tmp& t : tiles) {
+    const int64_t s = stages_of(t.it);
+    if (chunk == 0 || s <= chunk) {
+      items.push_back(t);
+      continue;
+    }
+    const int64_t c = (s + chunk - 1) / chunk;
+    PrefillMerge m;
+    memset(&m, 0, sizeof(m));
+    m.b = t.it.b; m.row_begin = t.it.row_begin; m.row_end = t.it.row_end;
+    m.q_begin = t.it.q_begin; m.slot_begin = (int32_t)num_slots; m.num_slots = (int32_t)c;
+    merges.push_back(m);
+    const int64_t s0 = t.it.kv_begin / kPrefillKeyStage;
+    for (int64_t k = 0; k < c; ++k) {
+      Tmp u = t;
+      u.it.kv_begin = (int32_t)std::max<int64_t>(t.it.kv_begin, (s0 + s * k / c) * kPrefillKeyStage);
+      u.it.kv_end = (int32_t)std::min<int64_t>(t.it.kv_end, (s0 + s * (k + 1) / c) * kPrefillKeyStage);
+      u.it.slot = (int32_t)num_slots++;
+      items.push_back(u);
+    }
+  }
+  if (num_slots > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many prefill partials");
+  std::stable_sort(items.begin(), items.end(), [](const Tmp& a, const Tmp& b) {
     return (a.it.kv_end - a.it.kv_begin) > (b.it.kv_end - b.it.kv_begin);
   });
   plan_header(plan, 2, params, cache, batch);
-  plan->num_items = (int32_t)tiles.size();
+  plan->num_items = (int32_t)items.size();
+  plan->num_merges = (int32_t)merges.size();
+  plan->num_slots = (int32_t)num_slots;
+  plan->chunk_blocks = (int32_t)chunk;
   plan->tile_rows = kPrefillTileRows;
   plan->total_q = batch > 0 ? qo_indptr_host[batch] : 0;
   plan->max_kv_len = (int32_t)max_len;
   plan->items_offset = 0;
-  plan->merges_offset = align_up((int64_t)tiles.size() * sizeof(PrefillItem), 16);
-  plan->plan_bytes = align_up(plan->merges_offset, 256);
-  plan->partial_o_offset = plan->partial_lse_offset = plan->plan_bytes;
-  plan->workspace_bytes = plan->plan_bytes;
+  plan->merges_offset = align_up((int64_t)items.size() * sizeof(PrefillItem), 16);
+  plan->plan_bytes = align_up(plan->merges_offset + (int64_t)merges.size() * sizeof(PrefillMerge), 256);
+  // Partials: o [slot][kv head][tile row][head_dim_vo] fp32; lse [slot][kv head][tile row]
+  // x 2 fp32 (log2 domain: over the bf16-rounded weights, then over the fp32 weights).
+  plan->partial_o_offset = plan->plan_bytes;
+  const int64_t part_rows = num_slots * hkv * kPrefillTileRows;
+  plan->partial_lse_offset = align_up(plan->partial_o_offset + part_rows * cache->head_dim_vo * 4, 256);
+  plan->workspace_bytes = align_up(plan->partial_lse_offset + part_rows * 2 * 4, 256);
   if (!plan_buf_host) return PA_OK;
   if ((int64_t)plan_buf_bytes < plan->plan_bytes)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "plan buffer has %zu bytes, plan needs %lld",
@@ -445,7 +497,9 @@ pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache
   char* buf = (char*)plan_buf_host;
   memset(buf, 0, (size_t)plan->plan_bytes);
   PrefillItem* out = (PrefillItem*)(buf + plan->items_offset);
-  for (size_t i = 0; i < tiles.size(); ++i) out[i] = tiles[i].it;
+  for (size_t i = 0; i < items.size(); ++i) out[i] = items[i].it;
+  if (!merges.empty())
+    memcpy(buf + plan->merges_offset, merges.data(), merges.size() * sizeof(PrefillMerge));
   return PA_OK;
 }
 

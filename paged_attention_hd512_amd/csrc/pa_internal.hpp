@@ -19,6 +19,13 @@ constexpr int kMaxPrefillGroup = 16;
 
 // Prefill: query rows per tile ((token, head) pairs of one head group).
 constexpr int kPrefillTileRows = 128;
+constexpr int kPrefillKeyStage = 32;  // keys per LDS stage of the prefill kernel
+// Split-K prefill (a short query over a long KV): when the tiles give fewer than
+// kPrefillSplitItems workgroups (tiles x KV heads), tile key ranges longer than the chunk
+// length are cut into chunks of whole 32-key stages, chunk length =
+// max(kPrefillMinChunkStages, ceil(total stages x KV heads / kPrefillSplitItems)).
+constexpr int kPrefillSplitItems = 512;
+constexpr int kPrefillMinChunkStages = 8;
 
 struct DecodeSegment {  // 32 bytes: blocks of one (request, KV head) run by one wave
   int32_t b;             // request
@@ -36,15 +43,29 @@ struct MergeItem {       // 16 bytes
   int32_t num_slots;     // 0: the request has no keys (zero output, lse -inf)
 };
 
-struct PrefillItem {  // 32 bytes
+struct PrefillItem {  // 48 bytes
   int32_t b;
   int32_t row_begin;  // first (token, head) row of the tile within the request's group
   int32_t row_end;
-  int32_t kv_begin;   // keys the tile can see: [kv_begin, kv_end)
+  int32_t kv_begin;   // keys this item covers: [kv_begin, kv_end)
   int32_t kv_end;
   int32_t q_begin;    // qo_indptr[b]
   int32_t kv_len;     // L_b
   int32_t q_len;      // qo_indptr[b+1] - qo_indptr[b]
+  int32_t slot;       // -1: the tile's whole key range, written to the output; else the
+                      // partial slot of one key chunk of a split tile
+  int32_t pad[3];
+};
+
+// One split tile: its chunks' partials sit in slots [slot_begin, slot_begin + num_slots).
+struct PrefillMerge {  // 32 bytes
+  int32_t b;
+  int32_t row_begin;
+  int32_t row_end;
+  int32_t q_begin;
+  int32_t slot_begin;
+  int32_t num_slots;
+  int32_t pad[2];
 };
 
 pa_status fail(pa_status code, const char* fmt, ...);

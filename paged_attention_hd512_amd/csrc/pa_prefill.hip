@@ -37,7 +37,7 @@
 namespace pa {
 
 constexpr int kPrefillWaves = 8;          // 16 query rows each: 128 rows per tile
-constexpr int kKeyStage = 32;             // keys per LDS stage (double-buffered)
+constexpr int kKeyStage = kPrefillKeyStage;  // keys per LDS stage
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 // How a stage's key rows are found in the pages.
@@ -56,6 +56,8 @@ struct PrefillArgs {
   const PrefillItem* items;
   void* out;                  // [total_q, Hq, DVO]
   float* lse;                 // [total_q, Hq] or null
+  float* part_o;              // split tiles: [slot][kv head][tile row][DVO] fp32
+  float* part_lse;            // [slot][kv head][tile row][2] fp32, log2 domain
   int32_t num_qo_heads;
   int32_t num_kv_heads;
   int32_t group;
@@ -569,6 +571,20 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   const float l_bf_tot = sum_xor32(sum_xor16(l_bf));
   if (!row_valid) return;
   const float inv = l_bf_tot > 0.f ? 1.f / l_bf_tot : 0.f;
+  if (it.slot >= 0) {
+    // One key chunk of a split tile: its normalised output and two log-sum-exps, over the
+    // bf16-rounded weights (the merge weights, so the merged output is normalised by the
+    // whole bf16 sum as an unsplit tile is) and over the fp32 weights (the lse).
+    const int64_t prow = ((int64_t)it.slot * hkv + kvh) * kPrefillTileRows + (r - it.row_begin);
+    float* po = a.part_o + prow * DVO;
+#pragma unroll
+    for (int t = 0; t < OT; ++t) *(f32x4_t*)(po + 16 * t + 4 * g4) = o[t] * inv;
+    if (g4 == 0) {
+      a.part_lse[2 * prow] = l_bf_tot > 0.f ? m_ref + log2f(l_bf_tot) : -INFINITY;
+      a.part_lse[2 * prow + 1] = l_tot > 0.f ? m_ref + log2f(l_tot) : -INFINITY;
+    }
+    return;
+  }
   const int64_t out_row = q_row * DVO;
 #pragma unroll
   for (int t = 0; t < OT; ++t) {
@@ -582,6 +598,74 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   }
   if (a.lse && g4 == 0)
     a.lse[q_row] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+struct PrefillMergeArgs {
+  const PrefillMerge* merges;
+  const float* part_o;
+  const float* part_lse;
+  void* out;
+  float* lse;
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t out_fp32;
+};
+
+// Split tiles: one wave per (tile, KV head, row); workgroups of 4 waves take 4 consecutive
+// rows (grid: merges x KV heads x tile_rows / 4).  The chunk outputs are weighted by
+// exp2(lse_bf(c) - max) / sum (chunks with no visible key have lse -inf and weight 0); the
+// lse is the log-sum-exp of the fp32 ones.  A row with no visible key at all gets a zero
+// output and lse -inf.  Lane l owns dims DVO/64 * l .. +DVO/64.
+template <int DVO>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeArgs a) {
+  constexpr int E = DVO / 64;
+  const PrefillMerge m = a.merges[blockIdx.x];
+  const int kvh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int rr = 4 * blockIdx.z + (threadIdx.x >> 6);
+  if (rr >= m.row_end - m.row_begin) return;
+  const int r = m.row_begin + rr;
+  const int tok = r / a.group, head = kvh * a.group + r % a.group;
+  const int64_t q_row = (int64_t)(m.q_begin + tok) * a.num_qo_heads + head;
+  const int64_t row0 = ((int64_t)m.slot_begin * a.num_kv_heads + kvh) * kPrefillTileRows + rr;
+  const int64_t step = (int64_t)a.num_kv_heads * kPrefillTileRows;  // rows between slots
+  float mw = -INFINITY, mo = -INFINITY;
+  for (int c = 0; c < m.num_slots; ++c) {
+    const f32x2_t l = *(const f32x2_t*)(a.part_lse + 2 * (row0 + c * step));
+    mw = fmaxf(mw, l[0]);
+    mo = fmaxf(mo, l[1]);
+  }
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float sw = 0.f, so = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < m.num_slots; ++c) {
+    const int64_t pr = row0 + c * step;
+    const f32x2_t l = *(const f32x2_t*)(a.part_lse + 2 * pr);
+    const float w = l[0] == -INFINITY ? 0.f : exp2f(l[0] - mw);
+    so += l[1] == -INFINITY ? 0.f : exp2f(l[1] - mo);
+    sw += w;
+    const float* src = a.part_o + pr * DVO + E * lane;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const f32x4_t v = *(const f32x4_t*)(src + e);
+      acc[e] = fmaf(w, v[0], acc[e]);
+      acc[e + 1] = fmaf(w, v[1], acc[e + 1]);
+      acc[e + 2] = fmaf(w, v[2], acc[e + 2]);
+      acc[e + 3] = fmaf(w, v[3], acc[e + 3]);
+    }
+  }
+  const float inv = sw > 0.f ? 1.f / sw : 0.f;
+  const int64_t off = q_row * DVO + E * lane;
+#pragma unroll
+  for (int e = 0; e < E; e += 4) {
+    const f32x4_t v = {acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+    if (a.out_fp32) *(f32x4_t*)((float*)a.out + off + e) = v;
+    else *(u32x2_t*)((uint16_t*)a.out + off + e) = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+  }
+  if (a.lse && lane == 0) a.lse[q_row] = so > 0.f ? (mo + log2f(so)) * kLn2 : -INFINITY;
 }
 
 template <int DQK, int DVO>
@@ -610,7 +694,7 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)workspace) & 15)
     return fail(PA_ERR_UNSUPPORTED, "q, out and workspace must be 16-byte aligned");
   if ((uintptr_t)lse & 3) return fail(PA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  const char* ws = (const char*)workspace;
+  char* ws = (char*)workspace;
   PrefillArgs a;
   a.q = (const uint16_t*)q;
   a.k = (const char*)cache->k;
@@ -620,6 +704,8 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   a.kv_indptr = table->kv_indptr;
   a.kv_indices = table->kv_indices;
   a.items = (const PrefillItem*)(ws + plan->items_offset);
+  a.part_o = (float*)(ws + plan->partial_o_offset);
+  a.part_lse = (float*)(ws + plan->partial_lse_offset);
   a.out = out;
   a.lse = lse;
   a.num_qo_heads = params->num_qo_heads;
@@ -649,5 +735,23 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
   count_launches(1);
+  if (plan->num_merges > 0) {
+    PrefillMergeArgs m;
+    m.merges = (const PrefillMerge*)(ws + plan->merges_offset);
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.out = out;
+    m.lse = lse;
+    m.num_qo_heads = params->num_qo_heads;
+    m.num_kv_heads = cache->num_kv_heads;
+    m.group = a.group;
+    m.out_fp32 = a.out_fp32;
+    const dim3 mg(plan->num_merges, cache->num_kv_heads, kPrefillTileRows / 4);
+    if (dvo == 512) prefill_merge_kernel<512><<<mg, 256, 0, s>>>(m);
+    else prefill_merge_kernel<256><<<mg, 256, 0, s>>>(m);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill merge launch: %s", hipGetErrorString(e));
+    count_launches(1);
+  }
   return PA_OK;
 }

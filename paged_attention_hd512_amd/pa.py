@@ -393,5 +393,14 @@ def decode_merges(plan, plan_buf):
 
 
 def prefill_items(plan, plan_buf):
+    """Items of a prefill plan as a [num_items, 9] int32 array (b, row_begin, row_end,
+    kv_begin, kv_end, q_begin, kv_len, q_len, slot); slot -1 writes the output directly."""
     off = plan.items_offset
-    return plan_buf[off:off + 32 * plan.num_items].view(np.int32).reshape(-1, 8)
+    return plan_buf[off:off + 48 * plan.num_items].view(np.int32).reshape(-1, 12)[:, :9]
+
+
+def prefill_merges(plan, plan_buf):
+    """Merge entries of a prefill plan (split tiles) as a [num_merges, 6] int32 array
+    (b, row_begin, row_end, q_begin, slot_begin, num_slots)."""
+    off = plan.merges_offset
+    return plan_buf[off:off + 32 * plan.num_merges].view(np.int32).reshape(-1, 8)[:, :6]

@@ -256,8 +256,8 @@ def make_prefill_case(qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim_qk,
                        v_pool, cache, k_scale, v_scale, name)
 
 
-# The five workloads (sizes, head counts, page sizes, length mixes and dtypes) the
-# benchmark and the full-size parity tests run.  Seeds are 1000 + workload number.
+# The workloads (sizes, head counts, page sizes, length mixes and dtypes) the benchmark
+# and the full-size parity tests run.  Seeds are 1000 + workload number.
 WORKLOADS = {
     "tiny_decode": dict(kind="decode", kv_lens=[37, 64], num_qo_heads=8, num_kv_heads=1,
                         head_dim_qk=512, page_size=16, out_dtype="fp32", num_splits=1,
@@ -276,6 +276,11 @@ WORKLOADS = {
     "causal_prefill": dict(kind="prefill", batch=4, qo_len=4096, prefix=1024,
                            num_qo_heads=16, num_kv_heads=8, head_dim_qk=512, page_size=64,
                            variants=[512, 256], seed=1005),
+    # Short-query extend (a few new tokens over a long cached prefix): the split-K prefill
+    # geometry; HBM-bound.
+    "extend_prefill": dict(kind="prefill", batch=8, qo_len=16, prefix=16368,
+                           num_qo_heads=16, num_kv_heads=8, head_dim_qk=512, page_size=64,
+                           variants=[512], seed=1006),
 }
 
 

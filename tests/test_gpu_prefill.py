@@ -29,6 +29,12 @@ SWEEP = [
     ([150], [150], 16, 1, 256, 256, 16, True, 17, "bf16"),
     ([64, 0, 65], [64, 10, 200], 3, 1, 512, 512, 64, True, 0, "fp32"),
     ([300], [2000], 2, 2, 512, 512, 64, True, 0, "bf16"),
+    # short queries over long KV (split-K prefill: key chunks merged per tile)
+    ([3, 1, 16], [3000, 5000, 2100], 4, 2, 512, 512, 64, True, 0, "fp32"),
+    ([1, 40], [20000, 700], 8, 2, 512, 256, 16, False, 0, "bf16"),
+    ([8, 8], [9000, 9000], 4, 2, 512, 512, 32, True, 3000, "fp32"),
+    ([16] * 4, [6000] * 4, 16, 8, 512, 512, 64, True, 0, "bf16"),
+    ([5, 2], [2500, 4000], 6, 2, 256, 256, 3, True, 0, "fp32"),
 ]
 
 
@@ -40,8 +46,9 @@ def test_prefill_sweep(qo, kv, hq, hkv, dqk, dvo, page, causal, window, out):
     c = make_prefill_case(qo, kv, hq, hkv, dqk, page, head_dim_vo=dvo, causal=causal,
                           window=window, out_dtype=out, seed=sum(qo) + hq, device=dev())
     before = pa.pa_launch_count()
-    _, o, lse = gpu_prefill(c)
-    assert pa.pa_launch_count() == before + (1 if sum(qo) > 0 else 0)
+    runner, o, lse = gpu_prefill(c)
+    launches = (1 if sum(qo) > 0 else 0) + (1 if runner.plan.num_merges > 0 else 0)
+    assert pa.pa_launch_count() == before + launches
     ref, ref_lse = oracle_prefill(c)
     compare(name, out_to_np(o), ref, lse.cpu().numpy(), ref_lse, out_dtype=out)
 
@@ -101,6 +108,26 @@ def test_full_size_causal_prefill_on_sampled_rows(dvo):
     ref, ref_lse = oracle_prefill(c, tokens=toks)
     idx = torch.as_tensor(toks).to(o.device)
     compare(f"prefill vo={dvo} rows {len(toks)}", out_to_np(o.index_select(0, idx)), ref,
+            lse.index_select(0, idx).cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
+    assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.slow
+def test_full_size_extend_prefill_is_split_and_matches():
+    """The short-query extend workload (8 requests x 16 new tokens over 16368 cached keys,
+    16/8 heads, page 64) in its launch configuration: the plan cuts every tile into key
+    chunks, and every row of the first and last request matches the oracle."""
+    say("full-size extend prefill")
+    c = prefill_workload("extend_prefill", device=dev(), head_dim_vo=512)
+    runner, o, lse = gpu_prefill(c)
+    assert runner.plan.num_merges == c.batch and runner.plan.num_slots >= 2 * c.batch
+    toks = []
+    for b in (0, c.batch - 1):
+        toks += list(range(int(c.qo_indptr[b]), int(c.qo_indptr[b + 1])))
+    toks = np.array(toks)
+    ref, ref_lse = oracle_prefill(c, tokens=toks)
+    idx = torch.as_tensor(toks).to(o.device)
+    compare(f"extend prefill rows {len(toks)}", out_to_np(o.index_select(0, idx)), ref,
             lse.index_select(0, idx).cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
     assert torch.isfinite(o.float()).all()
 

@@ -12,7 +12,7 @@ import subprocess
 import numpy as np
 import pytest
 
-from oracle.partition import decode_partition_ref, prefill_tiles_ref
+from oracle.partition import decode_partition_ref, prefill_plan_ref
 import paged_attention_hd512_amd.pa as pa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -157,6 +157,11 @@ PREFILL_CASES = [
     ([33, 7], [40, 7], 6, True, 5),
     ([17], [17], 1, False, 0),
     ([200, 64], [1000, 64], 8, True, 100),
+    # short queries over long KV: tiles are split into key chunks
+    ([3, 1, 16], [3000, 5000, 2100], 2, True, 0),
+    ([16] * 8, [16384] * 8, 2, True, 0),
+    ([1, 40], [20000, 700], 4, False, 0),
+    ([8, 8], [9000, 9000], 2, True, 3000),
 ]
 
 
@@ -171,12 +176,42 @@ def test_prefill_plan_matches_reference_tiles(qo, kv, group, causal, window):
     plan, buf = pa.pa_prefill_plan(params(hq=hkv * group, window=window, causal=int(causal)),
                                    cache, qo_indptr, indptr, last)
     items = pa.prefill_items(plan, buf)
-    ref = prefill_tiles_ref(qo, kv, group, plan.tile_rows, causal, window)
-    assert [tuple(r[:5]) for r in items.tolist()] == [tuple(r) for r in ref]
+    merges = pa.prefill_merges(plan, buf)
+    ref_items, ref_merges = prefill_plan_ref(qo, kv, group, plan.tile_rows, causal, window, hkv)
+    assert [tuple(r[:5]) + (r[8],) for r in items.tolist()] == [tuple(r) for r in ref_items]
+    assert [tuple(r) for r in merges.tolist()] == [tuple(r) for r in ref_merges]
     for r in items:
         b = r[0]
         assert (r[5], r[6], r[7]) == (qo_indptr[b], kv[b], qo[b])
     assert plan.total_q == sum(qo)
+    assert plan.num_merges == len(ref_merges)
+    assert plan.num_slots == sum(m[5] for m in ref_merges)
+    part_rows = plan.num_slots * hkv * plan.tile_rows
+    assert plan.partial_lse_offset - plan.partial_o_offset >= part_rows * 512 * 4
+    assert plan.workspace_bytes >= plan.partial_lse_offset + part_rows * 8
+
+
+@pytest.mark.parametrize("qo,kv,group,causal,window", PREFILL_CASES)
+def test_prefill_reference_chunks_cover_each_tile_exactly(qo, kv, group, causal, window):
+    """A split tile's chunks are contiguous, cover its key range exactly, start on 32-key
+    stages (but the first) and take consecutive slots; whole tiles keep slot -1."""
+    hkv = 2
+    items, merges = prefill_plan_ref(qo, kv, group, 128, causal, window, hkv)
+    by_tile = {}
+    for b, r0, r1, kb, ke, slot in items:
+        by_tile.setdefault((b, r0, r1), []).append((kb, ke, slot))
+    split = {(b, r0, r1): (s0, c) for b, r0, r1, _, s0, c in merges}
+    for key, chunks in by_tile.items():
+        chunks.sort()
+        if key not in split:
+            assert len(chunks) == 1 and chunks[0][2] == -1
+            continue
+        s0, c = split[key]
+        assert len(chunks) == c and [s for *_, s in chunks] == list(range(s0, s0 + c))
+        for (a0, a1, _), (b0, b1, _) in zip(chunks, chunks[1:]):
+            assert a1 == b0 and b0 % 32 == 0 and a1 > a0
+    if len(by_tile) * hkv >= 512:
+        assert merges == []
 
 
 # ----------------------------------------------------------------------------- error paths
