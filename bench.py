@@ -131,6 +131,38 @@ def time_decode(case, steps, warmup):
     return max(step, 1e-9), part, merge, wall, run.plan
 
 
+def time_decode_graph(case, steps, warmup):
+    """The same decode step captured once in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed: ms per replayed step, from HIP events around `steps` back-to-back replays."""
+    import torch
+    from paged_attention_hd512_amd import PagedDecode
+
+    run = PagedDecode(case.k_pool, case.v_pool, case.kv_indptr, case.kv_indices,
+                      case.kv_last_page_len, case.num_qo_heads, kv_dtype=case.kv_dtype,
+                      k_scale=case.k_scale, v_scale=case.v_scale, sm_scale=case.sm_scale,
+                      window=case.window, num_splits=case.num_splits, out_dtype=case.out_dtype)
+    out, lse = run.run(case.q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run.run(case.q, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.run(case.q, out=out, lse=lse)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def time_prefill(case, steps, warmup):
     import torch
     from paged_attention_hd512_amd import PagedPrefill
@@ -424,6 +456,8 @@ def main():
     }
     if "merge_ms" in main_res:
         line["merge_ms"] = round(main_res["merge_ms"], 5)
+        # The same step replayed from a captured HIP graph (no per-call host work).
+        line["graph_ms_per_step"] = round(time_decode_graph(case, args.steps, args.warmup), 5)
     if "plan" in main_res:
         line["plan"] = main_res["plan"]
     if not args.no_cpu_baseline:
