@@ -21,7 +21,8 @@ Every function below is pinned by the CPU tests against something other than its
 Nothing here is "parity unpinned".
 """
 
-from .numerics import bf16_bits_to_f64, e4m3fn_value, E4M3FN_VALUES, kv_values
+from .numerics import (bf16_bits_to_f64, e4m3fn_value, E4M3FN_VALUES, e2m1_value, E2M1_VALUES,
+                       nvfp4_values, kv_values)
 from .attention import (
     request_kv_len,
     gather_request_kv,
@@ -38,6 +39,9 @@ __all__ = [
     "bf16_bits_to_f64",
     "e4m3fn_value",
     "E4M3FN_VALUES",
+    "e2m1_value",
+    "E2M1_VALUES",
+    "nvfp4_values",
     "kv_values",
     "request_kv_len",
     "gather_request_kv",

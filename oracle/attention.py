@@ -26,6 +26,9 @@ The definition, with the page citations for each step:
    ``pos_i = L_b - q_len + i`` and sees keys ``t <= pos_i``.  A sliding window W
    ([Triton-hd512], sections "Approach" and "Test Coverage") keeps the W most recent keys,
    the query's own position included: ``t > pos - W``.
+   NVFP4 caches ([VO-split], sections "Summary" and "NVFP4 split-KV correctness (added)")
+   carry a block-scale tensor per pool, addressed like the data (same page, head and slot),
+   so the oracle gathers both and dequantises (numerics.nvfp4_values).
 5. Softmax attention with the natural-log log-sum-exp ([VO-split], release notes: "lse
    values"): ``s_t = scale * q . k_t``; ``o = sum_t exp(s_t - m) v_t / Z``;
    ``lse = m + ln Z``.  An empty visible set gives o = 0 and lse = -inf.
@@ -108,19 +111,30 @@ def softmax_attention(q, k, v, mask, sm_scale):
 
 
 def _request_kv_f64(k_pool, v_pool, kv_dtype, k_scale, v_scale, kv_indptr, kv_indices,
-                    kv_last_page_len, page_size, b):
-    k_raw = gather_request_kv(k_pool, kv_indptr, kv_indices, kv_last_page_len, page_size, b)
-    v_raw = gather_request_kv(v_pool, kv_indptr, kv_indices, kv_last_page_len, page_size, b)
-    return kv_values(k_raw, kv_dtype, k_scale), kv_values(v_raw, kv_dtype, v_scale)
+                    kv_last_page_len, page_size, b, k_sf=None, v_sf=None):
+    """Dequantised K and V of request b, ``[L_b, H, D]`` each.  NVFP4 block scales are
+    gathered through the same page table as the data they scale."""
+    def gather(pool):
+        return gather_request_kv(pool, kv_indptr, kv_indices, kv_last_page_len, page_size, b)
+    k_bs = None if k_sf is None else gather(k_sf)
+    v_bs = None if v_sf is None else gather(v_sf)
+    return (kv_values(gather(k_pool), kv_dtype, k_scale, k_bs),
+            kv_values(gather(v_pool), kv_dtype, v_scale, v_bs))
+
+
+def _value_width(pool, kv_dtype):
+    """head_dim of a pool: NVFP4 stores two elements per byte."""
+    return pool.shape[3] * (2 if kv_dtype == "nvfp4" else 1)
 
 
 def decode_ref(q, k_pool, v_pool, kv_indptr, kv_indices, kv_last_page_len, page_size,
                sm_scale, window=0, kv_dtype="bf16", k_scale=1.0, v_scale=1.0,
-               requests=None):
+               requests=None, k_sf=None, v_sf=None):
     """Single-token paged decode.
 
     q: float64 ``[B, Hq, Dqk]`` (one query token per request, at position L_b - 1).
-    k_pool / v_pool: stored elements ``[num_pages, Hkv, P, Dqk]`` / ``[..., Dvo]``.
+    k_pool / v_pool: stored elements ``[num_pages, Hkv, P, Dqk]`` / ``[..., Dvo]`` (NVFP4:
+    packed bytes ``[..., D/2]`` with block scales k_sf / v_sf ``[..., D/16]``).
     Returns (o ``[B, Hq, Dvo]``, lse ``[B, Hq]``), or only the rows of ``requests``.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -129,14 +143,14 @@ def decode_ref(q, k_pool, v_pool, kv_indptr, kv_indices, kv_last_page_len, page_
     if hq % hkv:
         raise ValueError("num_qo_heads must be a multiple of num_kv_heads")
     group = hq // hkv
-    dvo = v_pool.shape[3]
+    dvo = _value_width(v_pool, kv_dtype)
     lens = request_kv_len(kv_indptr, kv_last_page_len, page_size)
     reqs = list(range(batch)) if requests is None else list(requests)
     o = np.zeros((len(reqs), hq, dvo), dtype=np.float64)
     lse = np.full((len(reqs), hq), -np.inf, dtype=np.float64)
     for r, b in enumerate(reqs):
         k, v = _request_kv_f64(k_pool, v_pool, kv_dtype, k_scale, v_scale, kv_indptr,
-                               kv_indices, kv_last_page_len, page_size, b)
+                               kv_indices, kv_last_page_len, page_size, b, k_sf, v_sf)
         length = int(lens[b])
         mask = visible_mask([length - 1], length, True, window)
         for h in range(hq):
@@ -149,7 +163,7 @@ def decode_ref(q, k_pool, v_pool, kv_indptr, kv_indices, kv_last_page_len, page_
 
 def prefill_ref(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_last_page_len,
                 page_size, sm_scale, causal=True, window=0, kv_dtype="bf16", k_scale=1.0,
-                v_scale=1.0, tokens=None):
+                v_scale=1.0, tokens=None, k_sf=None, v_sf=None):
     """Paged prefill of the new tokens of every request.
 
     q: float64 ``[Nq, Hq, Dqk]``, ragged by ``qo_indptr``.  The q_len_b new tokens of
@@ -164,7 +178,7 @@ def prefill_ref(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_last_pag
     if hq % hkv:
         raise ValueError("num_qo_heads must be a multiple of num_kv_heads")
     group = hq // hkv
-    dvo = v_pool.shape[3]
+    dvo = _value_width(v_pool, kv_dtype)
     lens = request_kv_len(kv_indptr, kv_last_page_len, page_size)
     sel = np.arange(n_q) if tokens is None else np.asarray(tokens, dtype=np.int64)
     o = np.zeros((len(sel), hq, dvo), dtype=np.float64)
@@ -179,7 +193,7 @@ def prefill_ref(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_last_pag
         if q_len > length:
             raise ValueError("a request has more new tokens than KV tokens")
         k, v = _request_kv_f64(k_pool, v_pool, kv_dtype, k_scale, v_scale, kv_indptr,
-                               kv_indices, kv_last_page_len, page_size, b)
+                               kv_indices, kv_last_page_len, page_size, b, k_sf, v_sf)
         pos = length - q_len + (sel[rows] - q0)
         mask = visible_mask(pos, length, causal, window)
         for h in range(hq):

@@ -5,12 +5,18 @@ generator seeded with ``seed``; Q, K and V values come from a torch generator se
 ``seed + 1`` on the target device (CPU for the small cases, the GPU for the large ones),
 drawn as float32 N(0, 1) and rounded to bf16 (round-to-nearest-even).  FP8 K and V are
 N(0, 1) divided by a per-tensor scale amax/448 of the drawn data, clamped to +-448 and
-rounded to E4M3FN; the scale is returned with the case.
+rounded to E4M3FN; the scale (rounded to fp32, the type the library takes) is returned
+with the case.  NVFP4 K and V are N(0, 1) quantised
+the usual two-level way: a per-tensor fp32 scale g = amax / (6 * 448), then per 16
+consecutive head_dim elements of one token a block scale amax_block / (6 g) rounded to
+E4M3FN, then each element x / (block scale * g) rounded to the nearest E2M1 value and
+packed two per byte (element 2i in the low nibble).  The block scales sit in a separate
+uint8 tensor shaped like the data with head_dim / 16 per row.
 
 The pool holds the pages the requests need plus slack; pages are handed out in a random
 order.  Every element no query can see -- slots past a request's last-page length, pages
 no request uses, and keys before a sliding window -- holds a finite poison value (bf16
-+-30000, FP8 code 0x7E) so that a kernel reading them produces a visibly wrong result.
++-30000, FP8 code 0x7E, NVFP4 byte 0x77 with block scale 0x7E) so that a kernel reading them produces a visibly wrong result.
 
 The cache is the combined HND layout ``[num_pages, 2, num_kv_heads, page_size, head_dim]``
 (K at index 0, V at 1) when K and V have the same width, or two pools
@@ -30,6 +36,11 @@ BF16_POISON_K = 30000.0
 BF16_POISON_V = -30000.0
 FP8_POISON_CODE = 0x7E
 FP8_MAX = 448.0
+FP4_POISON_BYTE = 0x77
+FP4_MAX = 6.0
+# E2M1 magnitudes of codes 0..7 and the midpoints between neighbours (for rounding).
+_E2M1_MAGS = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+_E2M1_MIDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
 
 
 @dataclass
@@ -40,7 +51,7 @@ class DecodeCase:
     head_dim_qk: int
     head_dim_vo: int
     page_size: int
-    kv_dtype: str  # "bf16" | "fp8"
+    kv_dtype: str  # "bf16" | "fp8" | "nvfp4"
     window: int
     num_splits: int
     out_dtype: str  # "fp32" | "bf16"
@@ -58,6 +69,9 @@ class DecodeCase:
     v_scale: float = 1.0
     name: str = ""
     meta: dict = field(default_factory=dict)
+    k_sf: Optional[torch.Tensor] = None  # NVFP4 block scales [NP, Hkv, P, Dqk/16] view
+    v_sf: Optional[torch.Tensor] = None
+    sf_cache: Optional[torch.Tensor] = None  # combined [NP, 2, Hkv, P, D/16]
 
 
 @dataclass
@@ -88,6 +102,9 @@ class PrefillCase:
     v_scale: float = 1.0
     name: str = ""
     meta: dict = field(default_factory=dict)
+    k_sf: Optional[torch.Tensor] = None  # NVFP4 block scales [NP, Hkv, P, Dqk/16] view
+    v_sf: Optional[torch.Tensor] = None
+    sf_cache: Optional[torch.Tensor] = None  # combined [NP, 2, Hkv, P, D/16]
 
 
 def _page_table(rng, kv_lens, page_size, slack_pages):
@@ -145,7 +162,7 @@ def _fp8_pool(shape, gen, device, chunk_elems=1 << 28):
         x = _randn((e - s,) + tuple(shape[1:]), gen, device)
         amax = max(amax, float(x.abs().max()))
         slabs.append((s, e, state))
-    scale = amax / FP8_MAX
+    scale = float(np.float32(amax / FP8_MAX))  # the C ABI takes fp32 scales
     for s, e, state in slabs:
         gen.set_state(state)
         x = _randn((e - s,) + tuple(shape[1:]), gen, device)
@@ -154,19 +171,75 @@ def _fp8_pool(shape, gen, device, chunk_elems=1 << 28):
     return codes, scale
 
 
-def _poison(pool_k, pool_v, valid, kv_dtype):
+def _nvfp4_encode(x, g):
+    """x float32 [..., D], tensor scale g -> (packed uint8 [..., D/2], block scales [..., D/16])."""
+    blocks = x.reshape(x.shape[:-1] + (x.shape[-1] // 16, 16))
+    bs = (blocks.abs().amax(dim=-1) / (FP4_MAX * g)).clamp(max=FP8_MAX)
+    bs_codes = bs.to(torch.float8_e4m3fn)
+    bs_val = bs_codes.to(torch.float32)
+    y = blocks / (torch.where(bs_val > 0, bs_val, torch.ones_like(bs_val)) * g)[..., None]
+    y = y.clamp(-FP4_MAX, FP4_MAX).reshape(x.shape)
+    mids = torch.tensor(_E2M1_MIDS, dtype=torch.float32, device=x.device)
+    mag = torch.bucketize(y.abs(), mids).to(torch.uint8)
+    codes = mag | ((y < 0) & (mag > 0)).to(torch.uint8) << 3
+    packed = codes[..., 0::2] | (codes[..., 1::2] << 4)
+    return packed, bs_codes.view(torch.uint8)
+
+
+def _nvfp4_pool(shape, gen, device, chunk_elems=1 << 26):
+    """N(0,1) quantised to NVFP4; returns (packed [..., D/2], block scales [..., D/16], g)."""
+    d = shape[-1]
+    packed = torch.empty(tuple(shape[:-1]) + (d // 2,), dtype=torch.uint8, device=device)
+    scales = torch.empty(tuple(shape[:-1]) + (d // 16,), dtype=torch.uint8, device=device)
+    per = max(1, chunk_elems // max(1, math.prod(shape[1:])))
+    slabs = []
+    amax = 0.0
+    for s in range(0, shape[0], per):
+        e = min(shape[0], s + per)
+        state = gen.get_state()
+        x = _randn((e - s,) + tuple(shape[1:]), gen, device)
+        amax = max(amax, float(x.abs().max()))
+        slabs.append((s, e, state))
+    g = float(np.float32(amax / (FP4_MAX * FP8_MAX)))  # the C ABI takes fp32 scales
+    for s, e, state in slabs:
+        gen.set_state(state)
+        x = _randn((e - s,) + tuple(shape[1:]), gen, device)
+        packed[s:e], scales[s:e] = _nvfp4_encode(x, g)
+    return packed, scales, g
+
+
+def _poison(pool_k, pool_v, valid, kv_dtype, k_sf=None, v_sf=None):
     dev = pool_k.device
     invalid = torch.from_numpy(~valid).to(dev)[:, None, :, None]  # [NP, 1, P, 1]
     if kv_dtype == "bf16":
         pool_k.masked_fill_(invalid, BF16_POISON_K)
         pool_v.masked_fill_(invalid, BF16_POISON_V)
-    else:
+    elif kv_dtype == "fp8":
         pool_k.masked_fill_(invalid, FP8_POISON_CODE)
         pool_v.masked_fill_(invalid, FP8_POISON_CODE)
+    else:
+        pool_k.masked_fill_(invalid, FP4_POISON_BYTE)
+        pool_v.masked_fill_(invalid, FP4_POISON_BYTE)
+        k_sf.masked_fill_(invalid, FP8_POISON_CODE)
+        v_sf.masked_fill_(invalid, FP8_POISON_CODE)
 
 
 def _kv_pools(num_pages, hkv, page_size, dqk, dvo, kv_dtype, gen, device):
-    """Returns (cache or None, k_pool, v_pool, k_scale, v_scale)."""
+    """Returns (cache or None, k_pool, v_pool, k_scale, v_scale, block-scale dict)."""
+    if kv_dtype == "nvfp4":
+        k, k_sf, k_scale = _nvfp4_pool((num_pages, hkv, page_size, dqk), gen, device)
+        v, v_sf, v_scale = _nvfp4_pool((num_pages, hkv, page_size, dvo), gen, device)
+        if dqk != dvo:
+            return None, k, v, k_scale, v_scale, dict(k_sf=k_sf, v_sf=v_sf)
+        cache = torch.stack([k, v], dim=1)
+        sf_cache = torch.stack([k_sf, v_sf], dim=1)
+        del k, v, k_sf, v_sf
+        return (cache, cache[:, 0], cache[:, 1], k_scale, v_scale,
+                dict(k_sf=sf_cache[:, 0], v_sf=sf_cache[:, 1], sf_cache=sf_cache))
+    return _kv_pools_8_16(num_pages, hkv, page_size, dqk, dvo, kv_dtype, gen, device) + ({},)
+
+
+def _kv_pools_8_16(num_pages, hkv, page_size, dqk, dvo, kv_dtype, gen, device):
     if dqk == dvo:
         shape = (num_pages, 2, hkv, page_size, dqk)
         if kv_dtype == "bf16":
@@ -204,20 +277,20 @@ def make_decode_case(kv_lens, num_qo_heads, num_kv_heads, head_dim_qk, page_size
     gen.manual_seed(seed + 1)
     batch = len(kv_lens)
     q = _randn((batch, num_qo_heads, head_dim_qk), gen, device).to(torch.bfloat16)
-    cache, k_pool, v_pool, k_scale, v_scale = _kv_pools(
+    cache, k_pool, v_pool, k_scale, v_scale, sf = _kv_pools(
         num_pages, num_kv_heads, page_size, head_dim_qk, head_dim_vo, kv_dtype, gen, device)
     if window > 0 and poison_window:
         first = np.maximum(0, kv_lens - window)
     else:
         first = np.zeros_like(kv_lens)
     valid = _visible_slots(kv_lens, indptr, indices, page_size, num_pages, first)
-    _poison(k_pool, v_pool, valid, kv_dtype)
+    _poison(k_pool, v_pool, valid, kv_dtype, sf.get("k_sf"), sf.get("v_sf"))
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(head_dim_qk)
     return DecodeCase(batch, num_qo_heads, num_kv_heads, head_dim_qk, head_dim_vo, page_size,
                       kv_dtype, window, num_splits, out_dtype, sm_scale, kv_lens, indptr,
                       indices, last, num_pages, q, k_pool, v_pool, cache, k_scale, v_scale,
-                      name)
+                      name, **sf)
 
 
 def make_prefill_case(qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim_qk, page_size,
@@ -240,20 +313,20 @@ def make_prefill_case(qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim_qk,
     gen.manual_seed(seed + 1)
     n_q = int(qo_indptr[-1])
     q = _randn((n_q, num_qo_heads, head_dim_qk), gen, device).to(torch.bfloat16)
-    cache, k_pool, v_pool, k_scale, v_scale = _kv_pools(
+    cache, k_pool, v_pool, k_scale, v_scale, sf = _kv_pools(
         num_pages, num_kv_heads, page_size, head_dim_qk, head_dim_vo, kv_dtype, gen, device)
     if window > 0:
         first = np.maximum(0, kv_lens - qo_lens - window + 1)
     else:
         first = np.zeros_like(kv_lens)
     valid = _visible_slots(kv_lens, indptr, indices, page_size, num_pages, first)
-    _poison(k_pool, v_pool, valid, kv_dtype)
+    _poison(k_pool, v_pool, valid, kv_dtype, sf.get("k_sf"), sf.get("v_sf"))
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(head_dim_qk)
     return PrefillCase(len(qo_lens), num_qo_heads, num_kv_heads, head_dim_qk, head_dim_vo,
                        page_size, kv_dtype, window, causal, out_dtype, sm_scale, qo_lens,
                        qo_indptr, kv_lens, indptr, indices, last, num_pages, q, k_pool,
-                       v_pool, cache, k_scale, v_scale, name)
+                       v_pool, cache, k_scale, v_scale, name, **sf)
 
 
 # The workloads (sizes, head counts, page sizes, length mixes and dtypes) the benchmark
@@ -270,6 +343,10 @@ WORKLOADS = {
     "fp8_decode": dict(kind="decode", batch=64, len_range=(4096, 32768), num_qo_heads=12,
                        num_kv_heads=4, head_dim_qk=512, page_size=64, kv_dtype="fp8",
                        num_splits=0, seed=1003),
+    # NVFP4 KV at the FP8 workload's geometry: 4-bit codes plus one E4M3 scale per 16.
+    "nvfp4_decode": dict(kind="decode", batch=64, len_range=(4096, 32768), num_qo_heads=12,
+                         num_kv_heads=4, head_dim_qk=512, page_size=64, kv_dtype="nvfp4",
+                         num_splits=0, seed=1007),
     "window_decode": dict(kind="decode", batch=48, len_range=(512, 16384), num_qo_heads=16,
                           num_kv_heads=8, window=1024, num_splits=0, seed=1004,
                           variants=[(512, 1), (512, 32), (256, 1), (256, 32)]),
@@ -339,6 +416,9 @@ def extract_requests(case, requests, device="cpu"):
     out = dict(kv_lens=np.asarray(lens, np.int64), kv_indptr=indptr,
                kv_indices=np.arange(len(pages), dtype=np.int32),
                kv_last_page_len=np.asarray(lasts, np.int32), k_pool=k_pool, v_pool=v_pool)
+    if case.k_sf is not None:
+        out["k_sf"] = case.k_sf.index_select(0, sel).to(device)
+        out["v_sf"] = case.v_sf.index_select(0, sel).to(device)
     if isinstance(case, DecodeCase):
         out["q"] = case.q[requests].to(device)
     else:

@@ -437,3 +437,138 @@ def test_planted_kv_head_mapping_is_caught():
     o2, _ = decode_ref(q, kp_wrong, vp_wrong, c.kv_indptr, c.kv_indices, c.kv_last_page_len,
                        c.page_size, c.sm_scale)
     assert not np.allclose(o, o2, atol=1e-3)
+
+
+# --------------------------------------------------------------------------- NVFP4 KV
+
+def test_e2m1_codes_follow_the_format_structure():
+    """The 16 E2M1 codes, pinned by the structure of a sign-magnitude float with 2 exponent
+    bits and 1 mantissa bit rather than by the closed form: codes 8..15 negate 0..7 (with
+    -0), magnitudes rise strictly, the subnormal step is half the smallest normal, and each
+    binade doubles the one below (code c + 2 is twice code c for normal codes)."""
+    v = oracle.E2M1_VALUES
+    assert v.shape == (16,)
+    assert np.array_equal(v[8:], -v[:8]) and math.copysign(1.0, v[8]) == -1.0
+    assert np.all(np.diff(v[:8]) > 0) and v[0] == 0.0
+    assert v[2] == 1.0 and v[1] == v[2] / 2  # smallest normal 2^0; subnormal step 1/2
+    for c in range(2, 6):
+        assert v[c + 2] == 2 * v[c]
+    assert v[7] == 6.0 and v[3] == 1.5  # largest finite magnitude; mantissa bit = +1/2
+
+
+def test_nvfp4_hand_derived_rows():
+    """Hand-derived values: byte 0x21 holds elements (code 1, code 2) = (0.5, 1.0), byte 0xF7
+    holds (code 7, code 15) = (6.0, -6.0); block scale code 0x40 is E4M3FN 2.0, 0x38 is 1.0."""
+    packed = np.array([[0x21, 0xF7] + [0x00] * 6, [0x00] * 7 + [0x9B]], dtype=np.uint8)
+    scales = np.array([[0x40], [0x38]], dtype=np.uint8)
+    got = oracle.nvfp4_values(packed, scales, 0.25)
+    want = np.zeros((2, 16))
+    want[0, :4] = np.array([0.5, 1.0, 6.0, -6.0]) * 2.0 * 0.25
+    # 0x9B: low nibble 0xB = 1|011 = -1.5, high nibble 0x9 = 1|001 = -0.5
+    want[1, 14:] = np.array([-1.5, -0.5]) * 1.0 * 0.25
+    assert np.array_equal(got, want)
+
+
+def test_nvfp4_block_scale_index_is_element_over_16():
+    packed = np.full((1, 32), 0x22, dtype=np.uint8)  # every element 1.0, 64 elements
+    scales = np.array([[0x38, 0x40, 0x48, 0x50]], dtype=np.uint8)  # 1, 2, 4, 8
+    got = oracle.nvfp4_values(packed, scales)
+    assert np.array_equal(got[0], np.repeat([1.0, 2.0, 4.0, 8.0], 16))
+    with pytest.raises(ValueError):
+        oracle.nvfp4_values(packed, scales[:, :3])
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_nvfp4_round_trip_within_the_quantisation_bound(seed):
+    """The input generator's quantiser (its own E2M1 table and packing) followed by the
+    oracle's dequantisation lands within the rounding bound: each element's error is at
+    most half of the E2M1 spacing at its magnitude (1 at the top, 4..6) times its block's
+    scale, plus the clamp at 6 when the block scale rounded down."""
+    from synth.workloads import _nvfp4_encode
+    gen = torch.Generator().manual_seed(seed)
+    x = torch.randn((64, 512), generator=gen)
+    g = float(x.abs().max()) / (6 * 448)
+    packed, bs = _nvfp4_encode(x, g)
+    deq = oracle.nvfp4_values(packed.numpy(), bs.numpy(), g)
+    xs = x.double().numpy()
+    step = np.repeat(oracle.E4M3FN_VALUES[bs.numpy()], 16, axis=-1) * g
+    assert np.all(np.abs(xs - deq) <= 1.0 * step * (1 + 2 ** -3) + 1e-12)
+    # Relative RMS error of E2M1 with per-16 scales is about 10 %; a swapped nibble order or
+    # a wrong block index gives errors of the order of the values themselves.
+    assert np.sqrt(np.mean((xs - deq) ** 2)) < 0.15 * np.sqrt(np.mean(xs ** 2))
+
+
+def nvfp4_small_decode(seed=7, lens=(37, 64, 1, 16), hq=8, hkv=2, dim=64, page=16, dvo=None):
+    from synth import make_decode_case
+    c = make_decode_case(lens, hq, hkv, dim, page, head_dim_vo=dvo, kv_dtype="nvfp4",
+                         seed=seed, out_dtype="fp32")
+    q = bf16_bits_to_f64(c.q.view(torch.int16).numpy().view(np.uint16))
+    arrs = [t.contiguous().numpy() for t in (c.k_pool, c.v_pool, c.k_sf, c.v_sf)]
+    return (c, q) + tuple(arrs)
+
+
+def test_nvfp4_decode_matches_brute_force_on_decoded_values():
+    c, q, kp, vp, ksf, vsf = nvfp4_small_decode(dim=32, lens=(19, 1, 40))
+    o, lse = decode_ref(q, kp, vp, c.kv_indptr, c.kv_indices, c.kv_last_page_len, c.page_size,
+                        c.sm_scale, kv_dtype="nvfp4", k_scale=c.k_scale, v_scale=c.v_scale,
+                        k_sf=ksf, v_sf=vsf)
+    for b in range(c.batch):
+        L = int(c.kv_lens[b])
+        pages = c.kv_indices[c.kv_indptr[b]:c.kv_indptr[b + 1]]
+        for h in range(c.num_qo_heads):
+            kvh = h // (c.num_qo_heads // c.num_kv_heads)
+            ks, vs = [], []
+            for t in range(L):  # token by token, element by element, from the bytes
+                pg, sl = int(pages[t // c.page_size]), t % c.page_size
+                def elem(pool, sfp, d, scale):
+                    byte = int(pool[pg, kvh, sl, d // 2])
+                    nib = byte & 15 if d % 2 == 0 else byte >> 4
+                    mag = [0, 0.5, 1, 1.5, 2, 3, 4, 6][nib & 7]
+                    return (-mag if nib & 8 else mag) * \
+                        oracle.E4M3FN_VALUES[sfp[pg, kvh, sl, d // 16]] * scale
+                ks.append([elem(kp, ksf, d, c.k_scale) for d in range(32)])
+                vs.append([elem(vp, vsf, d, c.v_scale) for d in range(32)])
+            ob, lb = brute_force_attention([q[b, h].tolist()], ks, vs, [[True] * L], c.sm_scale)
+            assert np.allclose(o[b, h], ob[0], rtol=0, atol=1e-12)
+            assert abs(lse[b, h] - lb[0]) < 1e-12
+
+
+def test_nvfp4_block_scales_follow_the_page_table():
+    """Permuting pages of data and block scales together is invisible (bit-exact); permuting
+    the data alone is not."""
+    c, q, kp, vp, ksf, vsf = nvfp4_small_decode()
+    kw = dict(kv_dtype="nvfp4", k_scale=c.k_scale, v_scale=c.v_scale)
+    o, lse = decode_ref(q, kp, vp, c.kv_indptr, c.kv_indices, c.kv_last_page_len, c.page_size,
+                        c.sm_scale, k_sf=ksf, v_sf=vsf, **kw)
+    perm = np.random.default_rng(3).permutation(c.num_pages)
+    moved = []
+    for a in (kp, vp, ksf, vsf):
+        a2 = np.empty_like(a)
+        a2[perm] = a
+        moved.append(a2)
+    idx2 = perm[c.kv_indices].astype(np.int32)
+    o2, lse2 = decode_ref(q, moved[0], moved[1], c.kv_indptr, idx2, c.kv_last_page_len,
+                          c.page_size, c.sm_scale, k_sf=moved[2], v_sf=moved[3], **kw)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    o3, _ = decode_ref(q, moved[0], moved[1], c.kv_indptr, idx2, c.kv_last_page_len,
+                       c.page_size, c.sm_scale, k_sf=ksf, v_sf=vsf, **kw)
+    assert not np.allclose(o, o3, atol=1e-3)
+
+
+def test_nvfp4_poison_never_reaches_the_output():
+    c, q, kp, vp, ksf, vsf = nvfp4_small_decode(lens=(37, 5, 64))
+    o, _ = decode_ref(q, kp, vp, c.kv_indptr, c.kv_indices, c.kv_last_page_len, c.page_size,
+                      c.sm_scale, kv_dtype="nvfp4", k_scale=c.k_scale, v_scale=c.v_scale,
+                      k_sf=ksf, v_sf=vsf)
+    vmax = np.abs(oracle.nvfp4_values(vp, vsf, c.v_scale))
+    poison = 6 * 448 * c.v_scale
+    assert np.abs(o).max() < 0.5 * poison and vmax.max() >= poison
+
+
+def test_planted_nibble_swap_is_caught():
+    """Reading element 2i from the high nibble breaks the hand-derived rows."""
+    packed = np.array([[0x21] + [0] * 7], dtype=np.uint8)
+    swapped = ((packed & 15) << 4) | (packed >> 4)
+    right = oracle.nvfp4_values(packed, np.array([[0x38]], np.uint8))
+    wrong = oracle.nvfp4_values(swapped, np.array([[0x38]], np.uint8))
+    assert right[0, 0] == 0.5 and wrong[0, 0] != 0.5
