@@ -15,6 +15,10 @@
  *    separately allocated K and V pools ("feat(attention): asymmetric VO-split NVFP4 paged
  *    prefill (qk=512/vo=256) for Gemma-4 on SM120/121", FlashInfer pull request 3684,
  *    sections "Summary" and "What's in it").
+ *  - NVFP4 KV (decode): packed E2M1 pairs with one FP8 block scale per 16 head_dim
+ *    elements of a token, the scales in a tensor of their own laid out like the data (the
+ *    FlashInfer page, sections "Summary", "What's in it" and "NVFP4 split-KV correctness
+ *    (added)"), dequantised on load.
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless the parameter name ends in _host.  The library
@@ -30,7 +34,8 @@
  *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.  Enqueuing
  *    calls do not synchronise.
  *  - Element strides are in elements of the stored type; the innermost (head_dim) stride
- *    is 1.  Base pointers and strides must keep every 16-byte vector load aligned.
+ *    is 1.  Base pointers and strides must keep every 16-byte vector load aligned.  NVFP4
+ *    data and block-scale strides are in bytes (one data byte holds two elements).
  */
 #ifndef PA_H_
 #define PA_H_
@@ -53,7 +58,10 @@ typedef enum {
 typedef enum {
   PA_DTYPE_BF16 = 0,
   PA_DTYPE_FP32 = 1,
-  PA_DTYPE_FP8_E4M3FN = 2          /* OCP E4M3FN: bias 7, max 448, NaN only at S.1111.111 */
+  PA_DTYPE_FP8_E4M3FN = 2,         /* OCP E4M3FN: bias 7, max 448, NaN only at S.1111.111 */
+  PA_DTYPE_NVFP4 = 3               /* KV only: two OCP E2M1 values per byte (element 2i in the
+                                      low nibble, 2i+1 in the high one) and one E4M3FN block
+                                      scale per 16 head_dim elements of a token            */
 } pa_dtype;
 
 /* One paged KV cache.  K and V may be two halves of the combined HND cache or two
@@ -62,11 +70,21 @@ typedef enum {
  * differ).  Element (page, head, slot, d) of K is at
  *   k + page*k_stride_page + head*k_stride_head + slot*k_stride_token + d
  * and likewise for V.  For FP8 the stored code c stands for e4m3fn(c) * k_scale (or
- * v_scale); bf16 caches use scales of 1. */
+ * v_scale); bf16 caches use scales of 1.
+ *
+ * NVFP4: byte (page, head, slot, i) of K is at k + page*k_stride_page + head*k_stride_head
+ * + slot*k_stride_token + i and holds elements 2i and 2i+1; the block scale of elements
+ * 16j..16j+15 is byte k_sf + page*k_sf_stride_page + head*k_sf_stride_head +
+ * slot*k_sf_stride_token + j, an E4M3FN code.  Element value = e2m1(nibble) *
+ * e4m3fn(block scale) * k_scale (k_scale is the tensor-wide second-level scale); likewise
+ * for V.  Data and scale tensors, and their strides, must be 16-byte aligned.  The block
+ * scales are read through the same page table as the data, so a split of the key axis
+ * never cuts a scale block (they run along head_dim).  Other dtypes leave the k_sf / v_sf
+ * fields zero. */
 typedef struct pa_kv_cache {
   const void* k;
   const void* v;
-  int32_t kv_dtype;                /* PA_DTYPE_BF16 or PA_DTYPE_FP8_E4M3FN */
+  int32_t kv_dtype;                /* PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3FN or PA_DTYPE_NVFP4 */
   int32_t num_pages;
   int32_t num_kv_heads;
   int32_t page_size;               /* tokens per page, >= 1 */
@@ -76,6 +94,10 @@ typedef struct pa_kv_cache {
   int64_t v_stride_page, v_stride_head, v_stride_token;
   float k_scale;
   float v_scale;
+  const void* k_sf;                /* NVFP4 block scales of K (uint8 E4M3FN), else NULL */
+  const void* v_sf;
+  int64_t k_sf_stride_page, k_sf_stride_head, k_sf_stride_token;  /* bytes */
+  int64_t v_sf_stride_page, v_sf_stride_head, v_sf_stride_token;
 } pa_kv_cache;
 
 /* Page table, as the FlashInfer decode plan slices it (Triton page, section "Approach"):
@@ -152,6 +174,22 @@ pa_status pa_kv_cache_separate(const void* k, const void* v, int32_t kv_dtype,
                                int32_t num_pages, int32_t num_kv_heads, int32_t page_size,
                                int32_t head_dim_qk, int32_t head_dim_vo, float k_scale,
                                float v_scale, pa_kv_cache* out);
+
+/* NVFP4 combined cache: data [num_pages, 2, num_kv_heads, page_size, head_dim / 2] at
+ * `data` and block scales [num_pages, 2, num_kv_heads, page_size, head_dim / 16] at `sf`
+ * (K = index 0 of the "2" axis, V = index 1), both contiguous uint8.  Pure host
+ * arithmetic; no pointer is dereferenced. */
+pa_status pa_kv_cache_nvfp4_hnd(const void* data, const void* sf, int32_t num_pages,
+                                int32_t num_kv_heads, int32_t page_size, int32_t head_dim,
+                                float k_scale, float v_scale, pa_kv_cache* out);
+
+/* NVFP4 separate pools: K data [num_pages, num_kv_heads, page_size, head_dim_qk / 2] and
+ * block scales [..., head_dim_qk / 16], likewise V with head_dim_vo, all contiguous. */
+pa_status pa_kv_cache_nvfp4_separate(const void* k, const void* v, const void* k_sf,
+                                     const void* v_sf, int32_t num_pages,
+                                     int32_t num_kv_heads, int32_t page_size,
+                                     int32_t head_dim_qk, int32_t head_dim_vo, float k_scale,
+                                     float v_scale, pa_kv_cache* out);
 
 /* Checks host copies of a page table: kv_indptr[0] == 0 and non-decreasing, every index
  * in [0, num_pages), every last page length in [1, page_size] for a non-empty request.

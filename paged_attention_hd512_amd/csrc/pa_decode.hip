@@ -29,6 +29,14 @@
 //   * Waves never synchronise with each other; each one's results are deterministic.
 // FP8 E4M3FN keys are widened to bf16 in registers (exact); k_scale is folded into the
 // score scale and v_scale into the output.
+// NVFP4 ("feat(attention): asymmetric VO-split NVFP4 paged prefill ...", FlashInfer pull
+// request 3684, sections "Summary" and "NVFP4 split-KV correctness (added)"): each lane
+// reads its keys' packed E2M1 bytes and their E4M3 block scales (one per 16 head_dim
+// elements, from a tensor of their own addressed through the same page table), converts
+// the nibbles to fp32 and multiplies by the block scale.  For keys the product goes to
+// bf16 exactly (an E2M1 value times an E4M3 value has at most 6 significant bits); for
+// values the block scale multiplies the probability instead, one product per head rather
+// than one per element.  The global k_scale / v_scale apply as for FP8.
 
 #include <hip/hip_runtime.h>
 
@@ -43,12 +51,19 @@ namespace pa {
 
 constexpr int kDecodeWavesPerGroup = 8;  // the two waves of every SIMD of a CU
 
+// Stored KV formats of the decode kernel.
+constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvFp4 = 2;
+
 struct DecodeArgs {
   const uint16_t* q;           // [B, Hq, DQK] bf16 bits
   const char* k;               // byte base of the K pool
   const char* v;               // byte base of the V pool
-  int64_t k_sp, k_sh, k_st;    // element strides
+  int64_t k_sp, k_sh, k_st;    // element strides (NVFP4: bytes)
   int64_t v_sp, v_sh, v_st;
+  const char* k_sf;            // NVFP4 block scales of K and V, else null
+  const char* v_sf;
+  int64_t ks_sp, ks_sh, ks_st; // block-scale strides, bytes
+  int64_t vs_sp, vs_sh, vs_st;
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
   const DecodeSegment* segs;
@@ -68,10 +83,13 @@ struct DecodeArgs {
 
 // head_dim offset of the 8 bf16 operand elements that lane group g4 holds at MFMA step j.
 // bf16 keys: one 16-byte load per step.  FP8 keys: one 16-byte load covers two steps.
-template <int KVB>
+// NVFP4 keys: lane group g4 holds the contiguous quarter [DQK/4 g4, DQK/4 (g4+1)) of the
+// row (so its block scales are contiguous too); a 16-byte load covers four steps.
+template <int KV, int DQK>
 __device__ __forceinline__ int q_dim_of_step(int j, int g4) {
-  if constexpr (KVB == 2) return 32 * j + 8 * g4;
-  else return 64 * (j >> 1) + 16 * g4 + 8 * (j & 1);
+  if constexpr (KV == kKvBf16) return 32 * j + 8 * g4;
+  else if constexpr (KV == kKvFp8) return 64 * (j >> 1) + 16 * g4 + 8 * (j & 1);
+  else return (DQK / 4) * g4 + 8 * j;
 }
 
 // Eight waves per workgroup, one workgroup per CU: each wave runs its own piece (its
@@ -80,16 +98,22 @@ __device__ __forceinline__ int q_dim_of_step(int j, int g4) {
 // priority, because the hardware otherwise favours the older of the two waves on a SIMD,
 // which then finishes far ahead of its partner and leaves the SIMD half-occupied for the
 // rest of the kernel.
-template <int DQK, int DVO, int KVB, int GMAX>
+template <int DQK, int DVO, int KV, int GMAX>
 __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_kernel(DecodeArgs a) {
+  constexpr int UNIT = KV == kKvBf16 ? 2 : 1;    // bytes per stride unit
+  constexpr int KROW = KV == kKvBf16 ? 2 * DQK : KV == kKvFp8 ? DQK : DQK / 2;  // K row bytes
+  constexpr int VB8 = KV == kKvBf16 ? 16 : KV == kKvFp8 ? 8 : 4;  // bytes of 8 V elements
   constexpr int NSTEP = DQK / 32;                 // MFMA steps over head_dim
-  constexpr int NKL = 16 * DQK * KVB / (64 * 16); // 16-byte K loads per lane per block
+  constexpr int NKL = 16 * KROW / (64 * 16);      // 16-byte K loads per lane per block
+  constexpr int NKSF = DQK / 64;                  // NVFP4: K block scales per lane (4 or 8)
   constexpr int LPR = DVO / 8;                    // lanes per V row (8 elements per lane)
   constexpr int RPI = 64 / LPR;                   // V rows per load instruction (1 or 2)
   constexpr int NVL = 16 / RPI;                   // V load instructions per block
   constexpr int QPITCH = DQK + 8;                 // LDS row pitch of Q (bf16), padded
   constexpr int QV = (GMAX * DQK / 8 + 63) / 64;  // 16-byte Q pieces per lane
-  using vload_t = typename std::conditional<KVB == 2, u32x4_t, u32x2_t>::type;
+  using vload_t = typename std::conditional<
+      KV == kKvBf16, u32x4_t, typename std::conditional<KV == kKvFp8, u32x2_t, uint32_t>::type>::type;
+  using ksf_t = typename std::conditional<NKSF == 8, u32x2_t, uint32_t>::type;
 
   constexpr int NWG = kDecodeWavesPerGroup;
   __shared__ __attribute__((aligned(16))) uint16_t q_all[NWG][GMAX * QPITCH];
@@ -114,6 +138,8 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
 
   u32x4_t kbuf[NKL];
   vload_t vbuf[NVL];
+  ksf_t ksf;            // NVFP4: this lane's K block scales of the block (E4M3 codes)
+  uint32_t vsf[NVL];    // NVFP4: the block scale of each V row's 8 elements of this lane
   float acc[GMAX][8];
 
   for (int sgi = seg_first; sgi < seg_last; ++sgi) {
@@ -122,6 +148,8 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
     const int32_t* __restrict__ pages = a.kv_indices + a.kv_indptr[sg.b];
     const int64_t k_head = (int64_t)sg.kvh * a.k_sh;
     const int64_t v_head = (int64_t)sg.kvh * a.v_sh;
+    const int64_t ks_head = (int64_t)sg.kvh * a.ks_sh;
+    const int64_t vs_head = (int64_t)sg.kvh * a.vs_sh;
 
     // Page and slot of key n of a block, clamped into the segment: every load is of a key
     // the segment owns, and clamped lanes are masked out of the softmax.  Block indices
@@ -132,9 +160,18 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
       token_page_slot(pages, t, a.page_size, page, slot);
     };
     auto issue_k = [&](int32_t page, int32_t slot) {
-      const char* base = a.k + (row_elem_offset(page, 0, slot, a.k_sp, 0, a.k_st) + k_head) * KVB + 16 * g4;
+      const char* row = a.k + (row_elem_offset(page, 0, slot, a.k_sp, 0, a.k_st) + k_head) * UNIT;
+      if constexpr (KV == kKvFp4) {
+        const char* base = row + (KROW / 4) * g4;
 #pragma unroll
-      for (int l = 0; l < NKL; ++l) kbuf[l] = __builtin_nontemporal_load((const u32x4_t*)(base + 64 * l));
+        for (int l = 0; l < NKL; ++l) kbuf[l] = __builtin_nontemporal_load((const u32x4_t*)(base + 16 * l));
+        const char* sf = a.k_sf + row_elem_offset(page, 0, slot, a.ks_sp, 0, a.ks_st) + ks_head + NKSF * g4;
+        ksf = __builtin_nontemporal_load((const ksf_t*)sf);
+      } else {
+        const char* base = row + 16 * g4;
+#pragma unroll
+        for (int l = 0; l < NKL; ++l) kbuf[l] = __builtin_nontemporal_load((const u32x4_t*)(base + 64 * l));
+      }
     };
     auto issue_v = [&](int32_t page, int32_t slot) {
 #pragma unroll
@@ -148,9 +185,14 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
           pv = shfl_i(page, src);
           sv = shfl_i(slot, src);
         }
-        const char* base = a.v + (row_elem_offset(pv, 0, sv, a.v_sp, 0, a.v_st) + v_head) * KVB +
-                           (lane % LPR) * 8 * KVB;
+        const char* base = a.v + (row_elem_offset(pv, 0, sv, a.v_sp, 0, a.v_st) + v_head) * UNIT +
+                           (lane % LPR) * VB8;
         vbuf[i] = __builtin_nontemporal_load((const vload_t*)base);
+        if constexpr (KV == kKvFp4) {
+          const char* sf = a.v_sf + row_elem_offset(pv, 0, sv, a.vs_sp, 0, a.vs_st) + vs_head +
+                           (lane % LPR) / 2;
+          vsf[i] = __builtin_nontemporal_load((const uint8_t*)sf);
+        }
       }
     };
     // P V of one block: rescale the accumulators by the block's alpha, then add p * V with
@@ -172,15 +214,20 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
 #pragma unroll
         for (int h = 0; h < GMAX; ++h) p[h] = p_lds[pb][tk][h];
         float vf[8];
-        if constexpr (KVB == 2) {
+        if constexpr (KV == kKvBf16) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             vf[2 * e] = bf16_lo(vbuf[i][e]);
             vf[2 * e + 1] = bf16_hi(vbuf[i][e]);
           }
-        } else {
+        } else if constexpr (KV == kKvFp8) {
           fp8x4_to_f32(vbuf[i][0], vf);
           fp8x4_to_f32(vbuf[i][1], vf + 4);
+        } else {
+          fp4x8_to_f32(vbuf[i], vf);
+          const float bs = fp8_to_f32<0>(vsf[i]);
+#pragma unroll
+          for (int h = 0; h < GMAX; ++h) p[h] *= bs;
         }
 #pragma unroll
         for (int h = 0; h < GMAX; ++h) {
@@ -239,11 +286,28 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
       issue_v(page_c, slot_c);
       // ---- S^T = K Q^T for the 16 keys of this block (keys on rows, heads on columns).
       f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+      float kbs[NKSF];  // NVFP4: the lane's K block scales as fp32
+      if constexpr (KV == kKvFp4) {
+        if constexpr (NKSF == 8) {
+          fp8x4_to_f32(ksf[0], kbs);
+          fp8x4_to_f32(ksf[1], kbs + 4);
+        } else {
+          fp8x4_to_f32(ksf, kbs);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NSTEP; ++j) {
         bf16x8_t kf;
-        if constexpr (KVB == 2) {
+        if constexpr (KV == kKvBf16) {
           kf = __builtin_bit_cast(bf16x8_t, kbuf[j]);
+        } else if constexpr (KV == kKvFp4) {
+          float e[8];
+          fp4x8_to_f32(kbuf[j >> 2][j & 3], e);
+          const float bs = kbs[j >> 1];
+          u32x4_t packed;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) packed[u] = pack_bf16(e[2 * u] * bs, e[2 * u + 1] * bs);
+          kf = __builtin_bit_cast(bf16x8_t, packed);
         } else {
           const u32x4_t raw = kbuf[j >> 1];
           const u32x2_t lo = fp8x4_to_bf16x4(raw[(j & 1) * 2 + 0]);
@@ -251,7 +315,7 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
           const u32x4_t packed = {lo[0], lo[1], hi[0], hi[1]};
           kf = __builtin_bit_cast(bf16x8_t, packed);
         }
-        const u32x4_t qv = *(const u32x4_t*)(q_lds + qrow * QPITCH + q_dim_of_step<KVB>(j, g4));
+        const u32x4_t qv = *(const u32x4_t*)(q_lds + qrow * QPITCH + q_dim_of_step<KV, DQK>(j, g4));
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, __builtin_bit_cast(bf16x8_t, qv), s, 0, 0, 0);
       }
       // ---- prefetch the next block's keys.
@@ -430,29 +494,32 @@ __global__ void fp8_to_f32_kernel(const uint8_t* codes, float* out, int n) {
   for (int u = 0; u < 4 && 4 * i + u < n; ++u) out[4 * i + u] = f[u];
 }
 
-template <int DQK, int DVO, int KVB>
+template <int DQK, int DVO, int KV>
 static hipError_t launch_decode_dims(const DecodeArgs& a, int gmax, int grid, hipStream_t s) {
   switch (gmax) {
-    case 1: decode_partial_kernel<DQK, DVO, KVB, 1><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
-    case 2: decode_partial_kernel<DQK, DVO, KVB, 2><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
-    case 3: decode_partial_kernel<DQK, DVO, KVB, 3><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
-    case 4: decode_partial_kernel<DQK, DVO, KVB, 4><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
-    case 6: decode_partial_kernel<DQK, DVO, KVB, 6><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
-    default: decode_partial_kernel<DQK, DVO, KVB, 8><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
+    case 1: decode_partial_kernel<DQK, DVO, KV, 1><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
+    case 2: decode_partial_kernel<DQK, DVO, KV, 2><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
+    case 3: decode_partial_kernel<DQK, DVO, KV, 3><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
+    case 4: decode_partial_kernel<DQK, DVO, KV, 4><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
+    case 6: decode_partial_kernel<DQK, DVO, KV, 6><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
+    default: decode_partial_kernel<DQK, DVO, KV, 8><<<grid, 64 * kDecodeWavesPerGroup, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }
 
-static hipError_t launch_decode(const DecodeArgs& a, int dqk, int dvo, int kvb, int gmax,
+template <int KV>
+static hipError_t launch_decode_kv(const DecodeArgs& a, int dqk, int dvo, int gmax, int grid,
+                                   hipStream_t s) {
+  if (dqk == 512 && dvo == 512) return launch_decode_dims<512, 512, KV>(a, gmax, grid, s);
+  if (dqk == 256 && dvo == 256) return launch_decode_dims<256, 256, KV>(a, gmax, grid, s);
+  return launch_decode_dims<512, 256, KV>(a, gmax, grid, s);
+}
+
+static hipError_t launch_decode(const DecodeArgs& a, int dqk, int dvo, int kv_dtype, int gmax,
                                 int grid, hipStream_t s) {
-  if (kvb == 2) {
-    if (dqk == 512 && dvo == 512) return launch_decode_dims<512, 512, 2>(a, gmax, grid, s);
-    if (dqk == 256 && dvo == 256) return launch_decode_dims<256, 256, 2>(a, gmax, grid, s);
-    return launch_decode_dims<512, 256, 2>(a, gmax, grid, s);
-  }
-  if (dqk == 512 && dvo == 512) return launch_decode_dims<512, 512, 1>(a, gmax, grid, s);
-  if (dqk == 256 && dvo == 256) return launch_decode_dims<256, 256, 1>(a, gmax, grid, s);
-  return launch_decode_dims<512, 256, 1>(a, gmax, grid, s);
+  if (kv_dtype == PA_DTYPE_BF16) return launch_decode_kv<kKvBf16>(a, dqk, dvo, gmax, grid, s);
+  if (kv_dtype == PA_DTYPE_FP8_E4M3FN) return launch_decode_kv<kKvFp8>(a, dqk, dvo, gmax, grid, s);
+  return launch_decode_kv<kKvFp4>(a, dqk, dvo, gmax, grid, s);
 }
 
 }  // namespace pa
@@ -504,6 +571,10 @@ static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_
     a.v = (const char*)cache->v;
     a.k_sp = cache->k_stride_page; a.k_sh = cache->k_stride_head; a.k_st = cache->k_stride_token;
     a.v_sp = cache->v_stride_page; a.v_sh = cache->v_stride_head; a.v_st = cache->v_stride_token;
+    a.k_sf = (const char*)cache->k_sf;
+    a.v_sf = (const char*)cache->v_sf;
+    a.ks_sp = cache->k_sf_stride_page; a.ks_sh = cache->k_sf_stride_head; a.ks_st = cache->k_sf_stride_token;
+    a.vs_sp = cache->v_sf_stride_page; a.vs_sh = cache->v_sf_stride_head; a.vs_st = cache->v_sf_stride_token;
     a.kv_indptr = table->kv_indptr;
     a.kv_indices = table->kv_indices;
     a.segs = (const DecodeSegment*)(ws + plan->items_offset);
@@ -519,9 +590,9 @@ static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_
     a.out_fp32 = out_fp32;
     a.scale_log2 = params->sm_scale * cache->k_scale * kLog2e;
     a.v_scale = cache->v_scale;
-    const int kvb = cache->kv_dtype == PA_DTYPE_FP8_E4M3FN ? 1 : 2;
     const int grid = (plan->num_workers + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup;
-    hipError_t e = launch_decode(a, cache->head_dim_qk, cache->head_dim_vo, kvb, gmax, grid, s);
+    hipError_t e = launch_decode(a, cache->head_dim_qk, cache->head_dim_vo, cache->kv_dtype, gmax,
+                                 grid, s);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
     count_launches(1);
   }
@@ -574,6 +645,8 @@ pa_status pa_debug_gather_kv(const pa_kv_cache* cache, const pa_page_table* tabl
                              void* v_out, void* stream) {
   pa_status st = check_cache(cache, true);
   if (st != PA_OK) return st;
+  if (cache->kv_dtype == PA_DTYPE_NVFP4)
+    return fail(PA_ERR_UNSUPPORTED, "the debug gather copies bf16 and fp8 caches only");
   if (!table || !table->kv_indptr || !table->kv_indices)
     return fail(PA_ERR_INVALID_ARG, "page table is NULL");
   if (request < 0 || request >= table->batch) return fail(PA_ERR_INVALID_ARG, "request out of range");

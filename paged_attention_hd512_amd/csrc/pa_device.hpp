@@ -52,6 +52,25 @@ __device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+// Eight E2M1 values (one dword; element 2i is the low nibble of byte i) -> eight fp32,
+// exact.  v_cvt_scalef32_pk_f32_fp4 converts the byte `sel`, low nibble first.  Its f32
+// scale operand acts through its exponent only (an E8M0 scale: 448 acts as 256), so it
+// stays 1 here and E4M3 block scales are multiplied in separately.
+__device__ __forceinline__ void fp4x8_to_f32(uint32_t w, float* out) {
+  const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  out[0] = a[0]; out[1] = a[1]; out[2] = b[0]; out[3] = b[1];
+  out[4] = c[0]; out[5] = c[1]; out[6] = d[0]; out[7] = d[1];
+}
+
+// One FP8 E4M3FN code (byte `sel` of w) -> fp32, exact.
+template <int SEL>
+__device__ __forceinline__ float fp8_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
+}
+
 // LDS transpose load (ds_read_b64_tr_b16): within each block of 16 lanes, lane i = 4c + e
 // receives element e of the 8-byte rows addressed by lanes c, c+4, c+8 and c+12.
 typedef short s16x4_t __attribute__((ext_vector_type(4)));

@@ -36,9 +36,15 @@ static bool supported_dims(int qk, int vo) {
 
 pa_status check_cache(const pa_kv_cache* c, bool need_pointers) {
   if (!c) return fail(PA_ERR_INVALID_ARG, "cache is NULL");
-  if (c->kv_dtype != PA_DTYPE_BF16 && c->kv_dtype != PA_DTYPE_FP8_E4M3FN)
-    return fail(PA_ERR_UNSUPPORTED, "kv_dtype %d: only bf16 and fp8 e4m3fn KV are supported",
+  if (c->kv_dtype != PA_DTYPE_BF16 && c->kv_dtype != PA_DTYPE_FP8_E4M3FN &&
+      c->kv_dtype != PA_DTYPE_NVFP4)
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype %d: only bf16, fp8 e4m3fn and nvfp4 KV are supported",
                 c->kv_dtype);
+  const bool fp4 = c->kv_dtype == PA_DTYPE_NVFP4;
+  // A block-scale tensor on a cache that is not NVFP4 is refused rather than ignored (the
+  // FlashInfer page's review on output sizing keyed on a stray scale-factor tensor).
+  if (!fp4 && (c->k_sf || c->v_sf))
+    return fail(PA_ERR_INVALID_ARG, "k_sf / v_sf are set on a cache whose kv_dtype is not nvfp4");
   if (c->num_pages < 1 || c->num_kv_heads < 1 || c->page_size < 1)
     return fail(PA_ERR_INVALID_ARG, "num_pages (%d), num_kv_heads (%d) and page_size (%d) must be >= 1",
                 c->num_pages, c->num_kv_heads, c->page_size);
@@ -46,7 +52,8 @@ pa_status check_cache(const pa_kv_cache* c, bool need_pointers) {
     return fail(PA_ERR_UNSUPPORTED,
                 "head dims (qk=%d, vo=%d): supported are (512,512), (256,256), (512,256)",
                 c->head_dim_qk, c->head_dim_vo);
-  const int64_t vec = 16 / dtype_bytes(c->kv_dtype);  // elements per 16-byte vector
+  // Stored units per 16-byte vector: elements, or bytes for NVFP4 (two elements each).
+  const int64_t vec = fp4 ? 16 : 16 / dtype_bytes(c->kv_dtype);
   const int64_t s[6] = {c->k_stride_page, c->k_stride_head, c->k_stride_token,
                         c->v_stride_page, c->v_stride_head, c->v_stride_token};
   const char* names[6] = {"k_stride_page", "k_stride_head", "k_stride_token",
@@ -57,6 +64,18 @@ pa_status check_cache(const pa_kv_cache* c, bool need_pointers) {
       return fail(PA_ERR_UNSUPPORTED, "%s = %lld is not a multiple of 16 bytes", names[i],
                   (long long)s[i]);
   }
+  if (fp4) {
+    const int64_t f[6] = {c->k_sf_stride_page, c->k_sf_stride_head, c->k_sf_stride_token,
+                          c->v_sf_stride_page, c->v_sf_stride_head, c->v_sf_stride_token};
+    const char* fn[6] = {"k_sf_stride_page", "k_sf_stride_head", "k_sf_stride_token",
+                         "v_sf_stride_page", "v_sf_stride_head", "v_sf_stride_token"};
+    for (int i = 0; i < 6; ++i) {
+      if (f[i] < 0) return fail(PA_ERR_INVALID_ARG, "%s is negative", fn[i]);
+      if (f[i] % 16)
+        return fail(PA_ERR_UNSUPPORTED, "%s = %lld is not a multiple of 16 bytes", fn[i],
+                    (long long)f[i]);
+    }
+  }
   if (c->kv_dtype == PA_DTYPE_BF16 && (c->k_scale != 1.0f || c->v_scale != 1.0f))
     return fail(PA_ERR_INVALID_ARG, "bf16 KV takes k_scale = v_scale = 1");
   if (!(std::isfinite(c->k_scale) && c->k_scale > 0.f && std::isfinite(c->v_scale) &&
@@ -66,6 +85,11 @@ pa_status check_cache(const pa_kv_cache* c, bool need_pointers) {
     if (!c->k || !c->v) return fail(PA_ERR_INVALID_ARG, "cache k/v pointer is NULL");
     if (((uintptr_t)c->k | (uintptr_t)c->v) & 15)
       return fail(PA_ERR_UNSUPPORTED, "cache k/v pointers must be 16-byte aligned");
+    if (fp4) {
+      if (!c->k_sf || !c->v_sf) return fail(PA_ERR_INVALID_ARG, "nvfp4 cache: k_sf / v_sf is NULL");
+      if (((uintptr_t)c->k_sf | (uintptr_t)c->v_sf) & 15)
+        return fail(PA_ERR_UNSUPPORTED, "nvfp4 cache: k_sf / v_sf must be 16-byte aligned");
+    }
   }
   return PA_OK;
 }
@@ -166,6 +190,8 @@ pa_status pa_kv_cache_hnd(const void* base, int32_t kv_dtype, int32_t num_pages,
                           int32_t num_kv_heads, int32_t page_size, int32_t head_dim,
                           float k_scale, float v_scale, pa_kv_cache* out) {
   if (!out) return fail(PA_ERR_INVALID_ARG, "out is NULL");
+  if (kv_dtype == PA_DTYPE_NVFP4)
+    return fail(PA_ERR_INVALID_ARG, "nvfp4 caches carry block scales: use pa_kv_cache_nvfp4_hnd");
   pa_kv_cache c;
   memset(&c, 0, sizeof(c));
   const int esz = dtype_bytes(kv_dtype);
@@ -193,6 +219,9 @@ pa_status pa_kv_cache_separate(const void* k, const void* v, int32_t kv_dtype,
                                int32_t head_dim_qk, int32_t head_dim_vo, float k_scale,
                                float v_scale, pa_kv_cache* out) {
   if (!out) return fail(PA_ERR_INVALID_ARG, "out is NULL");
+  if (kv_dtype == PA_DTYPE_NVFP4)
+    return fail(PA_ERR_INVALID_ARG,
+                "nvfp4 caches carry block scales: use pa_kv_cache_nvfp4_separate");
   pa_kv_cache c;
   memset(&c, 0, sizeof(c));
   c.k = k;
@@ -215,6 +244,63 @@ pa_status pa_kv_cache_separate(const void* k, const void* v, int32_t kv_dtype,
   if (st != PA_OK) return st;
   *out = c;
   return PA_OK;
+}
+
+pa_status pa_kv_cache_nvfp4_separate(const void* k, const void* v, const void* k_sf,
+                                     const void* v_sf, int32_t num_pages,
+                                     int32_t num_kv_heads, int32_t page_size,
+                                     int32_t head_dim_qk, int32_t head_dim_vo, float k_scale,
+                                     float v_scale, pa_kv_cache* out) {
+  if (!out) return fail(PA_ERR_INVALID_ARG, "out is NULL");
+  pa_kv_cache c;
+  memset(&c, 0, sizeof(c));
+  c.k = k;
+  c.v = v;
+  c.k_sf = k_sf;
+  c.v_sf = v_sf;
+  c.kv_dtype = PA_DTYPE_NVFP4;
+  c.num_pages = num_pages;
+  c.num_kv_heads = num_kv_heads;
+  c.page_size = page_size;
+  c.head_dim_qk = head_dim_qk;
+  c.head_dim_vo = head_dim_vo;
+  const int64_t kb = head_dim_qk / 2, vb = head_dim_vo / 2;      // data bytes per row
+  const int64_t kf = head_dim_qk / 16, vf = head_dim_vo / 16;    // block scales per row
+  c.k_stride_token = kb;
+  c.k_stride_head = (int64_t)page_size * kb;
+  c.k_stride_page = (int64_t)num_kv_heads * page_size * kb;
+  c.v_stride_token = vb;
+  c.v_stride_head = (int64_t)page_size * vb;
+  c.v_stride_page = (int64_t)num_kv_heads * page_size * vb;
+  c.k_sf_stride_token = kf;
+  c.k_sf_stride_head = (int64_t)page_size * kf;
+  c.k_sf_stride_page = (int64_t)num_kv_heads * page_size * kf;
+  c.v_sf_stride_token = vf;
+  c.v_sf_stride_head = (int64_t)page_size * vf;
+  c.v_sf_stride_page = (int64_t)num_kv_heads * page_size * vf;
+  c.k_scale = k_scale;
+  c.v_scale = v_scale;
+  pa_status st = check_cache(&c, false);
+  if (st != PA_OK) return st;
+  *out = c;
+  return PA_OK;
+}
+
+pa_status pa_kv_cache_nvfp4_hnd(const void* data, const void* sf, int32_t num_pages,
+                                int32_t num_kv_heads, int32_t page_size, int32_t head_dim,
+                                float k_scale, float v_scale, pa_kv_cache* out) {
+  if (!out) return fail(PA_ERR_INVALID_ARG, "out is NULL");
+  const int64_t half_d = (int64_t)num_kv_heads * page_size * (head_dim / 2);    // K half, bytes
+  const int64_t half_f = (int64_t)num_kv_heads * page_size * (head_dim / 16);
+  const char* d = (const char*)data;
+  const char* f = (const char*)sf;
+  pa_status st = pa_kv_cache_nvfp4_separate(d, d ? d + half_d : nullptr, f, f ? f + half_f : nullptr,
+                                            num_pages, num_kv_heads, page_size, head_dim,
+                                            head_dim, k_scale, v_scale, out);
+  if (st != PA_OK) return st;
+  out->k_stride_page = out->v_stride_page = 2 * half_d;
+  out->k_sf_stride_page = out->v_sf_stride_page = 2 * half_f;
+  return check_cache(out, false);
 }
 
 pa_status pa_validate_page_table_host(const int32_t* kv_indptr_host,

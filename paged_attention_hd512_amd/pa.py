@@ -22,6 +22,7 @@ PA_ERR_HIP = 4
 PA_DTYPE_BF16 = 0
 PA_DTYPE_FP32 = 1
 PA_DTYPE_FP8_E4M3FN = 2
+PA_DTYPE_NVFP4 = 3
 
 _STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
                  3: "PA_ERR_WORKSPACE_TOO_SMALL", 4: "PA_ERR_HIP"}
@@ -40,7 +41,10 @@ class pa_kv_cache(Structure):
                 ("head_dim_vo", c_int32), ("k_stride_page", c_int64), ("k_stride_head", c_int64),
                 ("k_stride_token", c_int64), ("v_stride_page", c_int64),
                 ("v_stride_head", c_int64), ("v_stride_token", c_int64), ("k_scale", c_float),
-                ("v_scale", c_float)]
+                ("v_scale", c_float), ("k_sf", c_void_p), ("v_sf", c_void_p),
+                ("k_sf_stride_page", c_int64), ("k_sf_stride_head", c_int64),
+                ("k_sf_stride_token", c_int64), ("v_sf_stride_page", c_int64),
+                ("v_sf_stride_head", c_int64), ("v_sf_stride_token", c_int64)]
 
 
 class pa_page_table(Structure):
@@ -75,6 +79,10 @@ SIGNATURES = {
                                   c_float, POINTER(pa_kv_cache)]),
     "pa_kv_cache_separate": (c_int32, [_P, _P, c_int32, c_int32, c_int32, c_int32, c_int32,
                                        c_int32, c_float, c_float, POINTER(pa_kv_cache)]),
+    "pa_kv_cache_nvfp4_hnd": (c_int32, [_P, _P, c_int32, c_int32, c_int32, c_int32, c_float,
+                                        c_float, POINTER(pa_kv_cache)]),
+    "pa_kv_cache_nvfp4_separate": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, c_int32, c_int32,
+                                             c_int32, c_float, c_float, POINTER(pa_kv_cache)]),
     "pa_validate_page_table_host": (c_int32, [_I32P, _I32P, _I32P, c_int32, c_int32, c_int32]),
     "pa_decode_plan": (c_int32, [POINTER(pa_attn_params), POINTER(pa_kv_cache), _I32P, _I32P,
                                  c_int32, c_int32, _P, c_size_t, POINTER(pa_plan)]),
@@ -159,6 +167,23 @@ def pa_kv_cache_separate(k, v, kv_dtype, num_pages, num_kv_heads, page_size, hea
     _check(lib().pa_kv_cache_separate(k, v, kv_dtype, num_pages, num_kv_heads, page_size,
                                       head_dim_qk, head_dim_vo, k_scale, v_scale,
                                       ctypes.byref(c)))
+    return c
+
+
+def pa_kv_cache_nvfp4_hnd(data, sf, num_pages, num_kv_heads, page_size, head_dim, k_scale=1.0,
+                          v_scale=1.0):
+    c = pa_kv_cache()
+    _check(lib().pa_kv_cache_nvfp4_hnd(data, sf, num_pages, num_kv_heads, page_size, head_dim,
+                                       k_scale, v_scale, ctypes.byref(c)))
+    return c
+
+
+def pa_kv_cache_nvfp4_separate(k, v, k_sf, v_sf, num_pages, num_kv_heads, page_size,
+                               head_dim_qk, head_dim_vo, k_scale=1.0, v_scale=1.0):
+    c = pa_kv_cache()
+    _check(lib().pa_kv_cache_nvfp4_separate(k, v, k_sf, v_sf, num_pages, num_kv_heads,
+                                            page_size, head_dim_qk, head_dim_vo, k_scale,
+                                            v_scale, ctypes.byref(c)))
     return c
 
 
@@ -250,28 +275,42 @@ def _torch():
 
 
 def kv_dtype_code(kv_dtype):
-    return {"bf16": PA_DTYPE_BF16, "fp8": PA_DTYPE_FP8_E4M3FN}[kv_dtype]
+    return {"bf16": PA_DTYPE_BF16, "fp8": PA_DTYPE_FP8_E4M3FN, "nvfp4": PA_DTYPE_NVFP4}[kv_dtype]
 
 
 def out_dtype_code(out_dtype):
     return {"bf16": PA_DTYPE_BF16, "fp32": PA_DTYPE_FP32}[out_dtype]
 
 
-def cache_from_pools(k_pool, v_pool, kv_dtype, k_scale=1.0, v_scale=1.0):
+def cache_from_pools(k_pool, v_pool, kv_dtype, k_scale=1.0, v_scale=1.0, k_sf=None, v_sf=None):
     """pa_kv_cache for two [num_pages, Hkv, P, D] views (halves of a combined cache or
-    separate pools), taking strides from the tensors."""
-    for t in (k_pool, v_pool):
+    separate pools), taking strides from the tensors.  NVFP4 pools are uint8
+    [num_pages, Hkv, P, D/2] with block-scale views k_sf / v_sf [num_pages, Hkv, P, D/16]."""
+    fp4 = kv_dtype == "nvfp4"
+    if fp4 != (k_sf is not None and v_sf is not None):
+        raise ValueError("block scales k_sf and v_sf go with kv_dtype 'nvfp4' and only with it")
+    for t in (k_pool, v_pool) + ((k_sf, v_sf) if fp4 else ()):
         if t.dim() != 4 or t.stride(3) != 1:
             raise ValueError("pools must be [num_pages, num_kv_heads, page_size, head_dim] views "
                              "with a unit head_dim stride")
+    per_unit = 2 if fp4 else 1  # elements per stored unit
     c = pa_kv_cache()
     c.k, c.v = k_pool.data_ptr(), v_pool.data_ptr()
     c.kv_dtype = kv_dtype_code(kv_dtype)
-    c.num_pages, c.num_kv_heads, c.page_size, c.head_dim_qk = k_pool.shape
-    c.head_dim_vo = v_pool.shape[3]
+    c.num_pages, c.num_kv_heads, c.page_size = k_pool.shape[:3]
+    c.head_dim_qk = k_pool.shape[3] * per_unit
+    c.head_dim_vo = v_pool.shape[3] * per_unit
     c.k_stride_page, c.k_stride_head, c.k_stride_token = k_pool.stride()[:3]
     c.v_stride_page, c.v_stride_head, c.v_stride_token = v_pool.stride()[:3]
     c.k_scale, c.v_scale = k_scale, v_scale
+    if fp4:
+        if (k_sf.shape[3] * 16 != c.head_dim_qk or v_sf.shape[3] * 16 != c.head_dim_vo
+                or tuple(k_sf.shape[:3]) != tuple(k_pool.shape[:3])
+                or tuple(v_sf.shape[:3]) != tuple(v_pool.shape[:3])):
+            raise ValueError("block scales must be [num_pages, num_kv_heads, page_size, D/16]")
+        c.k_sf, c.v_sf = k_sf.data_ptr(), v_sf.data_ptr()
+        c.k_sf_stride_page, c.k_sf_stride_head, c.k_sf_stride_token = k_sf.stride()[:3]
+        c.v_sf_stride_page, c.v_sf_stride_head, c.v_sf_stride_token = v_sf.stride()[:3]
     return c
 
 
@@ -285,13 +324,13 @@ class PagedDecode:
 
     def __init__(self, k_pool, v_pool, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads,
                  *, kv_dtype="bf16", k_scale=1.0, v_scale=1.0, sm_scale=None, window=0,
-                 num_splits=0, out_dtype="bf16"):
+                 num_splits=0, out_dtype="bf16", k_sf=None, v_sf=None):
         torch = _torch()
         dev = k_pool.device
-        self.cache = cache_from_pools(k_pool, v_pool, kv_dtype, k_scale, v_scale)
-        self._keep = (k_pool, v_pool)
+        self.cache = cache_from_pools(k_pool, v_pool, kv_dtype, k_scale, v_scale, k_sf, v_sf)
+        self._keep = (k_pool, v_pool, k_sf, v_sf)
         self.params = pa_attn_params(num_qo_heads, sm_scale if sm_scale is not None
-                                     else 1.0 / float(k_pool.shape[3]) ** 0.5,
+                                     else 1.0 / float(self.cache.head_dim_qk) ** 0.5,
                                      window, 1, PA_DTYPE_BF16, out_dtype_code(out_dtype))
         self.out_dtype = out_dtype
         self.indptr_d = torch.as_tensor(np.asarray(kv_indptr, np.int32)).to(dev)

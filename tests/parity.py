@@ -2,7 +2,8 @@
 
 Tolerances: for bf16 inputs with fp32 accumulation, max-abs error <= 1e-2 and mean-abs
 error <= 1e-3 over every valid output element; lse max-abs <= 1e-3 where finite, and the
-same -inf positions.  FP8 KV is compared with the oracle run on the dequantised codes.
+same -inf positions.  FP8 and NVFP4 KV are compared with the oracle run on the stored
+codes (and block scales), which it dequantises itself.
 
 A bf16 output also carries the rounding of the exact result to bf16, up to half an ulp,
 i.e. 2^-8 |ref|; that alone exceeds 1e-2 once |ref| > 2.56 (rows that see few keys).  For
@@ -61,6 +62,13 @@ def compare(name, got, ref, got_lse=None, ref_lse=None, out_dtype="fp32"):
     return max_abs, mean_abs
 
 
+def _scales_np(src):
+    """NVFP4 block-scale pools of a case (or of a copied-out sample) as numpy, else None."""
+    if src.get("k_sf") is None:
+        return {}
+    return dict(k_sf=pool_to_np(src["k_sf"], "nvfp4"), v_sf=pool_to_np(src["v_sf"], "nvfp4"))
+
+
 def oracle_decode(case, requests=None):
     """Oracle on the case's inputs (all requests, or a sample copied out page by page)."""
     if requests is None:
@@ -70,14 +78,15 @@ def oracle_decode(case, requests=None):
         return oracle.decode_ref(q, kp, vp, case.kv_indptr, case.kv_indices,
                                  case.kv_last_page_len, case.page_size, case.sm_scale,
                                  window=case.window, kv_dtype=case.kv_dtype,
-                                 k_scale=case.k_scale, v_scale=case.v_scale)
+                                 k_scale=case.k_scale, v_scale=case.v_scale,
+                                 **_scales_np(dict(k_sf=case.k_sf, v_sf=case.v_sf)))
     sub = extract_requests(case, requests)
     q = oracle.bf16_bits_to_f64(bf16_to_np(sub["q"]))
     return oracle.decode_ref(q, pool_to_np(sub["k_pool"], case.kv_dtype),
                              pool_to_np(sub["v_pool"], case.kv_dtype), sub["kv_indptr"],
                              sub["kv_indices"], sub["kv_last_page_len"], case.page_size,
                              case.sm_scale, window=case.window, kv_dtype=case.kv_dtype,
-                             k_scale=case.k_scale, v_scale=case.v_scale)
+                             k_scale=case.k_scale, v_scale=case.v_scale, **_scales_np(sub))
 
 
 def oracle_prefill(case, tokens=None, requests=None):
@@ -105,7 +114,7 @@ def gpu_decode(case, num_splits=None, out_dtype=None, with_lse=True):
                          k_scale=case.k_scale, v_scale=case.v_scale, sm_scale=case.sm_scale,
                          window=case.window,
                          num_splits=case.num_splits if num_splits is None else num_splits,
-                         out_dtype=out_dtype or case.out_dtype)
+                         out_dtype=out_dtype or case.out_dtype, k_sf=case.k_sf, v_sf=case.v_sf)
     out, lse = runner.run(case.q, with_lse=with_lse)
     torch.cuda.synchronize()
     return runner, out, lse

@@ -1,0 +1,100 @@
+"""GPU parity of NVFP4 decode (packed E2M1 K/V with one E4M3 block scale per 16 head_dim
+elements, dequantised on load) with the oracle, through the C ABI.
+
+The FlashInfer NVFP4 page (section "NVFP4 split-KV correctness (added)") reports output
+drift when a short query over long KV is split across the key axis; here the split and
+unsplit decodes of the same inputs are both held to the oracle's tolerance, and to each
+other."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import make_decode_case, decode_workload
+from parity import say, compare, oracle_decode, gpu_decode, out_to_np, pool_to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return "cuda"
+
+
+def test_single_key_requests_return_the_dequantised_v_row_exactly():
+    """With one visible key the softmax weight is 1, so the fp32 output is the key's V row
+    dequantised (e2m1 x block scale, exact) times v_scale, one rounding: bit for bit the
+    oracle's value rounded to fp32.  The lse is sm_scale * k_scale * q.k of that key."""
+    for dim, dvo, page in ((512, 512, 16), (256, 256, 1), (512, 256, 3)):
+        say(f"nvfp4 single-key rows dims={dim}/{dvo} page={page}")
+        c = make_decode_case([1] * 96, 8, 2, dim, page, head_dim_vo=dvo, kv_dtype="nvfp4",
+                             out_dtype="fp32", seed=21, device=dev())
+        _, o, lse = gpu_decode(c)
+        ref, ref_lse = oracle_decode(c)
+        got = o.cpu().numpy()
+        assert np.array_equal(got, ref.astype(np.float32)), "V dequantisation is not exact"
+        assert np.abs(lse.cpu().numpy() - ref_lse).max() < 1e-4
+
+
+NVFP4_SWEEP = [
+    # lens, hq, hkv, dim, dvo, page, window, splits, out
+    ([37, 64, 1, 16, 17, 300], 8, 1, 512, 512, 16, 0, 0, "fp32"),
+    ([37, 64, 1, 16, 17, 300], 24, 4, 512, 512, 16, 0, 8, "bf16"),
+    ([5, 130, 777, 64], 12, 4, 512, 512, 64, 0, 0, "bf16"),
+    ([5, 130, 777, 64], 12, 4, 512, 512, 64, 0, 3, "fp32"),
+    ([600, 1500, 33, 2048], 16, 8, 512, 512, 1, 100, 0, "bf16"),
+    ([600, 1500, 33, 2048], 16, 8, 256, 256, 32, 1024, 0, "fp32"),
+    ([600, 1500, 33, 2048], 16, 8, 256, 256, 1, 100, 4, "bf16"),
+    ([45, 46, 47, 200], 6, 2, 512, 256, 3, 0, 2, "fp32"),
+    ([45, 46, 47, 200], 6, 2, 512, 256, 16, 17, 0, "fp32"),
+    ([100, 200, 300], 4, 1, 256, 256, 8, 0, 0, "bf16"),
+    ([64, 128, 192], 40, 8, 512, 512, 16, 0, 64, "bf16"),
+    ([0, 20, 0, 3], 8, 1, 512, 512, 16, 0, 2, "fp32"),
+]
+
+
+@pytest.mark.parametrize("lens,hq,hkv,dim,dvo,page,window,splits,out", NVFP4_SWEEP)
+def test_nvfp4_decode_sweep(lens, hq, hkv, dim, dvo, page, window, splits, out):
+    name = (f"nvfp4 lens={lens} heads={hq}/{hkv} dims={dim}/{dvo} page={page} "
+            f"window={window} splits={splits} out={out}")
+    say(name)
+    c = make_decode_case(lens, hq, hkv, dim, page, head_dim_vo=dvo, kv_dtype="nvfp4",
+                         window=window, num_splits=splits, out_dtype=out,
+                         seed=len(lens) + hq + 100, device=dev())
+    _, o, lse = gpu_decode(c)
+    ref, ref_lse = oracle_decode(c)
+    compare(name, out_to_np(o), ref, lse.cpu().numpy(), ref_lse, out_dtype=out)
+
+
+def test_split_and_unsplit_nvfp4_decode_agree_on_long_kv():
+    """One query over long NVFP4 KV, unsplit (balanced pieces), and cut into 1, 8 and 64
+    key chunks: every result meets the oracle's tolerance and they agree with each other
+    to fp32 rounding of the merge."""
+    lens = [9000, 12000, 700, 16384]
+    c = make_decode_case(lens, 16, 8, 512, 64, head_dim_vo=512, kv_dtype="nvfp4",
+                         out_dtype="fp32", seed=33, device=dev())
+    ref, ref_lse = oracle_decode(c)
+    outs = {}
+    for splits in (0, 1, 8, 64):
+        say(f"nvfp4 long KV splits={splits}")
+        _, o, lse = gpu_decode(c, num_splits=splits)
+        compare(f"nvfp4 long KV splits={splits}", out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
+        outs[splits] = (out_to_np(o), lse.cpu().numpy())
+    for splits in (0, 8, 64):
+        assert np.abs(outs[splits][0] - outs[1][0]).max() < 1e-4
+        assert np.abs(outs[splits][1] - outs[1][1]).max() < 1e-4
+
+
+@pytest.mark.slow
+def test_full_size_nvfp4_workload_on_sampled_requests():
+    say("full-size nvfp4_decode")
+    c = decode_workload("nvfp4_decode", device=dev())
+    _, o, lse = gpu_decode(c)
+    lens = c.kv_lens
+    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)),
+                     int(np.random.default_rng(0).integers(0, c.batch))})
+    ref, ref_lse = oracle_decode(c, requests=sample)
+    compare(f"nvfp4_decode requests {sample}", out_to_np(o[sample]), ref,
+            lse[sample].cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
+    assert torch.isfinite(o.float()).all()

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (pa_[a-z0-9_]+)$", out, flags=re.M))
@@ -281,6 +281,42 @@ def test_prefill_rejects_more_new_tokens_than_keys_and_fp8():
     c8 = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_FP8_E4M3FN, 10, 2, P, 512, 1.0, 1.0)
     with pytest.raises(pa.PaError) as e:
         pa.pa_prefill_plan(params(hq=4), c8, [0, 10], ip, la)
+    assert e.value.status == pa.PA_ERR_UNSUPPORTED
+
+
+def test_nvfp4_constructors_give_byte_strides_of_data_and_block_scales():
+    c = pa.pa_kv_cache_nvfp4_hnd(0x10000, 0x90000, 10, 2, 16, 512, 0.5, 0.25)
+    assert c.kv_dtype == pa.PA_DTYPE_NVFP4 and c.head_dim_qk == c.head_dim_vo == 512
+    assert (c.k_stride_token, c.k_stride_head, c.k_stride_page) == (256, 16 * 256, 2 * 2 * 16 * 256)
+    assert (c.k_sf_stride_token, c.k_sf_stride_head, c.k_sf_stride_page) == (32, 16 * 32,
+                                                                              2 * 2 * 16 * 32)
+    assert c.v == 0x10000 + 2 * 16 * 256 and c.v_sf == 0x90000 + 2 * 16 * 32
+    assert (c.v_stride_page, c.v_sf_stride_page) == (c.k_stride_page, c.k_sf_stride_page)
+    s = pa.pa_kv_cache_nvfp4_separate(0x10000, 0x20000, 0x30000, 0x40000, 10, 2, 1, 512, 256)
+    assert (s.k_stride_token, s.v_stride_token, s.k_sf_stride_token, s.v_sf_stride_token) == (
+        256, 128, 32, 16)
+    assert (s.k_stride_page, s.v_sf_stride_page) == (2 * 256, 2 * 16)
+    pa.pa_decode_plan(params(hq=8), c, *lens_to_table([37, 64], 16), 0)  # decode plans
+
+
+def test_nvfp4_misuse_is_refused():
+    ip, la = lens_to_table([20], 16)
+    with pytest.raises(pa.PaError) as e:  # the plain constructors have no block scales
+        pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_NVFP4, 10, 2, 16, 512)
+    assert e.value.status == pa.PA_ERR_INVALID_ARG and "nvfp4" in e.value.message
+    c = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_FP8_E4M3FN, 10, 2, 16, 512, 1.0, 1.0)
+    c.k_sf = 0x90000  # a stray block-scale tensor on an FP8 cache
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode_plan(params(hq=2), c, ip, la, 0)
+    assert e.value.status == pa.PA_ERR_INVALID_ARG and "k_sf" in e.value.message
+    f = pa.pa_kv_cache_nvfp4_hnd(0x10000, 0x90000, 10, 2, 16, 512)
+    f.v_sf_stride_token = 40  # not a multiple of 16 bytes
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode_plan(params(hq=2), f, ip, la, 0)
+    assert e.value.status == pa.PA_ERR_UNSUPPORTED and "v_sf_stride_token" in e.value.message
+    f = pa.pa_kv_cache_nvfp4_hnd(0x10000, 0x90000, 10, 2, 16, 512)
+    with pytest.raises(pa.PaError) as e:  # prefill reads bf16 KV only
+        pa.pa_prefill_plan(params(hq=4), f, [0, 20], ip, la)
     assert e.value.status == pa.PA_ERR_UNSUPPORTED
 
 
