@@ -51,7 +51,9 @@ def kernel_source_hash():
 def decode_algorithmic_bytes(case, requests=None):
     import numpy as np
     reqs = range(case.batch) if requests is None else requests
-    esz = 1 if case.kv_dtype == "fp8" else 2
+    # Bytes per KV element: bf16 2, FP8 1, NVFP4 half a byte plus one E4M3 block scale
+    # per 16 elements.
+    esz = {"bf16": 2.0, "fp8": 1.0, "nvfp4": 0.5 + 1.0 / 16}[case.kv_dtype]
     out_sz = 4 if case.out_dtype == "fp32" else 2
     total = 0
     for b in reqs:
@@ -59,7 +61,7 @@ def decode_algorithmic_bytes(case, requests=None):
         start = max(0, L - case.window) if case.window > 0 else 0
         vis = L - start
         pages = 0 if vis == 0 else (L - 1) // case.page_size - start // case.page_size + 1
-        total += case.num_kv_heads * vis * (case.head_dim_qk + case.head_dim_vo) * esz
+        total += int(case.num_kv_heads * vis * (case.head_dim_qk + case.head_dim_vo) * esz)
         total += case.num_qo_heads * (case.head_dim_qk * 2 + case.head_dim_vo * out_sz)
         total += 4 * pages
     total += 4 * (2 * len(list(reqs)) + 1)
@@ -106,7 +108,8 @@ def time_decode(case, steps, warmup):
     run = PagedDecode(case.k_pool, case.v_pool, case.kv_indptr, case.kv_indices,
                       case.kv_last_page_len, case.num_qo_heads, kv_dtype=case.kv_dtype,
                       k_scale=case.k_scale, v_scale=case.v_scale, sm_scale=case.sm_scale,
-                      window=case.window, num_splits=case.num_splits, out_dtype=case.out_dtype)
+                      window=case.window, num_splits=case.num_splits, out_dtype=case.out_dtype,
+                      k_sf=case.k_sf, v_sf=case.v_sf)
     out, lse = run.run(case.q)
     stream = torch.cuda.current_stream()
     sh = pa.current_stream_handle()
@@ -140,7 +143,8 @@ def time_decode_graph(case, steps, warmup):
     run = PagedDecode(case.k_pool, case.v_pool, case.kv_indptr, case.kv_indices,
                       case.kv_last_page_len, case.num_qo_heads, kv_dtype=case.kv_dtype,
                       k_scale=case.k_scale, v_scale=case.v_scale, sm_scale=case.sm_scale,
-                      window=case.window, num_splits=case.num_splits, out_dtype=case.out_dtype)
+                      window=case.window, num_splits=case.num_splits, out_dtype=case.out_dtype,
+                      k_sf=case.k_sf, v_sf=case.v_sf)
     out, lse = run.run(case.q)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -233,12 +237,15 @@ def oracle_decode_baseline(case, budget_s=12.0):
             vp = sub["v_pool"].contiguous().view(dt).numpy()
             if case.kv_dtype == "bf16":
                 kp, vp = kp.view(np.uint16), vp.view(np.uint16)
+            sf = {}
+            if case.kv_dtype == "nvfp4":
+                sf = {n: sub[n].contiguous().numpy() for n in ("k_sf", "v_sf")}
             q = oracle.bf16_bits_to_f64(sub["q"].contiguous().view(torch.int16).numpy().view(np.uint16))
             t0 = time.perf_counter()
             oracle.decode_ref(q, kp, vp, sub["kv_indptr"], sub["kv_indices"],
                               sub["kv_last_page_len"], case.page_size, case.sm_scale,
                               window=case.window, kv_dtype=case.kv_dtype,
-                              k_scale=case.k_scale, v_scale=case.v_scale)
+                              k_scale=case.k_scale, v_scale=case.v_scale, **sf)
             spent += time.perf_counter() - t0
             done.append(b)
             if spent >= budget_s:
@@ -399,7 +406,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa_decode",
-                    help="gqa_decode | gqa_decode_splitk8 | fp8_decode | "
+                    help="gqa_decode | gqa_decode_splitk8 | fp8_decode | nvfp4_decode | "
                          "window_decode_d512_p1 | ... | "
                          "causal_prefill_vo512 | causal_prefill_vo256 | extend_prefill")
     ap.add_argument("--no-secondary", action="store_true")
@@ -443,7 +450,7 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(main_res["step_ms"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if case.kv_dtype == "bf16" else "fp8-kv/bf16",
+        "dtype": "bf16" if case.kv_dtype == "bf16" else f"{case.kv_dtype}-kv/bf16",
         "data": "synthetic",
         "config": decode_config(case) if not is_prefill else {
             "workload": case.name, "batch": case.batch, "qo_len": int(case.qo_lens[0]),
@@ -470,7 +477,8 @@ def main():
 
     if not args.no_secondary:
         sec = {}
-        names = ["gqa_decode", "gqa_decode_splitk8", "fp8_decode", "window_decode_d512_p1",
+        names = ["gqa_decode", "gqa_decode_splitk8", "fp8_decode", "nvfp4_decode",
+                 "window_decode_d512_p1",
                  "window_decode_d512_p32",
                  "window_decode_d256_p1", "window_decode_d256_p32", "causal_prefill_vo512",
                  "causal_prefill_vo256", "extend_prefill"]

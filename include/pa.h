@@ -15,7 +15,7 @@
  *    separately allocated K and V pools ("feat(attention): asymmetric VO-split NVFP4 paged
  *    prefill (qk=512/vo=256) for Gemma-4 on SM120/121", FlashInfer pull request 3684,
  *    sections "Summary" and "What's in it").
- *  - NVFP4 KV (decode): packed E2M1 pairs with one FP8 block scale per 16 head_dim
+ *  - NVFP4 KV (decode and prefill): packed E2M1 pairs with one FP8 block scale per 16 head_dim
  *    elements of a token, the scales in a tensor of their own laid out like the data (the
  *    FlashInfer page, sections "Summary", "What's in it" and "NVFP4 split-KV correctness
  *    (added)"), dequantised on load.
@@ -231,7 +231,7 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
  * merge combines them (plan->num_merges split tiles, plan->num_slots slots,
  * plan->chunk_blocks = C, 0 without splitting).  Items run by key count, longest first.
  * The result does not depend on the split.  Same two-call sizing as pa_decode_plan.
- * Supported: head dims (512,512), (256,256), (512,256); kv bf16; q bf16; out fp32 or bf16;
+ * Supported: head dims (512,512), (256,256), (512,256); kv bf16 or nvfp4; q bf16; out fp32 or bf16;
  * num_qo_heads / num_kv_heads <= 16.  Never calls HIP. */
 pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache,
                           const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,

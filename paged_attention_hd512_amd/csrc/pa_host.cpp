@@ -472,8 +472,8 @@ pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache
   if (!plan) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
   pa_status st = check_cache(cache, false);
   if (st != PA_OK) return st;
-  if (cache->kv_dtype != PA_DTYPE_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 KV only");
+  if (cache->kv_dtype != PA_DTYPE_BF16 && cache->kv_dtype != PA_DTYPE_NVFP4)
+    return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 and nvfp4 KV");
   if ((st = check_params(params, cache, kMaxPrefillGroup)) != PA_OK) return st;
   if ((st = check_table_host(kv_indptr_host, kv_last_page_len_host, batch, cache->page_size)) != PA_OK)
     return st;

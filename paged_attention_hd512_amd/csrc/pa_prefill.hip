@@ -23,6 +23,11 @@
 //   * The running max is only moved when a row's max grows by more than 2^8, so the
 //     accumulators are rescaled rarely; the final normalisation uses the same reference
 //     max, so the result is unchanged.
+// NVFP4 KV (the FlashInfer page, sections "Summary" and "What's in it": packed E2M1 with one
+// E4M3 block scale per 16 head_dim elements): a direct-to-LDS copy cannot convert, so each
+// wave loads its key rows' packed bytes and block scales into registers when a stage's copy
+// would be issued and writes them to LDS as bf16 (exact), in the same swizzled layout, at
+// the end of the interval, before the barrier that hands the stage over.
 
 #include <hip/hip_runtime.h>
 
@@ -67,6 +72,11 @@ struct PrefillArgs {
   int32_t causal;
   int32_t out_fp32;
   float scale_log2;
+  float v_scale;              // NVFP4: tensor-wide V scale (1 otherwise)
+  const char* k_sf;           // NVFP4 block scales, else null
+  const char* v_sf;
+  int64_t ks_sp, ks_sh, ks_st;  // block-scale byte strides
+  int64_t vs_sp, vs_sh, vs_st;
 };
 
 // LDS stages hold key rows unpadded; 16-byte chunk c of row r sits at chunk position
@@ -141,7 +151,7 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <int DQK, int DVO, int PM>
+template <int DQK, int DVO, int PM, bool FP4>
 __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = kPrefillWaves;
   constexpr int KS = kKeyStage;
@@ -320,9 +330,70 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
           (__attribute__((address_space(3))) void*)(v_lds + vo + (my_row + i) * DVO), 16, off, 0, 0, 0);
     }
   };
+  // NVFP4: lane l holds key row my_row + l / 16 of the stage and part l % 16 of its packed
+  // row (FKB bytes of K, FVB of V: 2 FKB elements) with the block scales of that part.  Key
+  // rows are clamped into the tile's range like the copies' (clamped keys are masked out).
+  constexpr int FKB = DQK / 32, FVB = DVO / 32;
+  using fk_t = typename std::conditional<FKB == 16, u32x4_t, u32x2_t>::type;
+  using fv_t = typename std::conditional<FVB == 16, u32x4_t, u32x2_t>::type;
+  fk_t fk;
+  fv_t fv;
+  uint32_t fks = 0, fvs = 0;  // FKB / 8 (FVB / 8) block-scale codes, low byte first
+  auto fp4_load = [&](int st) {
+    const int part = lane & 15;
+    int t = st * KS + my_row + (lane >> 4);
+    t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
+    const int j = t / a.page_size;
+    const int64_t pg = pages[j];
+    const int64_t sl = t - j * a.page_size;
+    const char* kd = a.k + pg * a.k_sp + (int64_t)kvh * a.k_sh + sl * a.k_st + FKB * part;
+    const char* vd = a.v + pg * a.v_sp + (int64_t)kvh * a.v_sh + sl * a.v_st + FVB * part;
+    const char* ks = a.k_sf + pg * a.ks_sp + (int64_t)kvh * a.ks_sh + sl * a.ks_st + (FKB / 8) * part;
+    const char* vs = a.v_sf + pg * a.vs_sp + (int64_t)kvh * a.vs_sh + sl * a.vs_st + (FVB / 8) * part;
+    fk = *(const fk_t*)kd;
+    fv = *(const fv_t*)vd;
+    fks = FKB == 16 ? (uint32_t)*(const uint16_t*)ks : (uint32_t)*(const uint8_t*)ks;
+    fvs = FVB == 16 ? (uint32_t)*(const uint16_t*)vs : (uint32_t)*(const uint8_t*)vs;
+  };
+  // Converts the loaded rows and writes them as bf16: dword i of the part is the 16-byte
+  // chunk (FKB / 4) * part + i of the row, at chunk position chunk ^ swizzle(row).
+  auto fp4_store = [&](auto slot_c, int vo) {
+    const int row = my_row + (lane >> 4);
+    const int part = lane & 15;
+    auto chunk8 = [&](uint32_t w, float bs) {
+      float e[8];
+      fp4x8_to_f32(w, e);
+      u32x4_t pk;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pk[u] = pack_bf16(e[2 * u] * bs, e[2 * u + 1] * bs);
+      return pk;
+    };
+    float kbs[2], vbs[2];
+    kbs[0] = fp8_to_f32<0>(fks);
+    kbs[1] = fp8_to_f32<1>(fks);
+    vbs[0] = fp8_to_f32<0>(fvs);
+    vbs[1] = fp8_to_f32<1>(fvs);
+    uint16_t* kd = k_buf(slot_c) + row * DQK;
+#pragma unroll
+    for (int i = 0; i < FKB / 4; ++i) {
+      const int c = (FKB / 4) * part + i;
+      *(u32x4_t*)(kd + 8 * (c ^ k_swz(row))) = chunk8(fk[i], kbs[i >> 1]);
+    }
+    uint16_t* vd = v_lds + vo + row * DVO;
+#pragma unroll
+    for (int i = 0; i < FVB / 4; ++i) {
+      const int c = (FVB / 4) * part + i;
+      *(u32x4_t*)(vd + 8 * (c ^ v_swz(row))) = chunk8(fv[i], vbs[i >> 1]);
+    }
+    // The writes complete before this wave reaches the barrier that hands the stage over.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  };
+
   // Copies stage st: K into buffer slot_c, V into v_lds + vo.
   auto copy_stage = [&](int st, auto slot_c, int vo) {
-    if constexpr (PM == kPagesStage) {
+    if constexpr (FP4) {
+      fp4_load(st);
+    } else if constexpr (PM == kPagesStage) {
       copy_prep(st);
       static_for<NCOPY>([&](auto idx_c) { copy_one(idx_c, slot_c, vo); });
     } else {
@@ -370,7 +441,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   // the MFMAs run; the second group issues none (as bursts at the interval start they stall
   // the issuing waves).  Other page sizes: every wave copies its own rows at the interval
   // start.
-  constexpr bool SPREAD = PM == kPagesStage;
+  constexpr bool SPREAD = PM == kPagesStage && !FP4;
   // ---- S^T = K Q^T from K buffer kslot_c into s0 (keys 0..15) and s1 (keys 16..31); lane
   // holds keys 4*g4 + i.  With COPY the next stage's copies (K into the other buffer, V into
   // v_lds + vo_next) are issued among the steps.
@@ -516,7 +587,10 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   // copies of stage st + 1 refill.
   const bool second = w >= NW / 2;
   int vo_prev = 2 * VSTAGE, vo_cur = 0, vo_next = VSTAGE;
-  if (st_first < st_end) copy_stage(st_first, std::integral_constant<int, 0>{}, 0);
+  if (st_first < st_end) {
+    copy_stage(st_first, std::integral_constant<int, 0>{}, 0);
+    if constexpr (FP4) fp4_store(std::integral_constant<int, 0>{}, 0);
+  }
   auto interval = [&](int st, auto kslot_c, auto second_c) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
@@ -544,6 +618,9 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
       softmax(st);
       pv(vo_cur);
     }
+    if constexpr (FP4) {
+      if (has_next) fp4_store(other_c, vo_next);
+    }
     const int t = vo_prev;
     vo_prev = vo_cur;
     vo_cur = vo_next;
@@ -570,7 +647,8 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   const float l_tot = sum_xor32(sum_xor16(l_run));
   const float l_bf_tot = sum_xor32(sum_xor16(l_bf));
   if (!row_valid) return;
-  const float inv = l_bf_tot > 0.f ? 1.f / l_bf_tot : 0.f;
+  float inv = l_bf_tot > 0.f ? 1.f / l_bf_tot : 0.f;
+  if constexpr (FP4) inv *= a.v_scale;
   if (it.slot >= 0) {
     // One key chunk of a split tile: its normalised output and two log-sum-exps, over the
     // bf16-rounded weights (the merge weights, so the merged output is normalised by the
@@ -669,10 +747,11 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeArgs a) 
 }
 
 template <int DQK, int DVO>
-static void launch_prefill(const PrefillArgs& a, int pm, int grid, hipStream_t s) {
-  if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage><<<grid, 512, 0, s>>>(a);
-  else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2><<<grid, 512, 0, s>>>(a);
-  else prefill_kernel<DQK, DVO, kPagesAny><<<grid, 512, 0, s>>>(a);
+static void launch_prefill(const PrefillArgs& a, int pm, bool fp4, int grid, hipStream_t s) {
+  if (fp4) prefill_kernel<DQK, DVO, kPagesAny, true><<<grid, 512, 0, s>>>(a);
+  else if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, false><<<grid, 512, 0, s>>>(a);
+  else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2, false><<<grid, 512, 0, s>>>(a);
+  else prefill_kernel<DQK, DVO, kPagesAny, false><<<grid, 512, 0, s>>>(a);
 }
 
 }  // namespace pa
@@ -685,7 +764,9 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
                                       void* workspace, size_t workspace_bytes, void* stream) {
   pa_status st = check_cache(cache, true);
   if (st != PA_OK) return st;
-  if (cache->kv_dtype != PA_DTYPE_BF16) return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 KV only");
+  if (cache->kv_dtype != PA_DTYPE_BF16 && cache->kv_dtype != PA_DTYPE_NVFP4)
+    return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 and nvfp4 KV");
+  const bool fp4 = cache->kv_dtype == PA_DTYPE_NVFP4;
   if ((st = check_params(params, cache, kMaxPrefillGroup)) != PA_OK) return st;
   if ((st = check_plan_matches(plan, 2, params, cache, table, workspace_bytes)) != PA_OK) return st;
   if (plan->num_items == 0) return PA_OK;
@@ -699,8 +780,14 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   a.q = (const uint16_t*)q;
   a.k = (const char*)cache->k;
   a.v = (const char*)cache->v;
-  a.k_sp = 2 * cache->k_stride_page; a.k_sh = 2 * cache->k_stride_head; a.k_st = 2 * cache->k_stride_token;
-  a.v_sp = 2 * cache->v_stride_page; a.v_sh = 2 * cache->v_stride_head; a.v_st = 2 * cache->v_stride_token;
+  const int64_t unit = fp4 ? 1 : 2;  // bytes per stride unit
+  a.k_sp = unit * cache->k_stride_page; a.k_sh = unit * cache->k_stride_head; a.k_st = unit * cache->k_stride_token;
+  a.v_sp = unit * cache->v_stride_page; a.v_sh = unit * cache->v_stride_head; a.v_st = unit * cache->v_stride_token;
+  a.k_sf = (const char*)cache->k_sf;
+  a.v_sf = (const char*)cache->v_sf;
+  a.ks_sp = cache->k_sf_stride_page; a.ks_sh = cache->k_sf_stride_head; a.ks_st = cache->k_sf_stride_token;
+  a.vs_sp = cache->v_sf_stride_page; a.vs_sh = cache->v_sf_stride_head; a.vs_st = cache->v_sf_stride_token;
+  a.v_scale = fp4 ? cache->v_scale : 1.f;
   a.kv_indptr = table->kv_indptr;
   a.kv_indices = table->kv_indices;
   a.items = (const PrefillItem*)(ws + plan->items_offset);
@@ -716,7 +803,7 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   a.window = params->window > 0 ? params->window : 0;
   a.causal = params->causal ? 1 : 0;
   a.out_fp32 = params->out_dtype == PA_DTYPE_FP32;
-  a.scale_log2 = params->sm_scale * kLog2e;
+  a.scale_log2 = params->sm_scale * (fp4 ? cache->k_scale : 1.f) * kLog2e;
   const int grid = plan->num_items * cache->num_kv_heads;
   hipStream_t s = (hipStream_t)stream;
   const int dqk = cache->head_dim_qk, dvo = cache->head_dim_vo;
@@ -729,9 +816,9 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   const int pm = P % kKeyStage == 0 && page_fits_u32
                      ? kPagesStage
                      : ((P & (P - 1)) == 0 ? kPagesPow2 : kPagesAny);
-  if (dqk == 512 && dvo == 512) launch_prefill<512, 512>(a, pm, grid, s);
-  else if (dqk == 256 && dvo == 256) launch_prefill<256, 256>(a, pm, grid, s);
-  else launch_prefill<512, 256>(a, pm, grid, s);
+  if (dqk == 512 && dvo == 512) launch_prefill<512, 512>(a, pm, fp4, grid, s);
+  else if (dqk == 256 && dvo == 256) launch_prefill<256, 256>(a, pm, fp4, grid, s);
+  else launch_prefill<512, 256>(a, pm, fp4, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
   count_launches(1);

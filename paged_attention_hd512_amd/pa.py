@@ -370,13 +370,13 @@ class PagedPrefill:
 
     def __init__(self, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_len,
                  num_qo_heads, *, kv_dtype="bf16", k_scale=1.0, v_scale=1.0, sm_scale=None,
-                 window=0, causal=True, out_dtype="bf16"):
+                 window=0, causal=True, out_dtype="bf16", k_sf=None, v_sf=None):
         torch = _torch()
         dev = k_pool.device
-        self.cache = cache_from_pools(k_pool, v_pool, kv_dtype, k_scale, v_scale)
-        self._keep = (k_pool, v_pool)
+        self.cache = cache_from_pools(k_pool, v_pool, kv_dtype, k_scale, v_scale, k_sf, v_sf)
+        self._keep = (k_pool, v_pool, k_sf, v_sf)
         self.params = pa_attn_params(num_qo_heads, sm_scale if sm_scale is not None
-                                     else 1.0 / float(k_pool.shape[3]) ** 0.5,
+                                     else 1.0 / float(self.cache.head_dim_qk) ** 0.5,
                                      window, 1 if causal else 0, PA_DTYPE_BF16,
                                      out_dtype_code(out_dtype))
         self.out_dtype = out_dtype

@@ -353,6 +353,10 @@ WORKLOADS = {
     "causal_prefill": dict(kind="prefill", batch=4, qo_len=4096, prefix=1024,
                            num_qo_heads=16, num_kv_heads=8, head_dim_qk=512, page_size=64,
                            variants=[512, 256], seed=1005),
+    # The NVFP4 page's shape: asymmetric qk 512 / vo 256 prefill over an NVFP4 cache.
+    "nvfp4_prefill": dict(kind="prefill", batch=4, qo_len=4096, prefix=1024,
+                          num_qo_heads=16, num_kv_heads=8, head_dim_qk=512, page_size=64,
+                          kv_dtype="nvfp4", variants=[256], seed=1008),
     # Short-query extend (a few new tokens over a long cached prefix): the split-K prefill
     # geometry; HBM-bound.
     "extend_prefill": dict(kind="prefill", batch=8, qo_len=16, prefix=16368,

@@ -90,6 +90,7 @@ def oracle_decode(case, requests=None):
 
 
 def oracle_prefill(case, tokens=None, requests=None):
+    scales = dict(k_scale=case.k_scale, v_scale=case.v_scale)
     if requests is None:
         kp = pool_to_np(case.k_pool, case.kv_dtype)
         vp = pool_to_np(case.v_pool, case.kv_dtype)
@@ -97,14 +98,16 @@ def oracle_prefill(case, tokens=None, requests=None):
         return oracle.prefill_ref(q, case.qo_indptr, kp, vp, case.kv_indptr, case.kv_indices,
                                   case.kv_last_page_len, case.page_size, case.sm_scale,
                                   causal=case.causal, window=case.window,
-                                  kv_dtype=case.kv_dtype, tokens=tokens)
+                                  kv_dtype=case.kv_dtype, tokens=tokens, **scales,
+                                  **_scales_np(dict(k_sf=case.k_sf, v_sf=case.v_sf)))
     sub = extract_requests(case, requests)
     q = oracle.bf16_bits_to_f64(bf16_to_np(sub["q"]))
     return oracle.prefill_ref(q, sub["qo_indptr"], pool_to_np(sub["k_pool"], case.kv_dtype),
                               pool_to_np(sub["v_pool"], case.kv_dtype), sub["kv_indptr"],
                               sub["kv_indices"], sub["kv_last_page_len"], case.page_size,
                               case.sm_scale, causal=case.causal, window=case.window,
-                              kv_dtype=case.kv_dtype, tokens=tokens)
+                              kv_dtype=case.kv_dtype, tokens=tokens, **scales,
+                              **_scales_np(sub))
 
 
 def gpu_decode(case, num_splits=None, out_dtype=None, with_lse=True):
@@ -126,7 +129,7 @@ def gpu_prefill(case, out_dtype=None):
                           case.kv_indices, case.kv_last_page_len, case.num_qo_heads,
                           kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale,
                           sm_scale=case.sm_scale, window=case.window, causal=case.causal,
-                          out_dtype=out_dtype or case.out_dtype)
+                          out_dtype=out_dtype or case.out_dtype, k_sf=case.k_sf, v_sf=case.v_sf)
     out, lse = runner.run(case.q)
     torch.cuda.synchronize()
     return runner, out, lse

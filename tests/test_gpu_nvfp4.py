@@ -98,3 +98,75 @@ def test_full_size_nvfp4_workload_on_sampled_requests():
     compare(f"nvfp4_decode requests {sample}", out_to_np(o[sample]), ref,
             lse[sample].cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
     assert torch.isfinite(o.float()).all()
+
+
+# --------------------------------------------------------------------------- prefill
+
+from synth import make_prefill_case, prefill_workload  # noqa: E402
+from parity import oracle_prefill, gpu_prefill  # noqa: E402
+
+NVFP4_PREFILL_SWEEP = [
+    # qo_lens, kv_lens, hq, hkv, dqk, dvo, page, causal, window, out
+    ([40, 7], [100, 7], 4, 2, 512, 256, 16, True, 0, "fp32"),
+    ([130, 64, 1], [300, 64, 1], 16, 8, 512, 256, 1, True, 0, "bf16"),
+    ([200, 33], [1100, 40], 6, 2, 512, 256, 3, True, 100, "fp32"),
+    ([130, 64], [300, 64], 16, 8, 256, 256, 64, True, 0, "bf16"),
+    ([77, 5], [77, 9], 8, 1, 512, 512, 16, False, 0, "fp32"),
+    ([64, 0, 65], [64, 10, 200], 3, 1, 512, 512, 64, True, 0, "fp32"),
+    # short queries over long KV: the split-K prefill (key chunks merged per tile)
+    ([3, 1, 16], [3000, 5000, 2100], 4, 2, 512, 256, 64, True, 0, "fp32"),
+    ([16] * 4, [6000] * 4, 16, 8, 512, 256, 16, True, 0, "bf16"),
+    ([8, 8], [9000, 9000], 4, 2, 512, 256, 32, True, 3000, "fp32"),
+]
+
+
+@pytest.mark.parametrize("qo,kv,hq,hkv,dqk,dvo,page,causal,window,out", NVFP4_PREFILL_SWEEP)
+def test_nvfp4_prefill_sweep(qo, kv, hq, hkv, dqk, dvo, page, causal, window, out):
+    name = (f"nvfp4 prefill qo={qo} kv={kv} heads={hq}/{hkv} dims={dqk}/{dvo} page={page} "
+            f"causal={causal} window={window} out={out}")
+    say(name)
+    c = make_prefill_case(qo, kv, hq, hkv, dqk, page, head_dim_vo=dvo, causal=causal,
+                          window=window, out_dtype=out, kv_dtype="nvfp4", seed=sum(qo) + hq + 7,
+                          device=dev())
+    _, o, lse = gpu_prefill(c)
+    ref, ref_lse = oracle_prefill(c)
+    compare(name, out_to_np(o), ref, lse.cpu().numpy(), ref_lse, out_dtype=out)
+
+
+def test_split_nvfp4_prefill_of_one_token_equals_unsplit_decode():
+    """The geometry of the page's split-KV report (a short query over a long NVFP4 cache):
+    the prefill splits each tile's keys into chunks and merges them; the decode of the
+    same query token over the same cache, unsplit, must agree with it and with the oracle."""
+    from synth import make_decode_case
+    lens = [6000, 9000, 700]
+    d = make_decode_case(lens, 8, 2, 512, 64, head_dim_vo=256, kv_dtype="nvfp4", num_splits=1,
+                         out_dtype="fp32", seed=44, device=dev())
+    say("nvfp4 split prefill (q_len 1) vs unsplit decode")
+    from paged_attention_hd512_amd import PagedPrefill
+    qo_indptr = np.arange(len(lens) + 1, dtype=np.int32)
+    pre = PagedPrefill(d.k_pool, d.v_pool, qo_indptr, d.kv_indptr, d.kv_indices,
+                       d.kv_last_page_len, d.num_qo_heads, kv_dtype="nvfp4", k_scale=d.k_scale,
+                       v_scale=d.v_scale, sm_scale=d.sm_scale, causal=True, out_dtype="fp32",
+                       k_sf=d.k_sf, v_sf=d.v_sf)
+    assert pre.plan.num_merges > 0  # the split path runs
+    po, pl = pre.run(d.q.contiguous())
+    _, do, dl = gpu_decode(d)
+    ref, ref_lse = oracle_decode(d)
+    compare("nvfp4 split prefill", out_to_np(po), ref, pl.cpu().numpy(), ref_lse)
+    compare("nvfp4 unsplit decode", out_to_np(do), ref, dl.cpu().numpy(), ref_lse)
+    assert np.abs(out_to_np(po) - out_to_np(do)).max() < 2e-3
+
+
+@pytest.mark.slow
+def test_full_size_nvfp4_prefill_on_sampled_rows():
+    say("full-size nvfp4_prefill (qk 512, vo 256)")
+    c = prefill_workload("nvfp4_prefill", device=dev(), head_dim_vo=256)
+    _, o, lse = gpu_prefill(c)
+    # The oracle runs one row per request at the start, middle and end of its new tokens.
+    tokens = []
+    for b in range(c.batch):
+        q0, q1 = int(c.qo_indptr[b]), int(c.qo_indptr[b + 1])
+        tokens += [q0, (q0 + q1) // 2, q1 - 1]
+    ref, ref_lse = oracle_prefill(c, tokens=tokens)
+    compare("nvfp4_prefill sampled rows", out_to_np(o[tokens]), ref,
+            lse[tokens].cpu().numpy(), ref_lse, out_dtype=c.out_dtype)

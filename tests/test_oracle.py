@@ -572,3 +572,28 @@ def test_planted_nibble_swap_is_caught():
     right = oracle.nvfp4_values(packed, np.array([[0x38]], np.uint8))
     wrong = oracle.nvfp4_values(swapped, np.array([[0x38]], np.uint8))
     assert right[0, 0] == 0.5 and wrong[0, 0] != 0.5
+
+
+def test_nvfp4_prefill_rows_equal_decode_on_truncated_kv():
+    """Row i of an NVFP4 prefill is the decode of a request cut after its position, read
+    through the same pages and block scales (to fp64 rounding of the products)."""
+    from synth import make_prefill_case
+    c = make_prefill_case([5, 3], [21, 40], 4, 2, 32, 8, kv_dtype="nvfp4", seed=9)
+    q = bf16_bits_to_f64(c.q.view(torch.int16).numpy().view(np.uint16))
+    arrs = [t.contiguous().numpy() for t in (c.k_pool, c.v_pool, c.k_sf, c.v_sf)]
+    kw = dict(kv_dtype="nvfp4", k_scale=c.k_scale, v_scale=c.v_scale, k_sf=arrs[2], v_sf=arrs[3])
+    o, lse = prefill_ref(q, c.qo_indptr, arrs[0], arrs[1], c.kv_indptr, c.kv_indices,
+                         c.kv_last_page_len, c.page_size, c.sm_scale, **kw)
+    for b in range(c.batch):
+        q_len, L = int(c.qo_lens[b]), int(c.kv_lens[b])
+        for i in range(q_len):
+            pos = L - q_len + i
+            n_pages = pos // c.page_size + 1
+            ip = np.array([0, n_pages], np.int32)
+            idx = c.kv_indices[c.kv_indptr[b]:c.kv_indptr[b] + n_pages]
+            last = np.array([pos % c.page_size + 1], np.int32)
+            row = int(c.qo_indptr[b]) + i
+            od, ld = decode_ref(q[row][None], arrs[0], arrs[1], ip, idx, last, c.page_size,
+                                c.sm_scale, **kw)
+            assert np.allclose(o[row], od[0], rtol=0, atol=1e-12)
+            assert np.abs(lse[row] - ld[0]).max() < 1e-12
