@@ -174,8 +174,9 @@ def time_prefill(case, steps, warmup):
 
     run = PagedPrefill(case.k_pool, case.v_pool, case.qo_indptr, case.kv_indptr,
                        case.kv_indices, case.kv_last_page_len, case.num_qo_heads,
-                       kv_dtype=case.kv_dtype, sm_scale=case.sm_scale, window=case.window,
-                       causal=case.causal, out_dtype=case.out_dtype)
+                       kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale,
+                       sm_scale=case.sm_scale, window=case.window, causal=case.causal,
+                       out_dtype=case.out_dtype, k_sf=case.k_sf, v_sf=case.v_sf)
     out, lse = run.run(case.q)
     stream = torch.cuda.current_stream()
     sh = pa.current_stream_handle()
@@ -266,8 +267,16 @@ def oracle_prefill_baseline(case, budget_s=12.0):
 
     threads = cpu_threads()
     dt = torch.int16
-    kp = case.k_pool.contiguous().cpu().view(dt).numpy().view(np.uint16)
-    vp = case.v_pool.contiguous().cpu().view(dt).numpy().view(np.uint16)
+    extra = {}
+    if case.kv_dtype == "nvfp4":
+        kp = case.k_pool.contiguous().cpu().numpy()
+        vp = case.v_pool.contiguous().cpu().numpy()
+        extra = dict(kv_dtype="nvfp4", k_scale=case.k_scale, v_scale=case.v_scale,
+                     k_sf=case.k_sf.contiguous().cpu().numpy(),
+                     v_sf=case.v_sf.contiguous().cpu().numpy())
+    else:
+        kp = case.k_pool.contiguous().cpu().view(dt).numpy().view(np.uint16)
+        vp = case.v_pool.contiguous().cpu().view(dt).numpy().view(np.uint16)
     q = oracle.bf16_bits_to_f64(case.q.contiguous().cpu().view(dt).numpy().view(np.uint16))
     flops, spent, rows = 0, 0.0, 0
     with threadpool_limits(limits=threads):
@@ -278,7 +287,7 @@ def oracle_prefill_baseline(case, budget_s=12.0):
             t0 = time.perf_counter()
             oracle.prefill_ref(q, case.qo_indptr, kp, vp, case.kv_indptr, case.kv_indices,
                                case.kv_last_page_len, case.page_size, case.sm_scale,
-                               causal=case.causal, window=case.window, tokens=toks)
+                               causal=case.causal, window=case.window, tokens=toks, **extra)
             spent += time.perf_counter() - t0
             L = int(case.kv_lens[0])
             for i in toks:
@@ -408,7 +417,8 @@ def main():
     ap.add_argument("--workload", default="gqa_decode",
                     help="gqa_decode | gqa_decode_splitk8 | fp8_decode | nvfp4_decode | "
                          "window_decode_d512_p1 | ... | "
-                         "causal_prefill_vo512 | causal_prefill_vo256 | extend_prefill")
+                         "causal_prefill_vo512 | causal_prefill_vo256 | nvfp4_prefill | "
+                         "extend_prefill")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -435,6 +445,8 @@ def main():
                                    int(wl[len("causal_prefill_vo"):]))
         if wl == "extend_prefill":
             return measure_extend(wl, args.steps, args.warmup)
+        if wl == "nvfp4_prefill":
+            return measure_prefill(wl, args.steps, args.warmup, 256)
         if wl.startswith("gqa_decode_splitk"):
             return measure_decode("gqa_decode", args.steps, args.warmup,
                                   wl[len("gqa_decode_"):])
@@ -481,7 +493,7 @@ def main():
                  "window_decode_d512_p1",
                  "window_decode_d512_p32",
                  "window_decode_d256_p1", "window_decode_d256_p32", "causal_prefill_vo512",
-                 "causal_prefill_vo256", "extend_prefill"]
+                 "causal_prefill_vo256", "nvfp4_prefill", "extend_prefill"]
         for wl in names:
             if wl == args.workload:
                 continue

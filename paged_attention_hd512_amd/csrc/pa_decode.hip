@@ -173,26 +173,28 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
         for (int l = 0; l < NKL; ++l) kbuf[l] = __builtin_nontemporal_load((const u32x4_t*)(base + 64 * l));
       }
     };
+    // Row byte offsets are formed on the vector ALU, lane n for key n of the block (all
+    // sixteen at once), and each row's load takes its offset by v_readlane (or a lane
+    // shuffle when two rows share an instruction): per-row 64-bit address arithmetic on the
+    // scalar unit, which the CU's waves share, would serialise them.
     auto issue_v = [&](int32_t page, int32_t slot) {
+      const int64_t voff = (row_elem_offset(page, 0, slot, a.v_sp, 0, a.v_st) + v_head) * UNIT;
+      int64_t vsoff = 0;
+      if constexpr (KV == kKvFp4) vsoff = row_elem_offset(page, 0, slot, a.vs_sp, 0, a.vs_st) + vs_head;
 #pragma unroll
       for (int i = 0; i < NVL; ++i) {
         const int src = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
-        int32_t pv, sv;
+        int64_t off, soff = 0;
         if constexpr (RPI == 1) {
-          pv = __builtin_amdgcn_readlane(page, src);
-          sv = __builtin_amdgcn_readlane(slot, src);
+          off = readlane_i64(voff, src);
+          if constexpr (KV == kKvFp4) soff = readlane_i64(vsoff, src);
         } else {
-          pv = shfl_i(page, src);
-          sv = shfl_i(slot, src);
+          off = shfl_i64(voff, src);
+          if constexpr (KV == kKvFp4) soff = shfl_i64(vsoff, src);
         }
-        const char* base = a.v + (row_elem_offset(pv, 0, sv, a.v_sp, 0, a.v_st) + v_head) * UNIT +
-                           (lane % LPR) * VB8;
-        vbuf[i] = __builtin_nontemporal_load((const vload_t*)base);
-        if constexpr (KV == kKvFp4) {
-          const char* sf = a.v_sf + row_elem_offset(pv, 0, sv, a.vs_sp, 0, a.vs_st) + vs_head +
-                           (lane % LPR) / 2;
-          vsf[i] = __builtin_nontemporal_load((const uint8_t*)sf);
-        }
+        vbuf[i] = __builtin_nontemporal_load((const vload_t*)(a.v + off + (lane % LPR) * VB8));
+        if constexpr (KV == kKvFp4)
+          vsf[i] = __builtin_nontemporal_load((const uint8_t*)(a.v_sf + soff + (lane % LPR) / 2));
       }
     };
     // P V of one block: rescale the accumulators by the block's alpha, then add p * V with

@@ -176,5 +176,16 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
 __device__ __forceinline__ int shfl_i(int v, int src_lane) {
   return __builtin_amdgcn_ds_bpermute(src_lane << 2, v);
 }
+__device__ __forceinline__ int64_t shfl_i64(int64_t v, int src_lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+// The value of v in lane src (wave-uniform src), as a scalar.
+__device__ __forceinline__ int64_t readlane_i64(int64_t v, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)((uint64_t)v >> 32), src);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 }  // namespace pa
