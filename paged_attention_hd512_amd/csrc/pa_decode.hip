@@ -33,10 +33,15 @@
 // request 3684, sections "Summary" and "NVFP4 split-KV correctness (added)"): each lane
 // reads its keys' packed E2M1 bytes and their E4M3 block scales (one per 16 head_dim
 // elements, from a tensor of their own addressed through the same page table), converts
-// the nibbles to fp32 and multiplies by the block scale.  For keys the product goes to
-// bf16 exactly (an E2M1 value times an E4M3 value has at most 6 significant bits); for
-// values the block scale multiplies the probability instead, one product per head rather
-// than one per element.  The global k_scale / v_scale apply as for FP8.
+// the nibbles and multiplies by the block scale.  Keys go through the fp16 MFMA: nibbles
+// to fp16 pairs (v_cvt_scalef32_pk_f16_fp4 at scale 1) times the block scale in fp16
+// (v_pk_mul_f16), exact since an E2M1 value times an E4M3 value has at most 6 significant
+// bits and lies in [2^-10, 2688]; Q is staged in fp16, each segment's rows scaled by the
+// power of two that brings their largest magnitude just below 2^15, so every bf16 query
+// element converts exactly (short of 2^-29 of that largest one) and none overflows, and
+// the factor comes back out of the score scale.  For values the nibbles go to fp32 and
+// the block scale multiplies the probability, one product per head rather than one per
+// element.  The global k_scale / v_scale apply as for FP8.
 
 #include <hip/hip_runtime.h>
 
@@ -259,6 +264,28 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
     int32_t page_c, slot_c;
     block_page(blk, page_c, slot_c);
     issue_k(page_c, slot_c);
+    float seg_scale = a.scale_log2;  // log2-domain factor of the raw scores
+    if constexpr (KV == kKvFp4) {
+      // Q to fp16, scaled by 2^sh so that max |q| lies in [2^14, 2^15).
+      float qm = 0.f;
+#pragma unroll
+      for (int r = 0; r < QV; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          qm = fmaxf(qm, fmaxf(fabsf(bf16_lo(qv_pre[r][e])), fabsf(bf16_hi(qv_pre[r][e]))));
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) qm = fmaxf(qm, shfl_xor_f(qm, o));
+      int ex = 0;
+      frexpf(qm, &ex);  // qm < 2^ex
+      const int sh = qm > 0.f ? min(max(15 - ex, -126), 126) : 0;
+      const float up = __builtin_ldexpf(1.f, sh);
+      seg_scale = a.scale_log2 * __builtin_ldexpf(1.f, -sh);
+#pragma unroll
+      for (int r = 0; r < QV; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          qv_pre[r][e] = pack_f16(bf16_lo(qv_pre[r][e]) * up, bf16_hi(qv_pre[r][e]) * up);
+    }
 #pragma unroll
     for (int r = 0; r < QV; ++r) {
       const int idx = lane + 64 * r;
@@ -299,17 +326,15 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
       }
 #pragma unroll
       for (int j = 0; j < NSTEP; ++j) {
+        if constexpr (KV == kKvFp4) {
+          const f16x8_t kf = fp4x8_to_f16_scaled(kbuf[j >> 2][j & 3], (_Float16)kbs[j >> 1]);
+          const u32x4_t qv = *(const u32x4_t*)(q_lds + qrow * QPITCH + q_dim_of_step<KV, DQK>(j, g4));
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, __builtin_bit_cast(f16x8_t, qv), s, 0, 0, 0);
+          continue;
+        }
         bf16x8_t kf;
         if constexpr (KV == kKvBf16) {
           kf = __builtin_bit_cast(bf16x8_t, kbuf[j]);
-        } else if constexpr (KV == kKvFp4) {
-          float e[8];
-          fp4x8_to_f32(kbuf[j >> 2][j & 3], e);
-          const float bs = kbs[j >> 1];
-          u32x4_t packed;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) packed[u] = pack_bf16(e[2 * u] * bs, e[2 * u + 1] * bs);
-          kf = __builtin_bit_cast(bf16x8_t, packed);
         } else {
           const u32x4_t raw = kbuf[j >> 1];
           const u32x2_t lo = fp8x4_to_bf16x4(raw[(j & 1) * 2 + 0]);
@@ -329,7 +354,7 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = blk * 16 + 4 * g4 + i;
-        sc[i] = (t >= t0 && t < t1) ? s[i] * a.scale_log2 : -INFINITY;
+        sc[i] = (t >= t0 && t < t1) ? s[i] * seg_scale : -INFINITY;
         mx = fmaxf(mx, sc[i]);
       }
       mx = max_xor16(mx);

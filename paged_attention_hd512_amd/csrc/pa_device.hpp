@@ -65,6 +65,27 @@ __device__ __forceinline__ void fp4x8_to_f32(uint32_t w, float* out) {
   out[4] = c[0]; out[5] = c[1]; out[6] = d[0]; out[7] = d[1];
 }
 
+// Eight E2M1 values (one dword, element 2i in the low nibble of byte i) times a block
+// scale, as eight fp16 values: the nibbles convert exactly at scale 1 and the products are
+// exact in fp16 when the scale is an E4M3 value (at most 6 significant bits, magnitudes in
+// [2^-10, 2688]).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8_t fp4x8_to_f16_scaled(uint32_t w, _Float16 bs) {
+  const f16x2_t s2 = {bs, bs};
+  const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  return f16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Two fp32 -> two fp16 in one dword, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // One FP8 E4M3FN code (byte `sel` of w) -> fp32, exact.
 template <int SEL>
 __device__ __forceinline__ float fp8_to_f32(uint32_t w) {

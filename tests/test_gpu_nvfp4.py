@@ -170,3 +170,73 @@ def test_full_size_nvfp4_prefill_on_sampled_rows():
     ref, ref_lse = oracle_prefill(c, tokens=tokens)
     compare("nvfp4_prefill sampled rows", out_to_np(o[tokens]), ref,
             lse[tokens].cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
+
+
+def _repad(t, extra):
+    """The same values in a new allocation whose rows are `extra` bytes longer: a strided
+    view with its own stride family."""
+    parent = torch.zeros(tuple(t.shape[:-1]) + (t.shape[-1] + extra,), dtype=t.dtype,
+                         device=t.device)
+    parent[..., :t.shape[-1]] = t
+    return parent[..., :t.shape[-1]]
+
+
+@pytest.mark.parametrize("dqk,dvo,page", [(512, 256, 16), (512, 512, 1), (256, 256, 64)])
+def test_nvfp4_pools_with_different_stride_families(dqk, dvo, page):
+    """K, V and their block-scale tensors in separate allocations with different row
+    paddings (the FlashInfer page's test of separately allocated K/V pools and scale
+    tensors with different strides): decode and prefill read each through its own
+    strides."""
+    say(f"nvfp4 padded pools dims={dqk}/{dvo} page={page}")
+    from synth import make_decode_case
+    d = make_decode_case([37, 300, 1000, 5], 8, 2, dqk, page, head_dim_vo=dvo, kv_dtype="nvfp4",
+                         out_dtype="fp32", num_splits=2, seed=51, device=dev())
+    d.k_pool, d.v_pool = _repad(d.k_pool, 16), _repad(d.v_pool, 48)
+    d.k_sf, d.v_sf = _repad(d.k_sf, 16), _repad(d.v_sf, 32)
+    d.cache = None
+    assert d.k_pool.stride(2) != d.v_pool.stride(2) and d.k_sf.stride(2) != d.v_sf.stride(2)
+    _, o, lse = gpu_decode(d)
+    ref, ref_lse = oracle_decode(d)
+    compare(f"nvfp4 padded decode {dqk}/{dvo}", out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
+    p = make_prefill_case([40, 3], [300, 900], 8, 2, dqk, page, head_dim_vo=dvo,
+                          kv_dtype="nvfp4", out_dtype="fp32", seed=52, device=dev())
+    p.k_pool, p.v_pool = _repad(p.k_pool, 48), _repad(p.v_pool, 16)
+    p.k_sf, p.v_sf = _repad(p.k_sf, 32), _repad(p.v_sf, 16)
+    p.cache = None
+    _, o, lse = gpu_prefill(p)
+    ref, ref_lse = oracle_prefill(p)
+    compare(f"nvfp4 padded prefill {dqk}/{dvo}", out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
+
+
+def test_nvfp4_decode_replays_from_a_graph():
+    say("nvfp4 decode in a captured graph")
+    from synth import make_decode_case
+    from paged_attention_hd512_amd import PagedDecode
+    c = make_decode_case([37, 300, 1024, 5000], 12, 4, 512, 64, kv_dtype="nvfp4", num_splits=0,
+                         seed=53, device=dev())
+    run = PagedDecode(c.k_pool, c.v_pool, c.kv_indptr, c.kv_indices, c.kv_last_page_len,
+                      c.num_qo_heads, kv_dtype="nvfp4", k_scale=c.k_scale, v_scale=c.v_scale,
+                      sm_scale=c.sm_scale, out_dtype=c.out_dtype, k_sf=c.k_sf, v_sf=c.v_sf)
+    q = c.q.clone()
+    out_g, lse_g = run.run(q)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run.run(q, out=out_g, lse=lse_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.run(q, out=out_g, lse=lse_g)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    for i in range(3):
+        q.copy_(torch.randn(c.q.shape, generator=gen).to(torch.bfloat16).to(q.device))
+        out_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        out_e, lse_e = run.run(q)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e) and torch.equal(lse_g, lse_e), f"replay {i}"
