@@ -192,7 +192,7 @@ def test_nvfp4_pools_with_different_stride_families(dqk, dvo, page):
     d = make_decode_case([37, 300, 1000, 5], 8, 2, dqk, page, head_dim_vo=dvo, kv_dtype="nvfp4",
                          out_dtype="fp32", num_splits=2, seed=51, device=dev())
     d.k_pool, d.v_pool = _repad(d.k_pool, 16), _repad(d.v_pool, 48)
-    d.k_sf, d.v_sf = _repad(d.k_sf, 16), _repad(d.v_sf, 32)
+    d.k_sf, d.v_sf = _repad(d.k_sf, 16), _repad(d.v_sf, 48)
     d.cache = None
     assert d.k_pool.stride(2) != d.v_pool.stride(2) and d.k_sf.stride(2) != d.v_sf.stride(2)
     _, o, lse = gpu_decode(d)
