@@ -21,6 +21,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -39,10 +40,15 @@ KERNEL_SOURCES = ["paged_attention_hd512_amd/csrc/pa_decode.hip",
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code: comments and whitespace are dropped, so editing a
+    comment does not mark counters taken on the same code as stale."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

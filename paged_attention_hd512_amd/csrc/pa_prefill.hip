@@ -11,18 +11,23 @@
 //
 // Work decomposition.  A tile is 128 query rows of one (request, KV head): the (token,
 // head) pairs of the head group, flattened token-major, so the G heads that share a KV
-// head share every K/V tile.  One workgroup of 4 waves runs a tile; each wave owns 32 rows.
-// Keys stream through LDS in tiles of 32 (K and V rows staged from their pages).  Per key
-// tile and wave, with v_mfma_f32_32x32x16_bf16:
-//   * S^T = K Q^T (keys on M, the wave's 32 rows on N, head_dim on K): A = K rows from LDS,
+// head share every K/V tile.  One workgroup of 8 waves runs a tile; each wave owns 16 rows.
+// Keys stream through LDS in stages of 32 (K double-buffered, V triple-buffered, filled by
+// direct-to-LDS copies from the pages).  Per stage and wave, with v_mfma_f32_16x16x32_bf16:
+//   * S^T = K Q^T (keys on M, the wave's 16 rows on N, head_dim on K): A = K rows from LDS,
 //     B = Q held in registers for the whole tile.  In the output layout every lane holds
-//     16 scores of one query row, so the online softmax of a row lives in one lane pair.
+//     8 scores of one query row, so the online softmax of a row lives in one lane group.
 //   * O^T += V^T P^T (head_dim on M, rows on N, keys on K): B = P straight from the score
 //     registers (same lane, same key order), A = V read transposed from LDS.  The O^T
 //     accumulators of a lane again all belong to its own row.
+//   * The two waves sharing a SIMD run the stage's phases in rotated order, so one's
+//     softmax overlaps the other's MFMAs.
 //   * The running max is only moved when a row's max grows by more than 2^8, so the
 //     accumulators are rescaled rarely; the final normalisation uses the same reference
 //     max, so the result is unchanged.
+// Every wave reads the whole K and V stage from LDS (64 KB at 512/512) for its 16 rows, so
+// a stage moves 512 KB of LDS reads per CU against 2048 MFMA clocks per SIMD: the LDS read
+// rate, not the MFMA rate, sets the stage time.
 // NVFP4 KV (the FlashInfer page, sections "Summary" and "What's in it": packed E2M1 with one
 // E4M3 block scale per 16 head_dim elements): a direct-to-LDS copy cannot convert, so each
 // wave loads its key rows' packed bytes and block scales into registers when a stage's copy
