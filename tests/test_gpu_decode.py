@@ -148,6 +148,22 @@ def test_waves_that_run_several_segments():
     compare("several segments per wave", out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
 
 
+def test_merges_of_more_than_64_segments():
+    """Long requests cut into well over 64 balanced segments (129, 130 and 71 with the
+    current planner): the merge reads the segments' log-sum-exps 64 at a time and their rows
+    8 at a time, so these counts take every path (whole chunks of 64, a partial chunk, a
+    tail shorter than 8 rows)."""
+    say("merges of more than 64 segments")
+    c = make_decode_case([16464, 9000], 12, 2, 512, 16, num_splits=0, out_dtype="fp32",
+                         seed=21, device=dev())
+    runner, o, lse = gpu_decode(c)
+    counts = pa.decode_merges(runner.plan, runner.plan_buf)[:, 3].tolist()
+    assert max(counts) > 128 and any(64 < x < 128 for x in counts)
+    assert any(x % 8 for x in counts)
+    ref, ref_lse = oracle_decode(c)
+    compare("more than 64 segments per merge", out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name,variant", [("gqa_decode", None), ("gqa_decode", "splitk8"),
                                           ("fp8_decode", None),
