@@ -104,9 +104,41 @@ def extend_algorithmic_bytes(case):
 
 # ----------------------------------------------------------------------------- timing
 
+def time_steps(launch, stream, steps):
+    """ms per step of `steps` back-to-back steps, from one pair of HIP events on the launch
+    stream around them (events recorded between the kernels would themselves add several
+    microseconds to every step), and the host wall-clock per step."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_kernels(launches, stream, steps):
+    """Average duration (ms) of each launch in `launches` over `steps` steps, from HIP events
+    recorded on the launch stream around every launch."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for j, f in enumerate(launches):
+            f()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    return [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j in range(len(launches))]
+
+
 def time_decode(case, steps, warmup):
-    """Returns (ms_per_step, partial_kernel_ms, merge_ms) measured with HIP events on the
-    stream the kernels run on."""
+    """Returns (ms_per_step, partial_kernel_ms, merge_ms, wall_ms, plan): the step time of
+    back-to-back decode steps, then the two kernels' durations from events around each."""
     import torch
     from paged_attention_hd512_amd import PagedDecode
     import paged_attention_hd512_amd.pa as pa
@@ -123,20 +155,9 @@ def time_decode(case, steps, warmup):
             lse.data_ptr(), run.workspace.data_ptr(), run.workspace.numel(), sh)
     for _ in range(warmup):
         pa.pa_paged_decode(*args)
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record(stream)
-        pa.pa_paged_decode_partial(*args)
-        ev[i][1].record(stream)
-        pa.pa_paged_decode_merge(*args)
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    part = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    merge = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-    step = ev[0][0].elapsed_time(ev[-1][2]) / steps
+    step, wall = time_steps(lambda: pa.pa_paged_decode(*args), stream, steps)
+    part, merge = time_kernels([lambda: pa.pa_paged_decode_partial(*args),
+                                lambda: pa.pa_paged_decode_merge(*args)], stream, steps)
     return max(step, 1e-9), part, merge, wall, run.plan
 
 
@@ -174,6 +195,8 @@ def time_decode_graph(case, steps, warmup):
 
 
 def time_prefill(case, steps, warmup):
+    """Returns (ms_per_step, kernel_ms, wall_ms, plan): back-to-back prefill steps, then the
+    duration of one step's launch(es) from events around it."""
     import torch
     from paged_attention_hd512_amd import PagedPrefill
     import paged_attention_hd512_amd.pa as pa
@@ -191,21 +214,10 @@ def time_prefill(case, steps, warmup):
             run.workspace.numel(), sh)
     for _ in range(warmup):
         pa.pa_paged_prefill(*args)
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record(stream)
-        pa.pa_paged_prefill(*args)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    kern = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    step = ev[0][0].elapsed_time(ev[-1][1]) / steps
+    step, wall = time_steps(lambda: pa.pa_paged_prefill(*args), stream, steps)
+    (kern,) = time_kernels([lambda: pa.pa_paged_prefill(*args)], stream, steps)
     return step, kern, wall, run.plan
 
-
-# ----------------------------------------------------------------------------- cpu baseline
 
 def cpu_threads():
     try:
