@@ -25,9 +25,9 @@
 //   * The running max is only moved when a row's max grows by more than 2^8, so the
 //     accumulators are rescaled rarely; the final normalisation uses the same reference
 //     max, so the result is unchanged.
-// Every wave reads the whole K and V stage from LDS (64 KB at 512/512) for its 16 rows, so
-// a stage moves 512 KB of LDS reads per CU against 2048 MFMA clocks per SIMD: the LDS read
-// rate, not the MFMA rate, sets the stage time.
+// Every wave reads the whole K and V stage from LDS (64 KB at 512/512) for its 16 rows: 1 KB
+// of LDS reads per 16-clock MFMA, so the MFMA pipes run only as fast as the LDS delivers
+// (256 B per clock per CU at most) and as its latency is hidden.
 // NVFP4 KV (the FlashInfer page, sections "Summary" and "What's in it": packed E2M1 with one
 // E4M3 block scale per 16 head_dim elements): a direct-to-LDS copy cannot convert, so each
 // wave loads its key rows' packed bytes and block scales into registers when a stage's copy
