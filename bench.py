@@ -34,22 +34,31 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "paged decode attn HBM GB/s (% peak) at hd512 GQA; prefill TFLOP/s"
-KERNEL_SOURCES = ["paged_attention_hd512_amd/csrc/pa_decode.hip",
-                  "paged_attention_hd512_amd/csrc/pa_prefill.hip",
-                  "paged_attention_hd512_amd/csrc/pa_device.hpp"]
+# Kernel sources per kernel family, for tying counter summaries to the code they were
+# taken on.
+KERNEL_SOURCES = {
+    "decode": ["paged_attention_hd512_amd/csrc/pa_decode.hip",
+               "paged_attention_hd512_amd/csrc/pa_device.hpp"],
+    "prefill": ["paged_attention_hd512_amd/csrc/pa_prefill.hip",
+                "paged_attention_hd512_amd/csrc/pa_device.hpp"],
+}
 
 
-def kernel_source_hash():
-    """Hash of the kernel sources' code: comments and whitespace are dropped, so editing a
-    comment does not mark counters taken on the same code as stale."""
+def kernel_source_hash(family):
+    """Hash of one kernel family's sources' code: comments and whitespace are dropped, so
+    editing a comment does not mark counters taken on the same code as stale."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, p)) as f:
             src = f.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
         src = re.sub(r"//[^\n]*", " ", src)
         h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_family(workload):
+    return "prefill" if "prefill" in workload else "decode"
 
 
 # ----------------------------------------------------------------------------- work counts
@@ -333,7 +342,7 @@ def traffic_for(workload):
     except (OSError, ValueError):
         return None
     ent = data.get(workload)
-    if not ent or ent.get("kernel_source_hash") != kernel_source_hash():
+    if not ent or ent.get("kernel_source_hash") != kernel_source_hash(kernel_family(workload)):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -489,7 +498,7 @@ def main():
             "head_dim_vo": case.head_dim_vo, "page_size": case.page_size, "causal": True},
         "roofline": main_res["roofline"],
         "wall_ms_per_step": round(main_res["wall_ms"], 5),
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": {f: kernel_source_hash(f) for f in KERNEL_SOURCES},
     }
     if "merge_ms" in main_res:
         line["merge_ms"] = round(main_res["merge_ms"], 5)
