@@ -212,7 +212,7 @@ pa_status pa_validate_page_table_host(const int32_t* kv_indptr_host,
  * the cuts).  Waves run longest first.  Call with plan_buf_host == NULL to
  * learn plan->plan_bytes (and plan->workspace_bytes); then call again with a buffer of
  * at least that size.
- * Supported: head dims (512,512), (256,256), (512,256); kv bf16 or FP8 E4M3FN;
+ * Supported: head dims (512,512), (256,256), (512,256); kv bf16, FP8 E4M3FN or NVFP4;
  * q bf16; out fp32 or bf16; 1 <= num_qo_heads / num_kv_heads <= 8; num_splits <= 64.
  * Never calls HIP. */
 pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
