@@ -89,6 +89,8 @@ SWEEP = [
     ([100, 200, 300], 4, 1, 256, 256, 8, "fp8", 0, 0, "bf16"),
     ([1, 2, 3, 1000], 16, 2, 512, 512, 16, "bf16", 1, 0, "fp32"),
     ([64, 128, 192], 40, 8, 512, 512, 16, "bf16", 0, 64, "bf16"),
+    ([300, 1000, 129, 256], 8, 2, 512, 512, 128, "bf16", 0, 0, "bf16"),
+    ([300, 1000, 129, 257], 12, 4, 512, 512, 256, "fp8", 500, 3, "fp32"),
 ]
 
 

@@ -29,6 +29,9 @@ SWEEP = [
     ([150], [150], 16, 1, 256, 256, 16, True, 17, "bf16"),
     ([64, 0, 65], [64, 10, 200], 3, 1, 512, 512, 64, True, 0, "fp32"),
     ([300], [2000], 2, 2, 512, 512, 64, True, 0, "bf16"),
+    # pages holding several 32-key stages (the one-lookup path steps within a page)
+    ([260, 70], [1000, 300], 4, 2, 512, 512, 128, True, 0, "fp32"),
+    ([129], [900], 8, 4, 512, 256, 256, True, 200, "bf16"),
     # short queries over long KV (split-K prefill: key chunks merged per tile)
     ([3, 1, 16], [3000, 5000, 2100], 4, 2, 512, 512, 64, True, 0, "fp32"),
     ([1, 40], [20000, 700], 8, 2, 512, 256, 16, False, 0, "bf16"),
