@@ -246,8 +246,9 @@ def cpu_model():
 
 
 def oracle_decode_baseline(case, budget_s=12.0):
-    """The oracle, as it stands, timed on requests of the same batch until the budget is
-    spent; throughput in algorithmic GB/s of the requests it finished."""
+    """The oracle, as it stands, timed on the requests of the same batch, pass after pass,
+    until the budget is spent; throughput in algorithmic GB/s of the requests it finished.
+    Each request's inputs are extracted once, outside the timed calls."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -255,10 +256,10 @@ def oracle_decode_baseline(case, budget_s=12.0):
     from synth import extract_requests
 
     threads = cpu_threads()
-    done, spent, nbytes = [], 0.0, 0
-    order = list(range(case.batch))
-    with threadpool_limits(limits=threads):
-        for b in order:
+    inputs = {}
+
+    def request_inputs(b):
+        if b not in inputs:
             sub = extract_requests(case, [b])
             dt = torch.int16 if case.kv_dtype == "bf16" else torch.uint8
             kp = sub["k_pool"].contiguous().view(dt).numpy()
@@ -269,21 +270,28 @@ def oracle_decode_baseline(case, budget_s=12.0):
             if case.kv_dtype == "nvfp4":
                 sf = {n: sub[n].contiguous().numpy() for n in ("k_sf", "v_sf")}
             q = oracle.bf16_bits_to_f64(sub["q"].contiguous().view(torch.int16).numpy().view(np.uint16))
-            t0 = time.perf_counter()
-            oracle.decode_ref(q, kp, vp, sub["kv_indptr"], sub["kv_indices"],
-                              sub["kv_last_page_len"], case.page_size, case.sm_scale,
-                              window=case.window, kv_dtype=case.kv_dtype,
-                              k_scale=case.k_scale, v_scale=case.v_scale, **sf)
-            spent += time.perf_counter() - t0
-            done.append(b)
-            if spent >= budget_s:
-                break
+            inputs[b] = (q, kp, vp, sub["kv_indptr"], sub["kv_indices"], sub["kv_last_page_len"], sf)
+        return inputs[b]
+
+    done, spent = [], 0.0
+    with threadpool_limits(limits=threads):
+        while spent < budget_s:
+            for b in range(case.batch):
+                q, kp, vp, ip, ix, la, sf = request_inputs(b)
+                t0 = time.perf_counter()
+                oracle.decode_ref(q, kp, vp, ip, ix, la, case.page_size, case.sm_scale,
+                                  window=case.window, kv_dtype=case.kv_dtype,
+                                  k_scale=case.k_scale, v_scale=case.v_scale, **sf)
+                spent += time.perf_counter() - t0
+                done.append(b)
+                if spent >= budget_s:
+                    break
     nbytes = decode_algorithmic_bytes(case, done)
+    passes = len(done) / case.batch
     return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{len(done)} of {case.batch} requests of the same batch "
-                      f"({sum(int(case.kv_lens[b]) for b in done)} keys), fp64 numpy on "
-                      f"{cpu_model()}, {spent:.1f} s"}
+            "sample": f"{len(done)} request decodes ({passes:.1f} passes over the {case.batch} "
+                      f"requests of the same batch), fp64 numpy on {cpu_model()}, {spent:.1f} s"}
 
 
 def oracle_prefill_baseline(case, budget_s=12.0):
