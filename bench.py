@@ -35,12 +35,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "paged decode attn HBM GB/s (% peak) at hd512 GQA; prefill TFLOP/s"
 # Kernel sources per kernel family, for tying counter summaries to the code they were
-# taken on.
+# taken on; the host planner decides the kernels' work split, so it counts too.
+_SHARED_SOURCES = ["paged_attention_hd512_amd/csrc/pa_device.hpp",
+                   "paged_attention_hd512_amd/csrc/pa_internal.hpp",
+                   "paged_attention_hd512_amd/csrc/pa_host.cpp"]
 KERNEL_SOURCES = {
-    "decode": ["paged_attention_hd512_amd/csrc/pa_decode.hip",
-               "paged_attention_hd512_amd/csrc/pa_device.hpp"],
-    "prefill": ["paged_attention_hd512_amd/csrc/pa_prefill.hip",
-                "paged_attention_hd512_amd/csrc/pa_device.hpp"],
+    "decode": ["paged_attention_hd512_amd/csrc/pa_decode.hip"] + _SHARED_SOURCES,
+    "prefill": ["paged_attention_hd512_amd/csrc/pa_prefill.hip"] + _SHARED_SOURCES,
 }
 
 

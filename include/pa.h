@@ -203,8 +203,9 @@ pa_status pa_validate_page_table_host(const int32_t* kv_indptr_host,
  * copies passed to pa_paged_decode must hold the same values).  The work is the set of
  * (request, kv head, 16-token key block) units; each wave of the partial kernel runs one
  * piece of them: the units, flattened in (request, kv head, block) order, are cut into
- * min(2048, ceil(units / 8)) equal pieces, i.e. one wave per SIMD slot of the 256 CUs at
- * two waves per SIMD, so every wave streams the same number of bytes.  A piece is cut at
+ * P near-equal pieces, at most one wave per SIMD slot of the 256 CUs at two waves per SIMD
+ * (2048): with P0 = min(2048, ceil(units / 8)) and m = ceil(units / P0) the largest piece,
+ * P = ceil(units / m), so (nearly) every wave streams m blocks.  A piece is cut at
  * (request, kv head) boundaries into segments.  num_splits S > 0 (split-K S) also cuts
  * each (request, kv head) at the boundaries of its min(S, blocks) near-equal chunks, so
  * every chunk is computed by whole segments; S == 0 adds no cuts.  A (request, kv head)

@@ -16,8 +16,9 @@ Decode rule (units of 16-token logical blocks, block j = tokens [16j, 16j+16)):
 * Visible blocks: fb = s_b // 16, eb = ceil(L_b / 16), n_b = max(0, eb - fb).
 * Work units are the (request b, KV head h, block j) triples, flattened in (b, h, j)
   order; the range of (b, h) is [o_bh, o_bh + n_b) and U is the total.
-* Pieces (one wave each) cut the flattened axis into P = min(WAVE_SLOTS,
-  ceil(U / MIN_PIECE_BLOCKS)) near-equal parts [U p // P, U (p+1) // P).
+* Pieces (one wave each) cut the flattened axis into P near-equal parts
+  [U p // P, U (p+1) // P): with P0 = min(WAVE_SLOTS, ceil(U / MIN_PIECE_BLOCKS)) and the
+  largest part size m = ceil(U / P0), P = ceil(U / m), the fewest parts of at most m units.
 * A fixed split S > 0 (split-K S) cuts every (b, h) range into c = min(S, n_b) chunks
   [o_bh + n_b k // c, o_bh + n_b (k+1) // c); S = 0 adds no cuts.
 * A piece is cut at (b, h) boundaries and at chunk boundaries into segments, so every
@@ -76,7 +77,9 @@ def decode_partition_ref(kv_lens, window, num_splits, num_kv_heads):
         origin.append(total)
         total += nblk[b]
 
-    p = min(WAVE_SLOTS, _ceil_div(total, MIN_PIECE_BLOCKS))
+    p0 = min(WAVE_SLOTS, _ceil_div(total, MIN_PIECE_BLOCKS))
+    m = _ceil_div(total, p0) if p0 > 0 else 0
+    p = _ceil_div(total, m) if m > 0 else 0
     pieces = [(total * k // p, total * (k + 1) // p) for k in range(p)]
 
     def cuts_of(i):  # unit positions that end a segment inside pair i's range

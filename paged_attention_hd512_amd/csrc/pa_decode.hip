@@ -8,8 +8,8 @@
 // into chunks whose partial results are merged by log-sum-exp weights (flash-decoding).
 //
 // Work decomposition.  The host planner flattens the (request, KV head, 16-token block)
-// units and cuts them into equal pieces, one per wave (2048 on the 256 CUs at two waves
-// per SIMD), so every wave streams the same number of bytes and the whole grid is
+// units and cuts them into equal pieces, one per wave (up to 2048 on the 256 CUs at two
+// waves per SIMD), so every wave streams the same number of bytes and the whole grid is
 // resident from start to end: no second round of workgroups, no tail of stragglers.  A
 // piece is cut into segments at (request, KV head) boundaries; a segment's result goes to
 // the output directly when it covers the whole pair, else to a workspace slot that the

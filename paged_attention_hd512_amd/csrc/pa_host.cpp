@@ -355,7 +355,13 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
   // Pieces (one wave each): the flattened axis in near-equal parts.
   std::vector<std::pair<int64_t, int64_t>> pieces;
   {
-    const int64_t np = std::min<int64_t>(kDecodeWaveSlots, (total + kMinPieceBlocks - 1) / kMinPieceBlocks);
+    // The largest piece sets the launch's length, and while the waves with one block more
+    // than the rest finish, the others leave HBM idle: keep the largest size that
+    // min(wave slots, units / 8) pieces would need, and use as few pieces as that size
+    // allows, so (nearly) every piece holds it.
+    const int64_t np0 = std::min<int64_t>(kDecodeWaveSlots, (total + kMinPieceBlocks - 1) / kMinPieceBlocks);
+    const int64_t per = np0 > 0 ? (total + np0 - 1) / np0 : 0;
+    const int64_t np = per > 0 ? (total + per - 1) / per : 0;
     for (int64_t k = 0; k < np; ++k) pieces.emplace_back(total * k / np, total * (k + 1) / np);
   }
   // End of the segment that starts at unit u of pair i: the pair's end, or with a fixed

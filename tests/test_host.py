@@ -142,12 +142,19 @@ def test_reference_partition_covers_visible_keys_exactly(lens, P, window, splits
     assert slots == list(range(len(slots)))  # every slot written once
 
 
-def test_balanced_partition_of_the_gqa_decode_shape_fills_every_wave_slot():
+def test_balanced_partition_of_the_gqa_decode_shape_gives_equal_pieces():
+    """The GQA decode shape: at most 2048 waves, every piece holds the largest size that
+    2048 pieces would need (ceil(units / 2048) blocks) or one block less, and the fewest
+    waves that size allows run, so almost none is short."""
     lens = list(np.random.default_rng(5).integers(1024, 8193, size=32))
     waves, merges = decode_partition_ref(lens, 0, 0, 4)
     total = 4 * sum(-(-int(L) // 16) for L in lens)
-    assert len(waves) == 2048
-    assert sum(sum(-(-t1 // 16) - t0 // 16 for _, _, t0, t1, _ in w) for w in waves) == total
+    blocks = [sum(-(-t1 // 16) - t0 // 16 for _, _, t0, t1, _ in w) for w in waves]
+    m = -(-total // 2048)
+    assert sum(blocks) == total
+    assert len(waves) <= 2048 and len(waves) == -(-total // m)
+    assert max(blocks) == m and min(blocks) >= m - 1
+    assert sum(b < m for b in blocks) < len(waves) // 100 + 1
     assert all(1 <= len(w) <= 2 for w in waves)  # pieces of ~36 blocks vs pairs of >= 64
 
 
