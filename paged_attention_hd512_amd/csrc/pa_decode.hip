@@ -444,67 +444,95 @@ struct MergeArgs {
 };
 
 // One wave per (merged (request, KV head), head of the group): log-sum-exp weights over
-// the segments, then the weighted sum of the segment outputs in segment order.  The
-// segments' log-sum-exps are read 64 at a time, one per lane, and their rows eight at a
-// time, so a wave keeps eight row loads in flight instead of waiting on each in turn.  A
-// pair with no segments (no keys) gets a zero output and lse -inf.
+// the segments, then the weighted sum of the segment outputs in segment order.  The rows
+// do not depend on the weights, so the log-sum-exps of up to 64 segments (one per lane) and
+// the rows of the first 16 segments are requested together before any of them is used: a
+// pair of up to 16 segments costs one memory round trip.  Further rows are read 8 at a
+// time.  A pair with no segments (no keys) gets a zero output and lse -inf.
 template <int DVO>
 __global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a) {
   constexpr int EPT = DVO / 64;
-  constexpr int UN = 8;
+  constexpr int UN0 = 16;  // rows requested with the log-sum-exps
+  constexpr int UN = 8;    // rows in flight per later step
   const MergeItem mi = a.merges[blockIdx.x];
   const int h = blockIdx.y;
   const int lane = threadIdx.x;
   const int G = a.group;
   const int n = mi.num_slots;
-  const float* lse_col = a.part_lse + (int64_t)mi.slot_begin * G + h;
-  float mx = -INFINITY;
-  for (int c = lane; c < n; c += 64) mx = fmaxf(mx, lse_col[(int64_t)c * G]);
-  mx = max_xor16(max_xor32(mx));
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
-  const float mu = mx == -INFINITY ? 0.f : mx;
   float o[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) o[e] = 0.f;
-  float wpart = 0.f;
-  const int64_t rstride = (int64_t)G * DVO;
-  const float* src0 = a.part_o + ((int64_t)mi.slot_begin * G + h) * DVO + lane * EPT;
-  for (int c0 = 0; c0 < n; c0 += 64) {
-    const int cn = min(64, n - c0);
-    const float lv = lse_col[(int64_t)min(c0 + lane, n - 1) * G];
-    const float w = lane < cn ? exp2f(lv - mu) : 0.f;
-    wpart += w;
-    const float* src = src0 + (int64_t)c0 * rstride;
-    int c = 0;
-    for (; c + UN <= cn; c += UN) {
-      f32x4_t x[UN][EPT / 4];
+  float mx = -INFINITY, wsum = 0.f;
+  if (n > 0) {
+    const float* lse_col = a.part_lse + (int64_t)mi.slot_begin * G + h;
+    const int64_t rstride = (int64_t)G * DVO;
+    const float* src0 = a.part_o + ((int64_t)mi.slot_begin * G + h) * DVO + lane * EPT;
+    // Lane c: log-sum-exp of segment min(c, n - 1); rows 0 .. UN0 - 1, clamped to the last
+    // segment (the clamped copies get weight 0).
+    const float lv0 = lse_col[(int64_t)min(lane, n - 1) * G];
+    f32x4_t x0[UN0][EPT / 4];
 #pragma unroll
-      for (int u = 0; u < UN; ++u)
+    for (int u = 0; u < UN0; ++u)
 #pragma unroll
-        for (int e = 0; e < EPT / 4; ++e) x[u][e] = *(const f32x4_t*)(src + (c + u) * rstride + 4 * e);
+      for (int e = 0; e < EPT / 4; ++e)
+        x0[u][e] = *(const f32x4_t*)(src0 + (int64_t)min(u, n - 1) * rstride + 4 * e);
+    mx = lane < n ? lv0 : -INFINITY;
+    for (int c = 64 + lane; c < n; c += 64) mx = fmaxf(mx, lse_col[(int64_t)c * G]);
+    mx = max_xor16(max_xor32(mx));
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c + u));
+    for (int m = 8; m >= 1; m >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
+    const float mu = mx == -INFINITY ? 0.f : mx;
+    float w = lane < n ? exp2f(lv0 - mu) : 0.f;
+    float wpart = w;
 #pragma unroll
-        for (int e = 0; e < EPT / 4; ++e)
+    for (int u = 0; u < UN0; ++u) {
+      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
 #pragma unroll
-          for (int v = 0; v < 4; ++v) o[4 * e + v] = fmaf(wu, x[u][e][v], o[4 * e + v]);
+      for (int e = 0; e < EPT / 4; ++e)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[4 * e + v] = fmaf(wu, x0[u][e][v], o[4 * e + v]);
+    }
+    // The rest, in segment order: rows UN0 .. of the first 64, then 64 at a time (their
+    // log-sum-exps one per lane again).
+    int c = UN0;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const int cn = min(64, n - c0);
+      if (c0 > 0) {
+        const float lv = lse_col[(int64_t)(c0 + min(lane, cn - 1)) * G];
+        w = lane < cn ? exp2f(lv - mu) : 0.f;
+        wpart += w;
+        c = 0;
+      }
+      const float* src = src0 + (int64_t)c0 * rstride;
+      for (; c + UN <= cn; c += UN) {
+        f32x4_t x[UN][EPT / 4];
+#pragma unroll
+        for (int u = 0; u < UN; ++u)
+#pragma unroll
+          for (int e = 0; e < EPT / 4; ++e) x[u][e] = *(const f32x4_t*)(src + (c + u) * rstride + 4 * e);
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c + u));
+#pragma unroll
+          for (int e = 0; e < EPT / 4; ++e)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[4 * e + v] = fmaf(wu, x[u][e][v], o[4 * e + v]);
+        }
+      }
+      for (; c < cn; ++c) {
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
+#pragma unroll
+        for (int e = 0; e < EPT / 4; ++e) {
+          const f32x4_t x = *(const f32x4_t*)(src + c * rstride + 4 * e);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[4 * e + v] = fmaf(wu, x[v], o[4 * e + v]);
+        }
       }
     }
-    for (; c < cn; ++c) {
-      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
+    wsum = sum_xor16(sum_xor32(wpart));
 #pragma unroll
-      for (int e = 0; e < EPT / 4; ++e) {
-        const f32x4_t x = *(const f32x4_t*)(src + c * rstride + 4 * e);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) o[4 * e + v] = fmaf(wu, x[v], o[4 * e + v]);
-      }
-    }
+    for (int m = 8; m >= 1; m >>= 1) wsum += shfl_xor_f(wsum, m);
   }
-  float wsum = sum_xor16(sum_xor32(wpart));
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) wsum += shfl_xor_f(wsum, m);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int hq = a.num_qo_heads;
   const int64_t off = ((int64_t)mi.b * hq + mi.kvh * G + h) * DVO + lane * EPT;
