@@ -214,6 +214,30 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
       }
+      if constexpr (KV == kKvFp4) {
+        // Loads i and i + 1 hold the same columns of keys tk and tk + RPI: one column of
+        // both as an fp16 pair, times (p * block scale) of both keys as an fp16 pair, summed
+        // in fp32 by v_dot2_f32_f16 (the products are exact in fp32).
+        static_assert(NVL % 2 == 0, "V loads come in pairs");
+#pragma unroll
+        for (int i = 0; i < NVL; i += 2) {
+          const int tk = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
+          const float bs0 = fp8_to_f32<0>(vsf[i]), bs1 = fp8_to_f32<0>(vsf[i + 1]);
+          f16x2_t pp[GMAX];
+#pragma unroll
+          for (int h = 0; h < GMAX; ++h)
+            pp[h] = f16x2_t{(_Float16)(p_lds[pb][tk][h] * bs0), (_Float16)(p_lds[pb][tk + RPI][h] * bs1)};
+          f16x2_t col[8];
+          fp4x8_pair_to_f16x2(vbuf[i], vbuf[i + 1], col);
+#pragma unroll
+          for (int h = 0; h < GMAX; ++h) {
+            if (GMAX == 1 || h < G) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_amdgcn_fdot2(col[e], pp[h], acc[h][e], false);
+            }
+          }
+        }
+      } else {
 #pragma unroll
       for (int i = 0; i < NVL; ++i) {
         const int tk = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
@@ -227,14 +251,9 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
             vf[2 * e] = bf16_lo(vbuf[i][e]);
             vf[2 * e + 1] = bf16_hi(vbuf[i][e]);
           }
-        } else if constexpr (KV == kKvFp8) {
+        } else {
           fp8x4_to_f32(vbuf[i][0], vf);
           fp8x4_to_f32(vbuf[i][1], vf + 4);
-        } else {
-          fp4x8_to_f32(vbuf[i], vf);
-          const float bs = fp8_to_f32<0>(vsf[i]);
-#pragma unroll
-          for (int h = 0; h < GMAX; ++h) p[h] *= bs;
         }
 #pragma unroll
         for (int h = 0; h < GMAX; ++h) {
@@ -243,6 +262,7 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
             for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p[h], vf[e], acc[h][e]);
           }
         }
+      }
       }
     };
 

@@ -80,6 +80,23 @@ __device__ __forceinline__ f16x8_t fp4x8_to_f16_scaled(uint32_t w, _Float16 bs) 
   return f16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Two E2M1 rows a and b (one dword each, element 2i in the low nibble of byte i), column
+// by column as fp16 pairs: out[e] = (a[e], b[e]) for e = 0..7, exact.  The nibbles are
+// interleaved first (byte i of lo holds a[2i] and b[2i], byte i of hi a[2i+1] and b[2i+1]),
+// so each conversion yields one column of both rows.
+__device__ __forceinline__ void fp4x8_pair_to_f16x2(uint32_t a, uint32_t b, f16x2_t* out) {
+  const uint32_t lo = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
+  const uint32_t hi = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 1.0f, 0);
+  out[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 1.0f, 0);
+  out[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 1.0f, 1);
+  out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 1.0f, 1);
+  out[4] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 1.0f, 2);
+  out[5] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 1.0f, 2);
+  out[6] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 1.0f, 3);
+  out[7] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 1.0f, 3);
+}
+
 // Two fp32 -> two fp16 in one dword, round to nearest even.
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   const f16x2_t v = {(_Float16)lo, (_Float16)hi};
