@@ -150,6 +150,29 @@ def test_waves_that_run_several_segments():
     compare("several segments per wave", out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
 
 
+def test_fp8_single_key_requests_return_every_value_code_exactly():
+    """With one visible key the softmax weight is 1, so the fp32 output is the key's V row
+    decoded (E4M3FN, exact) times v_scale, one rounding: bit for bit the oracle's value
+    rounded to fp32.  The keys' V rows are rewritten so that every finite E4M3FN code
+    appears in every column position class: this checks the kernel's FP8 value decoding
+    code by code."""
+    for dim, dvo, page in ((512, 512, 16), (256, 256, 1), (512, 256, 3)):
+        say(f"fp8 single-key rows, all codes, dims={dim}/{dvo} page={page}")
+        c = make_decode_case([1] * 64, 8, 2, dim, page, head_dim_vo=dvo, kv_dtype="fp8",
+                             out_dtype="fp32", seed=23, device=dev())
+        for b in range(c.batch):
+            pg = int(c.kv_indices[c.kv_indptr[b]])  # the request's only key: slot 0
+            for h in range(c.num_kv_heads):
+                row = (np.arange(dvo) + 7 * (b * c.num_kv_heads + h)) % 256
+                row[(row & 0x7F) == 0x7F] = 0  # the NaN codes
+                c.v_pool[pg, h, 0, :] = torch.as_tensor(row.astype(np.uint8)).to(dev())
+        _, o, lse = gpu_decode(c)
+        ref, ref_lse = oracle_decode(c)
+        got = o.cpu().numpy()
+        assert np.array_equal(got, ref.astype(np.float32)), "FP8 V decoding is not exact"
+        assert np.abs(lse.cpu().numpy() - ref_lse).max() < 1e-4
+
+
 def test_merges_of_more_than_64_segments():
     """Long requests cut into well over 64 balanced segments (129, 130 and 71 with the
     current planner): the merge reads the segments' log-sum-exps 64 at a time and their rows
