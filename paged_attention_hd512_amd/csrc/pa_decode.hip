@@ -395,13 +395,16 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
       page_c = page_n;
       slot_c = slot_n;
       // ---- issue priority from the workgroup's progress (plain LDS words; a stale value
-      // only delays the adjustment by an iteration).
+      // only delays the adjustment by an iteration): highest while behind the CU's
+      // average, low within a block ahead of it, lowest further ahead.
       ++done;
       if (lane == 0) progress[wv] = done;
       int sum = 0;
 #pragma unroll
       for (int x = 0; x < NWG; ++x) sum += progress[x];
-      if (done * NWG < sum) __builtin_amdgcn_s_setprio(3);
+      const int lag = sum - done * NWG;  // NWG x (blocks behind the CU's average)
+      if (lag > 0) __builtin_amdgcn_s_setprio(3);
+      else if (lag > -NWG) __builtin_amdgcn_s_setprio(1);
       else __builtin_amdgcn_s_setprio(0);
     }
     pv((iter - 1) & 1);
