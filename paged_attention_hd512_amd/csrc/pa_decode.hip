@@ -116,9 +116,11 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
   constexpr int NVL = 16 / RPI;                   // V load instructions per block
   constexpr int QPITCH = DQK + 8;                 // LDS row pitch of Q (bf16), padded
   constexpr int QV = (GMAX * DQK / 8 + 63) / 64;  // 16-byte Q pieces per lane
+  constexpr int TPD = DVO / 32;                   // NVFP4: P V MFMA tiles per block
   using vload_t = typename std::conditional<
       KV == kKvBf16, u32x4_t, typename std::conditional<KV == kKvFp8, u32x2_t, uint32_t>::type>::type;
   using ksf_t = typename std::conditional<NKSF == 8, u32x2_t, uint32_t>::type;
+  using vq_t = typename std::conditional<TPD == 16, u32x2_t, uint32_t>::type;  // TPD nibbles
 
   constexpr int NWG = kDecodeWavesPerGroup;
   __shared__ __attribute__((aligned(16))) uint16_t q_all[NWG][GMAX * QPITCH];
@@ -144,8 +146,11 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
   u32x4_t kbuf[NKL];
   vload_t vbuf[NVL];
   ksf_t ksf;            // NVFP4: this lane's K block scales of the block (E4M3 codes)
-  uint32_t vsf[NVL];    // NVFP4: the block scale of each V row's 8 elements of this lane
+  uint32_t vsf[NVL];    // V block scales (E4M3 codes), when V rows are read a row per lane set
+  vq_t vq[8];           // NVFP4: TPD head_dim columns of eight V rows (see issue_v)
+  uint32_t vsq[8];      // NVFP4: their block scales (E4M3 codes)
   float acc[GMAX][8];
+  f32x4_t acc4[TPD];    // NVFP4: the P V tiles, one MFMA output each
 
   for (int sgi = seg_first; sgi < seg_last; ++sgi) {
     const DecodeSegment sg = a.segs[sgi];
@@ -186,6 +191,20 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
       const int64_t voff = (row_elem_offset(page, 0, slot, a.v_sp, 0, a.v_st) + v_head) * UNIT;
       int64_t vsoff = 0;
       if constexpr (KV == kKvFp4) vsoff = row_elem_offset(page, 0, slot, a.vs_sp, 0, a.vs_st) + vs_head;
+      if constexpr (KV == kKvFp4) {
+        // NVFP4: lane (g4, n) reads keys 8 (g4 & 1) + r, r < 8, of the block, each at the TPD
+        // contiguous columns DVO/2 (g4 >> 1) + TPD n, which lie in one 16-column scale block.
+        const int kb = 8 * (g4 & 1);
+        const int vcol = (DVO / 4) * (g4 >> 1) + (TPD / 2) * n;
+        const int scol = ((DVO / 2) * (g4 >> 1) + TPD * n) / 16;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int64_t off = shfl_i64(voff, kb + r);
+          const int64_t soff = shfl_i64(vsoff, kb + r);
+          vq[r] = __builtin_nontemporal_load((const vq_t*)(a.v + off + vcol));
+          vsq[r] = __builtin_nontemporal_load((const uint8_t*)(a.v_sf + soff + scol));
+        }
+      } else {
 #pragma unroll
       for (int i = 0; i < NVL; ++i) {
         const int src = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
@@ -198,13 +217,52 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
           if constexpr (KV == kKvFp4) soff = shfl_i64(vsoff, src);
         }
         vbuf[i] = __builtin_nontemporal_load((const vload_t*)(a.v + off + (lane % LPR) * VB8));
-        if constexpr (KV == kKvFp4)
-          vsf[i] = __builtin_nontemporal_load((const uint8_t*)(a.v_sf + soff + (lane % LPR) / 2));
+      }
       }
     };
     // P V of one block: rescale the accumulators by the block's alpha, then add p * V with
     // the probabilities from LDS buffer `pb` and the V rows in vbuf.
     auto pv = [&](int pb) {
+      if constexpr (KV == kKvFp4) {
+        // NVFP4: O^T += V^T P^T on v_mfma_f32_16x16x32_f16, one MFMA per tile t < TPD.  The
+        // 32-long contraction runs over (half x, key): A[i][(x, key)] = V[key][DVO/2 x + TPD i
+        // + t] times the key's block scale (exact in fp16), B[(x, key)][(x', h)] = P[key][h]
+        // when x = x', else 0.  Output column (x', h) of tile t is head h at head_dim columns
+        // DVO/2 x' + TPD i + t, so lane (g4, n) ends with head n & 7 at the 4 TPD columns
+        // from DVO/2 (n >> 3) + 4 TPD g4 (acc4[t][r] at column TPD r + t).
+        const float al = alpha_lds[pb][n & 7];
+#pragma unroll
+        for (int t = 0; t < TPD; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc4[t][r] *= al;
+        const bool on = (g4 >> 1) == (n >> 3);
+        const int kb = 8 * (g4 & 1);
+        u32x4_t pw;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          pw[c] = on ? pack_f16(p_lds[pb][kb + 2 * c][n & 7], p_lds[pb][kb + 2 * c + 1][n & 7]) : 0u;
+        const f16x8_t bop = __builtin_bit_cast(f16x8_t, pw);
+        f16x2_t sc2[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          sc2[c] = f16x2_t{(_Float16)fp8_to_f32<0>(vsq[2 * c]), (_Float16)fp8_to_f32<0>(vsq[2 * c + 1])};
+#pragma unroll
+        for (int w = 0; w < TPD / 8; ++w) {
+          f16x2_t col[4][8];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if constexpr (TPD == 16) fp4x8_pair_to_f16x2(vq[2 * c][w], vq[2 * c + 1][w], col[c]);
+            else fp4x8_pair_to_f16x2(vq[2 * c], vq[2 * c + 1], col[c]);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const f16x2_t x0 = col[0][e] * sc2[0], x1 = col[1][e] * sc2[1];
+            const f16x2_t x2 = col[2][e] * sc2[2], x3 = col[3][e] * sc2[3];
+            const f16x8_t aop = {x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+            acc4[8 * w + e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc4[8 * w + e], 0, 0, 0);
+          }
+        }
+      } else {
       {
         float al[GMAX];
 #pragma unroll
@@ -214,30 +272,6 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
       }
-      if constexpr (KV == kKvFp4) {
-        // Loads i and i + 1 hold the same columns of keys tk and tk + RPI: one column of
-        // both as an fp16 pair, times (p * block scale) of both keys as an fp16 pair, summed
-        // in fp32 by v_dot2_f32_f16 (the products are exact in fp32).
-        static_assert(NVL % 2 == 0, "V loads come in pairs");
-#pragma unroll
-        for (int i = 0; i < NVL; i += 2) {
-          const int tk = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
-          const float bs0 = fp8_to_f32<0>(vsf[i]), bs1 = fp8_to_f32<0>(vsf[i + 1]);
-          f16x2_t pp[GMAX];
-#pragma unroll
-          for (int h = 0; h < GMAX; ++h)
-            pp[h] = f16x2_t{(_Float16)(p_lds[pb][tk][h] * bs0), (_Float16)(p_lds[pb][tk + RPI][h] * bs1)};
-          f16x2_t col[8];
-          fp4x8_pair_to_f16x2(vbuf[i], vbuf[i + 1], col);
-#pragma unroll
-          for (int h = 0; h < GMAX; ++h) {
-            if (GMAX == 1 || h < G) {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_amdgcn_fdot2(col[e], pp[h], acc[h][e], false);
-            }
-          }
-        }
-      } else {
 #pragma unroll
       for (int i = 0; i < NVL; ++i) {
         const int tk = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
@@ -320,6 +354,8 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
     for (int h = 0; h < GMAX; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+    for (int t = 0; t < TPD; ++t) acc4[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     int iter = 0;
     for (; blk < blk_end; ++blk, ++iter) {
@@ -412,14 +448,49 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
     // ---- segment result: the sum over the 4 lanes of a head, and (two rows per V load)
     // the accumulator halves.  Lane h < 16 then holds head h's max and sum.
     l_run = sum_xor32(sum_xor16(l_run));
-    if constexpr (RPI == 2) {
+    if constexpr (RPI == 2 && KV != kKvFp4) {
 #pragma unroll
       for (int h = 0; h < GMAX; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] += shfl_xor_f(acc[h][e], 32);
     }
     const int h0 = sg.kvh * G;
-    if (lane < LPR) {
+    if constexpr (KV == kKvFp4) {
+      // Lane (g4, n): head n & 7 at the 4 TPD columns from DVO/2 (n >> 3) + 4 TPD g4.
+      const int h = n & 7;
+      const float lh = __builtin_bit_cast(
+          float, __builtin_amdgcn_ds_bpermute(h << 2, __builtin_bit_cast(int, l_run)));
+      if (h < G) {
+        const float inv = lh > 0.f ? a.v_scale / lh : 0.f;
+        const int d0 = (DVO / 2) * (n >> 3) + 4 * TPD * g4;
+        float o[4 * TPD];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int t = 0; t < TPD; ++t) o[TPD * r + t] = acc4[t][r] * inv;
+        if (sg.slot >= 0) {
+          float* dst = a.part_o + ((int64_t)sg.slot * G + h) * DVO + d0;
+#pragma unroll
+          for (int c = 0; c < TPD; ++c)
+            *(f32x4_t*)(dst + 4 * c) = f32x4_t{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
+        } else {
+          const int64_t off = ((int64_t)sg.b * a.num_qo_heads + h0 + h) * DVO + d0;
+          if (a.out_fp32) {
+            float* dst = (float*)a.out + off;
+#pragma unroll
+            for (int c = 0; c < TPD; ++c)
+              *(f32x4_t*)(dst + 4 * c) = f32x4_t{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
+          } else {
+#pragma unroll
+            for (int c = 0; c < TPD / 2; ++c) {
+              const u32x4_t pk = {pack_bf16(o[8 * c], o[8 * c + 1]), pack_bf16(o[8 * c + 2], o[8 * c + 3]),
+                                  pack_bf16(o[8 * c + 4], o[8 * c + 5]), pack_bf16(o[8 * c + 6], o[8 * c + 7])};
+              *(u32x4_t*)((uint16_t*)a.out + off + 8 * c) = pk;
+            }
+          }
+        }
+      }
+    } else if (lane < LPR) {
 #pragma unroll
       for (int h = 0; h < GMAX; ++h) {
         if (h >= G) continue;
