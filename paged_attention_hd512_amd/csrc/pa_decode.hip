@@ -195,14 +195,14 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
         // NVFP4: lane (g4, n) reads keys 8 (g4 & 1) + r, r < 8, of the block, each at the TPD
         // contiguous columns DVO/2 (g4 >> 1) + TPD n, which lie in one 16-column scale block.
         const int kb = 8 * (g4 & 1);
-        const int vcol = (DVO / 4) * (g4 >> 1) + (TPD / 2) * n;
-        const int scol = ((DVO / 2) * (g4 >> 1) + TPD * n) / 16;
+        const char* vbase = a.v + ((DVO / 4) * (g4 >> 1) + (TPD / 2) * n);
+        const char* sbase = a.v_sf + ((DVO / 2) * (g4 >> 1) + TPD * n) / 16;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const int64_t off = shfl_i64(voff, kb + r);
           const int64_t soff = shfl_i64(vsoff, kb + r);
-          vq[r] = __builtin_nontemporal_load((const vq_t*)(a.v + off + vcol));
-          vsq[r] = __builtin_nontemporal_load((const uint8_t*)(a.v_sf + soff + scol));
+          vq[r] = __builtin_nontemporal_load((const vq_t*)(vbase + off));
+          vsq[r] = __builtin_nontemporal_load((const uint8_t*)(sbase + soff));
         }
       } else {
 #pragma unroll
@@ -230,11 +230,15 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
         // when x = x', else 0.  Output column (x', h) of tile t is head h at head_dim columns
         // DVO/2 x' + TPD i + t, so lane (g4, n) ends with head n & 7 at the 4 TPD columns
         // from DVO/2 (n >> 3) + 4 TPD g4 (acc4[t][r] at column TPD r + t).
+        // Rescale only when some head's running max moved (a wave-uniform branch with no
+        // load inside): after a segment's first blocks the max rarely changes.
         const float al = alpha_lds[pb][n & 7];
+        if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
 #pragma unroll
-        for (int t = 0; t < TPD; ++t)
+          for (int t = 0; t < TPD; ++t)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc4[t][r] *= al;
+            for (int r = 0; r < 4; ++r) acc4[t][r] *= al;
+        }
         const bool on = (g4 >> 1) == (n >> 3);
         const int kb = 8 * (g4 & 1);
         u32x4_t pw;
