@@ -21,7 +21,8 @@
 //     row); Q sits in LDS with the same head_dim order.
 //   * The online softmax keeps a running max and sum per head; the block max is a
 //     cross-lane reduction over the 4 lanes that share a head.
-//   * P V runs on the vector ALU one block behind S: each V load instruction covers whole
+//   * P V (bf16 and FP8 values) runs on the vector ALU one block behind S: each V load
+//     instruction covers whole
 //     key rows (lane l holds 8 consecutive head_dim elements of one row), each lane keeps
 //     G x 8 fp32 accumulators, and the block's probabilities come from LDS as broadcast
 //     reads.  Block i's V rows are loaded while block i's scores are computed and used in
@@ -39,9 +40,11 @@
 // bits and lies in [2^-10, 2688]; Q is staged in fp16, each segment's rows scaled by the
 // power of two that brings their largest magnitude just below 2^15, so every bf16 query
 // element converts exactly (short of 2^-29 of that largest one) and none overflows, and
-// the factor comes back out of the score scale.  For values the nibbles go to fp32 and
-// the block scale multiplies the probability, one product per head rather than one per
-// element.  The global k_scale / v_scale apply as for FP8.
+// the factor comes back out of the score scale.  NVFP4 values go through the fp16 MFMA as
+// well, still one block behind S: the contraction is taken over (half of head_dim, key), so
+// each lane reads contiguous bytes of eight rows that share one scale block, and two rows'
+// nibbles interleave into fp16 pairs of an A operand (no transpose); P, rounded to fp16,
+// is the B operand.  The global k_scale / v_scale apply as for FP8.
 
 #include <hip/hip_runtime.h>
 
