@@ -22,11 +22,11 @@
 //   * The online softmax keeps a running max and sum per head; the block max is a
 //     cross-lane reduction over the 4 lanes that share a head.
 //   * P V (bf16 and FP8 values) runs on the vector ALU one block behind S: each V load
-//     instruction covers whole
-//     key rows (lane l holds 8 consecutive head_dim elements of one row), each lane keeps
-//     G x 8 fp32 accumulators, and the block's probabilities come from LDS as broadcast
-//     reads.  Block i's V rows are loaded while block i's scores are computed and used in
-//     the next iteration; block i+1's keys are loaded after block i's MFMAs.
+//     instruction covers whole key rows (lane l holds 8 consecutive head_dim elements of
+//     one row), each lane keeps G x 8 fp32 accumulators, and the block's probabilities
+//     come from LDS as broadcast reads.  Block i's V rows are loaded while block i's
+//     scores are computed and used in the next iteration; block i+1's keys are loaded
+//     after block i's MFMAs.
 //   * Waves never synchronise with each other; each one's results are deterministic.
 // FP8 E4M3FN keys are widened to bf16 in registers (exact); k_scale is folded into the
 // score scale and v_scale into the output.
