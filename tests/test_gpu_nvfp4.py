@@ -51,6 +51,12 @@ NVFP4_SWEEP = [
     ([100, 200, 300], 4, 1, 256, 256, 8, 0, 0, "bf16"),
     ([64, 128, 192], 40, 8, 512, 512, 16, 0, 64, "bf16"),
     ([0, 20, 0, 3], 8, 1, 512, 512, 16, 0, 2, "fp32"),
+    # one query head per KV head, and full groups of 8 at the narrower value widths: the
+    # value MFMA holds heads 0..7 of its output columns and discards those past the group
+    ([37, 64, 1, 16, 17, 300], 4, 4, 512, 512, 16, 0, 0, "bf16"),
+    ([100, 200, 300], 2, 2, 256, 256, 16, 0, 0, "fp32"),
+    ([45, 46, 47, 200], 16, 2, 512, 256, 16, 0, 0, "bf16"),
+    ([100, 200, 300], 8, 1, 256, 256, 8, 0, 3, "bf16"),
 ]
 
 
