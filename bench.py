@@ -15,8 +15,21 @@ Algorithmic work:
   prefill flops = sum_b sum_i Hq * |visible keys of row i| * 2 * (Dqk + Dvo)
 Both are counted from the realised seeded lengths.
 
+Timing: `ms_per_step` (and `value`) come from one pair of HIP events on the launch stream
+around K back-to-back steps; `protocol` gives the median, minimum and mean of 50 further
+iterations timed one by one (an event between consecutive iterations); the dominant
+kernel's average duration (`roofline.kernel_avg_ms`) comes from a pass with events around
+every launch.  The sliding-window workloads at head_dim 256 (about 0.4 GB of visible KV,
+close to the 256 MB last-level cache) alternate between two copies of the pool in every
+timed loop.  Every line carries the oracle's CPU throughput on a bounded sample of the same
+workload (`cpu_baseline`).
+
+`--profile` runs only W + K launches of the named workload's hot path (no other timing,
+no baseline, no secondary workloads), for rocprofv3: its kernel averages then cover exactly
+those calls.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-secondary] [--no-cpu-baseline]
+                       [--no-secondary] [--no-cpu-baseline] [--profile]
 """
 
 import argparse
@@ -146,29 +159,95 @@ def time_kernels(launches, stream, steps):
     return [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j in range(len(launches))]
 
 
-def time_decode(case, steps, warmup):
-    """Returns (ms_per_step, partial_kernel_ms, merge_ms, wall_ms, plan): the step time of
-    back-to-back decode steps, then the two kernels' durations from events around each."""
+def time_protocol(launch, stream, iters=50):
+    """Median, minimum and mean (ms) of `iters` iterations timed one by one: one HIP event
+    between consecutive iterations on the launch stream."""
     import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(iters):
+        launch()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+    med = (t[(iters - 1) // 2] + t[iters // 2]) / 2
+    return {"iters": iters, "median_ms": round(med, 5), "min_ms": round(t[0], 5),
+            "mean_ms": round(sum(t) / iters, 5)}
+
+
+class Rotation:
+    """Calls the launches of several copies of a workload in turn (one per call)."""
+
+    def __init__(self, fns):
+        self.fns, self.i = fns, 0
+
+    def __call__(self):
+        f = self.fns[self.i]
+        self.i = (self.i + 1) % len(self.fns)
+        f()
+
+
+def decode_runner(case):
     from paged_attention_hd512_amd import PagedDecode
+    return PagedDecode(case.k_pool, case.v_pool, case.kv_indptr, case.kv_indices,
+                       case.kv_last_page_len, case.num_qo_heads, kv_dtype=case.kv_dtype,
+                       k_scale=case.k_scale, v_scale=case.v_scale, sm_scale=case.sm_scale,
+                       window=case.window, num_splits=case.num_splits, out_dtype=case.out_dtype,
+                       k_sf=case.k_sf, v_sf=case.v_sf)
+
+
+def pool_copy(case):
+    """The same case over a second copy of its KV pool (and block scales)."""
+    import copy
+    c2 = copy.copy(case)
+    if case.cache is not None:
+        c2.cache = case.cache.clone()
+        c2.k_pool, c2.v_pool = c2.cache[:, 0], c2.cache[:, 1]
+    else:
+        c2.k_pool, c2.v_pool = case.k_pool.clone(), case.v_pool.clone()
+    if case.sf_cache is not None:
+        c2.sf_cache = case.sf_cache.clone()
+        c2.k_sf, c2.v_sf = c2.sf_cache[:, 0], c2.sf_cache[:, 1]
+    elif case.k_sf is not None:
+        c2.k_sf, c2.v_sf = case.k_sf.clone(), case.v_sf.clone()
+    return c2
+
+
+def time_decode(case, steps, warmup, copies=1, profile=False):
+    """Returns (ms_per_step, partial_kernel_ms, merge_ms, wall_ms, plan, protocol): the step
+    time of back-to-back decode steps, then the two kernels' durations from events around
+    each, then the 50-iteration protocol.  With copies = 2 every loop alternates between
+    two copies of the pool.  With profile, only warmup + steps decode steps run."""
+    import torch
     import paged_attention_hd512_amd.pa as pa
 
-    run = PagedDecode(case.k_pool, case.v_pool, case.kv_indptr, case.kv_indices,
-                      case.kv_last_page_len, case.num_qo_heads, kv_dtype=case.kv_dtype,
-                      k_scale=case.k_scale, v_scale=case.v_scale, sm_scale=case.sm_scale,
-                      window=case.window, num_splits=case.num_splits, out_dtype=case.out_dtype,
-                      k_sf=case.k_sf, v_sf=case.v_sf)
-    out, lse = run.run(case.q)
-    stream = torch.cuda.current_stream()
+    cases = [case] + [pool_copy(case) for _ in range(copies - 1)]
     sh = pa.current_stream_handle()
-    args = (run.plan, case.q.data_ptr(), run.cache, run.table, run.params, out.data_ptr(),
-            lse.data_ptr(), run.workspace.data_ptr(), run.workspace.numel(), sh)
+    argsets = []
+    runners = []
+    for c in cases:
+        run = decode_runner(c)
+        out, lse = run.run(c.q)
+        runners.append((run, out, lse))
+        argsets.append((run.plan, c.q.data_ptr(), run.cache, run.table, run.params,
+                        out.data_ptr(), lse.data_ptr(), run.workspace.data_ptr(),
+                        run.workspace.numel(), sh))
+    stream = torch.cuda.current_stream()
+    step_fn = Rotation([lambda a=a: pa.pa_paged_decode(*a) for a in argsets])
     for _ in range(warmup):
-        pa.pa_paged_decode(*args)
-    step, wall = time_steps(lambda: pa.pa_paged_decode(*args), stream, steps)
-    part, merge = time_kernels([lambda: pa.pa_paged_decode_partial(*args),
-                                lambda: pa.pa_paged_decode_merge(*args)], stream, steps)
-    return max(step, 1e-9), part, merge, wall, run.plan
+        step_fn()
+    if profile:
+        for _ in range(steps):
+            step_fn()
+        torch.cuda.synchronize()
+        return None, None, None, None, runners[0][0].plan, None
+    step, wall = time_steps(step_fn, stream, steps)
+    part_fn = Rotation([lambda a=a: pa.pa_paged_decode_partial(*a) for a in argsets])
+    merge_fn = Rotation([lambda a=a: pa.pa_paged_decode_merge(*a) for a in argsets])
+    part, merge = time_kernels([part_fn, merge_fn], stream, steps)
+    proto = time_protocol(step_fn, stream)
+    return max(step, 1e-9), part, merge, wall, runners[0][0].plan, proto
 
 
 def time_decode_graph(case, steps, warmup):
@@ -204,9 +283,10 @@ def time_decode_graph(case, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def time_prefill(case, steps, warmup):
-    """Returns (ms_per_step, kernel_ms, wall_ms, plan): back-to-back prefill steps, then the
-    duration of one step's launch(es) from events around it."""
+def time_prefill(case, steps, warmup, profile=False):
+    """Returns (ms_per_step, kernel_ms, wall_ms, plan, protocol): back-to-back prefill steps,
+    then the duration of one step's launch(es) from events around it, then the 50-iteration
+    protocol.  With profile, only warmup + steps prefill steps run."""
     import torch
     from paged_attention_hd512_amd import PagedPrefill
     import paged_attention_hd512_amd.pa as pa
@@ -224,9 +304,15 @@ def time_prefill(case, steps, warmup):
             run.workspace.numel(), sh)
     for _ in range(warmup):
         pa.pa_paged_prefill(*args)
+    if profile:
+        for _ in range(steps):
+            pa.pa_paged_prefill(*args)
+        torch.cuda.synchronize()
+        return None, None, None, run.plan, None
     step, wall = time_steps(lambda: pa.pa_paged_prefill(*args), stream, steps)
     (kern,) = time_kernels([lambda: pa.pa_paged_prefill(*args)], stream, steps)
-    return step, kern, wall, run.plan
+    proto = time_protocol(lambda: pa.pa_paged_prefill(*args), stream)
+    return step, kern, wall, run.plan, proto
 
 
 def cpu_threads():
@@ -296,6 +382,9 @@ def oracle_decode_baseline(case, budget_s=12.0):
 
 
 def oracle_prefill_baseline(case, budget_s=12.0):
+    """The oracle, as it stands, on rows of request 0 (64 query tokens at a time, all
+    heads, the longest rows first) until the budget is spent; algorithmic TFLOP/s of the
+    rows it finished."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -310,6 +399,10 @@ def oracle_prefill_baseline(case, budget_s=12.0):
         extra = dict(kv_dtype="nvfp4", k_scale=case.k_scale, v_scale=case.v_scale,
                      k_sf=case.k_sf.contiguous().cpu().numpy(),
                      v_sf=case.v_sf.contiguous().cpu().numpy())
+    elif case.kv_dtype == "fp8":
+        kp = case.k_pool.contiguous().cpu().view(torch.uint8).numpy()
+        vp = case.v_pool.contiguous().cpu().view(torch.uint8).numpy()
+        extra = dict(kv_dtype="fp8", k_scale=case.k_scale, v_scale=case.v_scale)
     else:
         kp = case.k_pool.contiguous().cpu().view(dt).numpy().view(np.uint16)
         vp = case.v_pool.contiguous().cpu().view(dt).numpy().view(np.uint16)
@@ -336,6 +429,50 @@ def oracle_prefill_baseline(case, budget_s=12.0):
             "kind": "oracle",
             "sample": f"{rows} of {int(case.qo_lens.sum())} query tokens (all heads) of "
                       f"request 0, fp64 numpy on {cpu_model()}, {spent:.1f} s"}
+
+
+def oracle_extend_baseline(case, budget_s=12.0):
+    """The oracle, as it stands, on whole requests of the short-query workload (all their new
+    tokens and heads), request after request until the budget is spent; algorithmic GB/s of
+    the requests it finished."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from synth import extract_requests
+
+    threads = cpu_threads()
+    done, spent, nbytes = [], 0.0, 0
+    with threadpool_limits(limits=threads):
+        while spent < budget_s:
+            for b in range(case.batch):
+                sub = extract_requests(case, [b])
+                kp = sub["k_pool"].contiguous().view(torch.int16).numpy().view(np.uint16)
+                vp = sub["v_pool"].contiguous().view(torch.int16).numpy().view(np.uint16)
+                q = oracle.bf16_bits_to_f64(
+                    sub["q"].contiguous().view(torch.int16).numpy().view(np.uint16))
+                t0 = time.perf_counter()
+                oracle.prefill_ref(q, sub["qo_indptr"], kp, vp, sub["kv_indptr"],
+                                   sub["kv_indices"], sub["kv_last_page_len"], case.page_size,
+                                   case.sm_scale, causal=case.causal, window=case.window)
+                spent += time.perf_counter() - t0
+                done.append(b)
+                if spent >= budget_s:
+                    break
+    one = extend_algorithmic_bytes(case) / case.batch  # every request has the same shape
+    return {"value": round(one * len(done) / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(done)} whole requests ({case.qo_lens[0]} new tokens each, all heads), "
+                      f"fp64 numpy on {cpu_model()}, {spent:.1f} s"}
+
+
+def cpu_baseline_for(res, budget_s):
+    case = res["case"]
+    if res.get("kind") == "extend":
+        return oracle_extend_baseline(case, budget_s)
+    if "flops" in res:
+        return oracle_prefill_baseline(case, budget_s)
+    return oracle_decode_baseline(case, budget_s)
 
 
 # ----------------------------------------------------------------------------- counters
@@ -368,7 +505,7 @@ def decode_config(case):
             "kv_len_mean": float(case.kv_lens.mean()), "out_dtype": case.out_dtype}
 
 
-def measure_decode(name, steps, warmup, variant=None):
+def measure_decode(name, steps, warmup, variant=None, profile=False):
     import torch
     from synth import decode_workload
     case = decode_workload(name, device="cuda", variant=variant)
@@ -376,7 +513,13 @@ def measure_decode(name, steps, warmup, variant=None):
         case.name = f"{name}_{variant}"
     elif variant is not None:
         case.name = f"{name}_d{variant[0]}_p{variant[1]}"
-    step_ms, part_ms, merge_ms, wall_ms, plan = time_decode(case, steps, warmup)
+    # Sliding window at head_dim 256: the visible KV (~0.4 GB) is close to the 256 MB
+    # last-level cache, so the timed loops alternate between two copies of the pool.
+    copies = 2 if name == "window_decode" and case.head_dim_qk == 256 else 1
+    step_ms, part_ms, merge_ms, wall_ms, plan, proto = time_decode(case, steps, warmup, copies,
+                                                                   profile)
+    if profile:
+        return {"case": case, "profiled_calls": warmup + steps, "pool_copies": copies}
     nbytes = decode_algorithmic_bytes(case)
     achieved = nbytes / (part_ms * 1e-3) / 1e9
     res = {
@@ -391,15 +534,18 @@ def measure_decode(name, steps, warmup, variant=None):
         "plan": {"segments": plan.num_items, "waves": plan.num_workers,
                  "merged_pairs": plan.num_merges, "partial_slots": plan.num_slots,
                  "max_wave_blocks": plan.chunk_blocks},
+        "protocol": dict(proto, pool_copies=copies),
     }
     return res
 
 
-def measure_prefill(name, steps, warmup, head_dim_vo):
+def measure_prefill(name, steps, warmup, head_dim_vo, profile=False):
     from synth import prefill_workload
     case = prefill_workload(name, device="cuda", head_dim_vo=head_dim_vo)
     case.name = f"{name}_qk512_vo{head_dim_vo}"
-    step_ms, kern_ms, wall_ms, plan = time_prefill(case, steps, warmup)
+    step_ms, kern_ms, wall_ms, plan, proto = time_prefill(case, steps, warmup, profile)
+    if profile:
+        return {"case": case, "profiled_calls": warmup + steps}
     flops = prefill_algorithmic_flops(case)
     achieved = flops / (kern_ms * 1e-3) / 1e12
     return {
@@ -410,25 +556,29 @@ def measure_prefill(name, steps, warmup, head_dim_vo):
                      "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic_for(case.name), "kernel": "prefill_kernel",
                      "algorithmic_flops_per_launch": flops, "kernel_avg_ms": round(kern_ms, 5)},
+        "protocol": proto,
     }
 
 
-def measure_extend(name, steps, warmup):
+def measure_extend(name, steps, warmup, profile=False):
     """Short-query extend: the whole call (prefill kernel over key chunks + merge) against
     the algorithmic HBM bytes."""
     from synth import prefill_workload
     case = prefill_workload(name, device="cuda", head_dim_vo=512)
-    step_ms, kern_ms, wall_ms, plan = time_prefill(case, steps, warmup)
+    step_ms, kern_ms, wall_ms, plan, proto = time_prefill(case, steps, warmup, profile)
+    if profile:
+        return {"case": case, "profiled_calls": warmup + steps, "kind": "extend"}
     nbytes = extend_algorithmic_bytes(case)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     return {
-        "case": case, "bytes": nbytes, "step_ms": step_ms, "wall_ms": wall_ms,
-        "kernel_ms": kern_ms, "value": nbytes / (step_ms * 1e-3) / 1e9,
+        "case": case, "bytes": nbytes, "step_ms": step_ms, "wall_ms": wall_ms, "kind": "extend",
+        "kernel_ms": kern_ms, "value": nbytes / (step_ms * 1e-3) / 1e9, "protocol": proto,
         "plan": {"items": plan.num_items, "split_tiles": plan.num_merges,
                  "partial_slots": plan.num_slots, "chunk_stages": plan.chunk_blocks},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "prefill_kernel + prefill_merge_kernel",
+                     "traffic": traffic_for(case.name),
+                     "kernel": "prefill_kernel + prefill_merge_kernel",
                      "algorithmic_bytes_per_launch": nbytes, "kernel_avg_ms": round(kern_ms, 5)},
     }
 
@@ -453,10 +603,14 @@ def main():
     ap.add_argument("--workload", default="gqa_decode",
                     help="gqa_decode | gqa_decode_splitk8 | fp8_decode | nvfp4_decode | "
                          "window_decode_d512_p1 | ... | "
-                         "causal_prefill_vo512 | causal_prefill_vo256 | nvfp4_prefill | "
-                         "extend_prefill")
+                         "causal_prefill_vo512 | causal_prefill_vo256 | fp8_prefill_vo512 | "
+                         "fp8_prefill_vo256 | nvfp4_prefill | extend_prefill")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="run only warmup + steps launches of the workload (for rocprofv3)")
+    ap.add_argument("--baseline-seconds", type=float, default=10.0,
+                    help="oracle time for the headline's cpu_baseline (secondaries: a quarter)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -472,25 +626,37 @@ def main():
         copy_calibration()
         return
 
-    def run_named(wl):
+    def run_named(wl, profile=False):
+        st, wu = args.steps, args.warmup
         if wl.startswith("window_decode_d"):
             d, p = wl[len("window_decode_d"):].split("_p")
-            return measure_decode("window_decode", args.steps, args.warmup, (int(d), int(p)))
+            return measure_decode("window_decode", st, wu, (int(d), int(p)), profile)
         if wl.startswith("causal_prefill_vo"):
-            return measure_prefill("causal_prefill", args.steps, args.warmup,
-                                   int(wl[len("causal_prefill_vo"):]))
+            return measure_prefill("causal_prefill", st, wu, int(wl[len("causal_prefill_vo"):]),
+                                   profile)
+        if wl.startswith("fp8_prefill_vo"):
+            return measure_prefill("fp8_prefill", st, wu, int(wl[len("fp8_prefill_vo"):]),
+                                   profile)
         if wl == "extend_prefill":
-            return measure_extend(wl, args.steps, args.warmup)
+            return measure_extend(wl, st, wu, profile)
         if wl == "nvfp4_prefill":
-            return measure_prefill(wl, args.steps, args.warmup, 256)
+            return measure_prefill(wl, st, wu, 256, profile)
         if wl.startswith("gqa_decode_splitk"):
-            return measure_decode("gqa_decode", args.steps, args.warmup,
-                                  wl[len("gqa_decode_"):])
-        return measure_decode(wl, args.steps, args.warmup)
+            return measure_decode("gqa_decode", st, wu, wl[len("gqa_decode_"):], profile)
+        return measure_decode(wl, st, wu, None, profile)
+
+    if args.profile:
+        r = run_named(args.workload, profile=True)
+        print(json.dumps({"profile": args.workload, "workload": r["case"].name,
+                          "calls": r["profiled_calls"], "warmup": args.warmup,
+                          "steps": args.steps,
+                          "kernel_source_hash": {f: kernel_source_hash(f)
+                                                 for f in KERNEL_SOURCES}}), flush=True)
+        return
 
     main_res = run_named(args.workload)
     case = main_res["case"]
-    is_prefill = "flops" in main_res or args.workload == "extend_prefill"
+    is_prefill = "flops" in main_res or main_res.get("kind") == "extend"
     line = {
         "metric": METRIC,
         "value": round(main_res["value"], 3),
@@ -506,6 +672,7 @@ def main():
             "num_kv_heads": case.num_kv_heads, "head_dim_qk": case.head_dim_qk,
             "head_dim_vo": case.head_dim_vo, "page_size": case.page_size, "causal": True},
         "roofline": main_res["roofline"],
+        "protocol": main_res["protocol"],
         "wall_ms_per_step": round(main_res["wall_ms"], 5),
         "kernel_source_hash": {f: kernel_source_hash(f) for f in KERNEL_SOURCES},
     }
@@ -516,34 +683,33 @@ def main():
     if "plan" in main_res:
         line["plan"] = main_res["plan"]
     if not args.no_cpu_baseline:
-        if is_prefill:
-            line["cpu_baseline"] = oracle_prefill_baseline(case)
-        else:
-            line["cpu_baseline"] = oracle_decode_baseline(case)
+        line["cpu_baseline"] = cpu_baseline_for(main_res, args.baseline_seconds)
     del main_res, case
     torch.cuda.empty_cache()
 
     if not args.no_secondary:
         sec = {}
         names = ["gqa_decode", "gqa_decode_splitk8", "fp8_decode", "nvfp4_decode",
-                 "window_decode_d512_p1",
-                 "window_decode_d512_p32",
-                 "window_decode_d256_p1", "window_decode_d256_p32", "causal_prefill_vo512",
-                 "causal_prefill_vo256", "nvfp4_prefill", "extend_prefill"]
+                 "window_decode_d512_p1", "window_decode_d512_p32",
+                 "window_decode_d256_p1", "window_decode_d256_p32",
+                 "causal_prefill_vo512", "causal_prefill_vo256",
+                 "fp8_prefill_vo512", "fp8_prefill_vo256", "nvfp4_prefill", "extend_prefill"]
         for wl in names:
             if wl == args.workload:
                 continue
             try:
                 r = run_named(wl)
+                unit = "TFLOP/s" if "flops" in r else "GB/s"
+                sec[wl] = {"value": round(r["value"], 3), "unit": unit,
+                           "ms_per_step": round(r["step_ms"], 5), "roofline": r["roofline"],
+                           "protocol": r["protocol"]}
+                if "plan" in r and wl == "extend_prefill":
+                    sec[wl]["plan"] = r["plan"]
+                if not args.no_cpu_baseline:
+                    sec[wl]["cpu_baseline"] = cpu_baseline_for(r, args.baseline_seconds / 4)
             except Exception as e:  # report, keep measuring the rest
                 sec[wl] = {"error": f"{type(e).__name__}: {e}"}
-                continue
-            unit = "TFLOP/s" if "flops" in r else "GB/s"
-            sec[wl] = {"value": round(r["value"], 3), "unit": unit,
-                       "ms_per_step": round(r["step_ms"], 5), "roofline": r["roofline"]}
-            if "plan" in r and wl == "extend_prefill":
-                sec[wl]["plan"] = r["plan"]
-            del r
+            r = None
             torch.cuda.empty_cache()
         line["secondary"] = sec
     print(json.dumps(line), flush=True)

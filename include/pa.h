@@ -116,7 +116,9 @@ typedef struct pa_page_table {
 typedef struct pa_attn_params {
   int32_t num_qo_heads;            /* multiple of num_kv_heads; query head h reads KV head
                                       h / (num_qo_heads / num_kv_heads)                  */
-  float sm_scale;                  /* scores are sm_scale * q.k (e.g. 1/sqrt(head_dim_qk)) */
+  float sm_scale;                  /* scores are sm_scale * q.k (e.g. 1/sqrt(head_dim_qk));
+                                      any finite value: 0 weighs every visible key the same,
+                                      a negative scale reverses the order of the scores   */
   int32_t window;                  /* > 0: a query at position p sees keys t > p - window;
                                       <= 0: no window                                      */
   int32_t causal;                  /* prefill: nonzero = causal; decode ignores it (the one
@@ -200,7 +202,12 @@ pa_status pa_validate_page_table_host(const int32_t* kv_indptr_host,
                                       int32_t num_pages, int32_t page_size);
 
 /* Plans a decode batch from host copies of kv_indptr and kv_last_page_len (the device
- * copies passed to pa_paged_decode must hold the same values).  The work is the set of
+ * copies passed to pa_paged_decode must hold the same values).  The split of the key axis
+ * into chunks merged by log-sum-exp is flash-decoding (the Triton page, sections
+ * "Approach" and "Not covered"; the FlashInfer page, section "NVFP4 split-KV correctness
+ * (added)", on split-KV for a short query over a long cache); a plan made once on the host
+ * and run many times is the plan()/run() split of the FlashInfer page's commits.  The
+ * result does not depend on the partition.  The work is the set of
  * (request, kv head, 16-token key block) units; each wave of the partial kernel runs one
  * piece of them: the units, flattened in (request, kv head, block) order, are cut into
  * P near-equal pieces, at most one wave per SIMD slot of the 256 CUs at two waves per SIMD
@@ -221,8 +228,10 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
                          int32_t batch, int32_t num_splits, void* plan_buf_host,
                          size_t plan_buf_bytes, pa_plan* plan);
 
-/* Plans a prefill batch.  qo_indptr_host [batch + 1] gives each request's new tokens,
- * which must not outnumber its KV tokens; row i of request b sits at key position
+/* Plans a prefill batch (the Triton page, section "Approach": causal attention of the new
+ * tokens over the paged cache, in one branch with decode; section "Not covered": the new
+ * tokens versus the cached prefix).  qo_indptr_host [batch + 1] gives each request's new
+ * tokens, which must not outnumber its KV tokens; row i of request b sits at key position
  * L_b - q_len_b + i.  Query rows of one (request, KV head) are the (token, head) pairs of
  * its head group, tiled in plan->tile_rows; a tile sees the keys some of its rows see.
  * Split-K for short queries over long KV: when tiles x num_kv_heads < 512, every tile
@@ -232,20 +241,25 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
  * merge combines them (plan->num_merges split tiles, plan->num_slots slots,
  * plan->chunk_blocks = C, 0 without splitting).  Items run by key count, longest first.
  * The result does not depend on the split.  Same two-call sizing as pa_decode_plan.
- * Supported: head dims (512,512), (256,256), (512,256); kv bf16 or nvfp4; q bf16; out fp32 or bf16;
- * num_qo_heads / num_kv_heads <= 16.  Never calls HIP. */
+ * Supported: head dims (512,512), (256,256), (512,256); kv bf16, FP8 E4M3FN or NVFP4; q bf16;
+ * out fp32 or bf16; num_qo_heads / num_kv_heads <= 16.  Never calls HIP. */
 pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache,
                           const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
                           const int32_t* kv_last_page_len_host, int32_t batch,
                           void* plan_buf_host, size_t plan_buf_bytes, pa_plan* plan);
 
 /* Copies plan->plan_bytes from plan_buf_host to the start of the device workspace
- * (stream-ordered hipMemcpyAsync).  The host buffer must stay unchanged until the copy
+ * (stream-ordered hipMemcpyAsync).  The workspace is preallocated by the caller and reused
+ * by every run of the plan (the Triton page, section "Not covered", names per-call
+ * workspace allocation as the cost to avoid).  The host buffer must stay unchanged until the copy
  * has run.  The run calls read the work items from there, so upload once per plan. */
 pa_status pa_plan_upload(const pa_plan* plan, const void* plan_buf_host, void* workspace,
                          size_t workspace_bytes, void* stream);
 
-/* Enqueues one decode step: q [batch, num_qo_heads, head_dim_qk] bf16 (contiguous) ->
+/* Enqueues one decode step (the Triton page, sections "Approach" and "Test Coverage":
+ * single-token paged decode over the HND cache, split-K, with sliding windows and FP8 KV
+ * cast on load; the FlashInfer page, section "Summary": head_dim_vo may differ from
+ * head_dim_qk, with V in its own pool): q [batch, num_qo_heads, head_dim_qk] bf16 (contiguous) ->
  * out [batch, num_qo_heads, head_dim_vo] in params->out_dtype, and, if lse != NULL,
  * lse [batch, num_qo_heads] fp32 (natural log; -inf for a request with no keys, whose
  * output row is zero).  workspace: device buffer of at least plan->workspace_bytes
@@ -271,9 +285,12 @@ pa_status pa_paged_decode_merge(const pa_plan* plan, const void* q, const pa_kv_
                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
-/* Enqueues one prefill: q [total_q, num_qo_heads, head_dim_qk] bf16 (contiguous, ragged
- * by qo_indptr) -> out [total_q, num_qo_heads, head_dim_vo] in params->out_dtype and
- * optional lse [total_q, num_qo_heads] fp32.  qo_indptr is the device copy of the array
+/* Enqueues one prefill (the Triton page, section "Approach": causal paged prefill, FP8 KV
+ * cast on load in both phases; the FlashInfer page, sections "Summary" and "What's in it":
+ * head_dim_qk 512 with head_dim_vo 256 over separate pools, NVFP4 KV): q [total_q,
+ * num_qo_heads, head_dim_qk] bf16 (contiguous, ragged by qo_indptr) -> out [total_q,
+ * num_qo_heads, head_dim_vo] in params->out_dtype and optional lse [total_q, num_qo_heads]
+ * fp32 (NULL: not written).  qo_indptr is the device copy of the array
  * given to pa_prefill_plan.  One kernel launch, or two when the plan splits tiles (the
  * chunk partials go to the workspace, then a merge kernel writes their rows). */
 pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const int32_t* qo_indptr,
@@ -282,8 +299,10 @@ pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const int32_t* qo
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Copies the stored K and V elements of (request, kv_head) in logical token order, through
- * the same address path as the attention kernels: k_out [kv_len, head_dim_qk] and
- * v_out [kv_len, head_dim_vo] in the cache's element type.  kv_len must equal the
+ * the same address path as the attention kernels (page-table semantics of the Triton page,
+ * section "Approach"): k_out [kv_len, head_dim_qk] and v_out [kv_len, head_dim_vo] in the
+ * cache's element type; for NVFP4 each row is the packed data (head_dim / 2 bytes)
+ * followed by its block-scale codes (head_dim / 16 bytes).  kv_len must equal the
  * request's length.  For bit-exact checks of the page-table handling. */
 pa_status pa_debug_gather_kv(const pa_kv_cache* cache, const pa_page_table* table,
                              int32_t request, int32_t kv_len, int32_t kv_head, void* k_out,
@@ -292,8 +311,9 @@ pa_status pa_debug_gather_kv(const pa_kv_cache* cache, const pa_page_table* tabl
 /* Converts n FP8 E4M3FN codes to fp32 with the same conversion the kernels use. */
 pa_status pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int32_t n, void* stream);
 
-const char* pa_last_error(void);   /* thread-local message of the last failing call */
-uint64_t pa_launch_count(void);    /* kernels launched by this process so far         */
+const char* pa_last_error(void);        /* thread-local message of the last failing call */
+uint64_t pa_launch_count(void);         /* kernels launched by this process so far         */
+uint64_t pa_debug_launch_count(void);   /* the same count, under its introspection name    */
 const char* pa_version(void);
 
 #ifdef __cplusplus

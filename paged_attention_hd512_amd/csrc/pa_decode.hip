@@ -59,9 +59,6 @@ namespace pa {
 
 constexpr int kDecodeWavesPerGroup = 8;  // the two waves of every SIMD of a CU
 
-// Stored KV formats of the decode kernel.
-constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvFp4 = 2;
-
 struct DecodeArgs {
   const uint16_t* q;           // [B, Hq, DQK] bf16 bits
   const char* k;               // byte base of the K pool
@@ -652,24 +649,44 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a) {
 }
 
 // Copies the rows of one (request, KV head) in logical order, through the same address
-// path as the attention kernels.  One workgroup per key.
-__global__ __launch_bounds__(64) void gather_kv_kernel(const char* k, const char* v, int64_t k_sp,
-                                                       int64_t k_sh, int64_t k_st, int64_t v_sp,
-                                                       int64_t v_sh, int64_t v_st,
-                                                       const int32_t* kv_indptr,
-                                                       const int32_t* kv_indices, int32_t b,
-                                                       int32_t head, int32_t page_size,
-                                                       int32_t k_row_bytes, int32_t v_row_bytes,
-                                                       int32_t esz, char* k_out, char* v_out) {
+// path as the attention kernels.  One workgroup per key.  NVFP4: each output row is the
+// packed data row followed by its block-scale row.
+struct GatherArgs {
+  const char* k;
+  const char* v;
+  int64_t k_sp, k_sh, k_st, v_sp, v_sh, v_st;        // strides in stored units
+  const char* k_sf;                                   // NVFP4 block scales, else null
+  const char* v_sf;
+  int64_t ks_sp, ks_sh, ks_st, vs_sp, vs_sh, vs_st;  // bytes
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  int32_t b, head, page_size, esz;                    // esz: bytes per stride unit
+  int32_t k_row_bytes, v_row_bytes;                   // data bytes per row
+  int32_t ks_row_bytes, vs_row_bytes;                 // block-scale bytes per row (0: none)
+  char* k_out;
+  char* v_out;
+};
+
+__device__ __forceinline__ void copy_row16(char* dst, const char* src, int bytes) {
+  for (int c = threadIdx.x; c < bytes / 16; c += 64)
+    *(u32x4_t*)(dst + 16 * c) = *(const u32x4_t*)(src + 16 * c);
+}
+
+__global__ __launch_bounds__(64) void gather_kv_kernel(GatherArgs a) {
   const int t = blockIdx.x;
   int32_t page, slot;
-  token_page_slot(kv_indices + kv_indptr[b], t, page_size, page, slot);
-  const char* ks = k + row_elem_offset(page, head, slot, k_sp, k_sh, k_st) * esz;
-  const char* vs = v + row_elem_offset(page, head, slot, v_sp, v_sh, v_st) * esz;
-  for (int c = threadIdx.x; c < k_row_bytes / 16; c += 64)
-    *(u32x4_t*)(k_out + (int64_t)t * k_row_bytes + 16 * c) = *(const u32x4_t*)(ks + 16 * c);
-  for (int c = threadIdx.x; c < v_row_bytes / 16; c += 64)
-    *(u32x4_t*)(v_out + (int64_t)t * v_row_bytes + 16 * c) = *(const u32x4_t*)(vs + 16 * c);
+  token_page_slot(a.kv_indices + a.kv_indptr[a.b], t, a.page_size, page, slot);
+  const int64_t k_out_row = a.k_row_bytes + a.ks_row_bytes, v_out_row = a.v_row_bytes + a.vs_row_bytes;
+  char* ko = a.k_out + (int64_t)t * k_out_row;
+  char* vo = a.v_out + (int64_t)t * v_out_row;
+  copy_row16(ko, a.k + row_elem_offset(page, a.head, slot, a.k_sp, a.k_sh, a.k_st) * a.esz, a.k_row_bytes);
+  copy_row16(vo, a.v + row_elem_offset(page, a.head, slot, a.v_sp, a.v_sh, a.v_st) * a.esz, a.v_row_bytes);
+  if (a.ks_row_bytes > 0) {
+    copy_row16(ko + a.k_row_bytes,
+               a.k_sf + row_elem_offset(page, a.head, slot, a.ks_sp, a.ks_sh, a.ks_st), a.ks_row_bytes);
+    copy_row16(vo + a.v_row_bytes,
+               a.v_sf + row_elem_offset(page, a.head, slot, a.vs_sp, a.vs_sh, a.vs_st), a.vs_row_bytes);
+  }
 }
 
 __global__ void fp8_to_f32_kernel(const uint8_t* codes, float* out, int n) {
@@ -716,6 +733,7 @@ using namespace pa;
 
 extern "C" {
 
+
 pa_status pa_plan_upload(const pa_plan* plan, const void* plan_buf_host, void* workspace,
                          size_t workspace_bytes, void* stream) {
   if (!plan || !plan_buf_host) return fail(PA_ERR_INVALID_ARG, "plan or plan buffer is NULL");
@@ -730,20 +748,36 @@ pa_status pa_plan_upload(const pa_plan* plan, const void* plan_buf_host, void* w
   return PA_OK;
 }
 
-static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_cache* cache,
-                                const pa_page_table* table, const pa_attn_params* params,
-                                void* out, float* lse, void* workspace, size_t workspace_bytes,
-                                void* stream, bool run_partial, bool run_merge) {
+// Argument checks of a decode run; *nothing_to_do is set when the plan holds no work.
+static pa_status decode_check(const pa_plan* plan, const void* q, const pa_kv_cache* cache,
+                              const pa_page_table* table, const pa_attn_params* params,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              bool* nothing_to_do) {
+  *nothing_to_do = false;
   pa_status st = check_cache(cache, true);
   if (st != PA_OK) return st;
   if ((st = check_params(params, cache, kMaxDecodeGroup)) != PA_OK) return st;
   if ((st = check_plan_matches(plan, 1, params, cache, table, workspace_bytes)) != PA_OK) return st;
-  if (plan->num_items == 0 && plan->num_merges == 0) return PA_OK;
+  if (plan->num_items == 0 && plan->num_merges == 0) {
+    *nothing_to_do = true;
+    return PA_OK;
+  }
   if (!q || !out) return fail(PA_ERR_INVALID_ARG, "q or out is NULL");
   if (!workspace) return fail(PA_ERR_INVALID_ARG, "workspace is NULL");
   if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)workspace) & 15)
     return fail(PA_ERR_UNSUPPORTED, "q, out and workspace must be 16-byte aligned");
   if ((uintptr_t)lse & 3) return fail(PA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  return PA_OK;
+}
+
+static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_cache* cache,
+                                const pa_page_table* table, const pa_attn_params* params,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream, bool run_partial, bool run_merge) {
+  bool nothing = false;
+  pa_status st = decode_check(plan, q, cache, table, params, out, lse, workspace,
+                              workspace_bytes, &nothing);
+  if (st != PA_OK || nothing) return st;
 
   const int group = params->num_qo_heads / cache->num_kv_heads;
   const int gmax = group <= 4 ? group : group <= 6 ? 6 : 8;
@@ -833,8 +867,6 @@ pa_status pa_debug_gather_kv(const pa_kv_cache* cache, const pa_page_table* tabl
                              void* v_out, void* stream) {
   pa_status st = check_cache(cache, true);
   if (st != PA_OK) return st;
-  if (cache->kv_dtype == PA_DTYPE_NVFP4)
-    return fail(PA_ERR_UNSUPPORTED, "the debug gather copies bf16 and fp8 caches only");
   if (!table || !table->kv_indptr || !table->kv_indices)
     return fail(PA_ERR_INVALID_ARG, "page table is NULL");
   if (request < 0 || request >= table->batch) return fail(PA_ERR_INVALID_ARG, "request out of range");
@@ -843,12 +875,29 @@ pa_status pa_debug_gather_kv(const pa_kv_cache* cache, const pa_page_table* tabl
   if (kv_len == 0) return PA_OK;
   if (!k_out || !v_out || (((uintptr_t)k_out | (uintptr_t)v_out) & 15))
     return fail(PA_ERR_INVALID_ARG, "k_out / v_out must be non-NULL and 16-byte aligned");
-  const int esz = dtype_bytes(cache->kv_dtype);
-  gather_kv_kernel<<<kv_len, 64, 0, (hipStream_t)stream>>>(
-      (const char*)cache->k, (const char*)cache->v, cache->k_stride_page, cache->k_stride_head,
-      cache->k_stride_token, cache->v_stride_page, cache->v_stride_head, cache->v_stride_token,
-      table->kv_indptr, table->kv_indices, request, kv_head, cache->page_size,
-      cache->head_dim_qk * esz, cache->head_dim_vo * esz, esz, (char*)k_out, (char*)v_out);
+  const bool fp4 = cache->kv_dtype == PA_DTYPE_NVFP4;
+  GatherArgs g;
+  g.k = (const char*)cache->k;
+  g.v = (const char*)cache->v;
+  g.k_sp = cache->k_stride_page; g.k_sh = cache->k_stride_head; g.k_st = cache->k_stride_token;
+  g.v_sp = cache->v_stride_page; g.v_sh = cache->v_stride_head; g.v_st = cache->v_stride_token;
+  g.k_sf = (const char*)cache->k_sf;
+  g.v_sf = (const char*)cache->v_sf;
+  g.ks_sp = cache->k_sf_stride_page; g.ks_sh = cache->k_sf_stride_head; g.ks_st = cache->k_sf_stride_token;
+  g.vs_sp = cache->v_sf_stride_page; g.vs_sh = cache->v_sf_stride_head; g.vs_st = cache->v_sf_stride_token;
+  g.kv_indptr = table->kv_indptr;
+  g.kv_indices = table->kv_indices;
+  g.b = request;
+  g.head = kv_head;
+  g.page_size = cache->page_size;
+  g.esz = fp4 ? 1 : dtype_bytes(cache->kv_dtype);
+  g.k_row_bytes = fp4 ? cache->head_dim_qk / 2 : cache->head_dim_qk * g.esz;
+  g.v_row_bytes = fp4 ? cache->head_dim_vo / 2 : cache->head_dim_vo * g.esz;
+  g.ks_row_bytes = fp4 ? cache->head_dim_qk / 16 : 0;
+  g.vs_row_bytes = fp4 ? cache->head_dim_vo / 16 : 0;
+  g.k_out = (char*)k_out;
+  g.v_out = (char*)v_out;
+  gather_kv_kernel<<<kv_len, 64, 0, (hipStream_t)stream>>>(g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "gather kernel launch: %s", hipGetErrorString(e));
   count_launches(1);

@@ -17,6 +17,9 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Stored KV formats, as kernel template arguments.
+constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvFp4 = 2;
+
 // ---------------------------------------------------------------- element conversions
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }

@@ -184,6 +184,7 @@ extern "C" {
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 uint64_t pa_launch_count(void) { return g_launches.load(std::memory_order_relaxed); }
+uint64_t pa_debug_launch_count(void) { return pa_launch_count(); }
 const char* pa_version(void) { return "libpa 0.1.0 (gfx950)"; }
 
 pa_status pa_kv_cache_hnd(const void* base, int32_t kv_dtype, int32_t num_pages,
@@ -478,8 +479,6 @@ pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache
   if (!plan) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
   pa_status st = check_cache(cache, false);
   if (st != PA_OK) return st;
-  if (cache->kv_dtype != PA_DTYPE_BF16 && cache->kv_dtype != PA_DTYPE_NVFP4)
-    return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 and nvfp4 KV");
   if ((st = check_params(params, cache, kMaxPrefillGroup)) != PA_OK) return st;
   if ((st = check_table_host(kv_indptr_host, kv_last_page_len_host, batch, cache->page_size)) != PA_OK)
     return st;

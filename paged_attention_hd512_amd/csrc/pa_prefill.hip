@@ -28,11 +28,16 @@
 // Every wave reads the whole K and V stage from LDS (64 KB at 512/512) for its 16 rows: 1 KB
 // of LDS reads per 16-clock MFMA, so the MFMA pipes run only as fast as the LDS delivers
 // (256 B per clock per CU at most) and as its latency is hidden.
-// NVFP4 KV (the FlashInfer page, sections "Summary" and "What's in it": packed E2M1 with one
-// E4M3 block scale per 16 head_dim elements): a direct-to-LDS copy cannot convert, so each
-// wave loads its key rows' packed bytes and block scales into registers when a stage's copy
-// would be issued and writes them to LDS as bf16 (exact), in the same swizzled layout, at
-// the end of the interval, before the barrier that hands the stage over.
+// FP8 E4M3FN KV (the Triton page, section "Approach": FP8 caches are cast on load by the
+// same kernels in both phases) and NVFP4 KV (the FlashInfer page, sections "Summary" and
+// "What's in it": packed E2M1 with one E4M3 block scale per 16 head_dim elements): a
+// direct-to-LDS copy cannot convert, so each wave loads its key rows' codes (and block
+// scales) into registers and writes them to LDS as bf16 (exact for both formats), in the
+// same swizzled layout, before the barrier that hands the stage over.  k_scale folds into
+// the score scale and v_scale into the final normalisation.
+// The score scale may have any sign: the kernel works with |scale| and flips the sign bits
+// of Q when the scale is negative (a zero scale zeroes Q, so every visible key weighs the
+// same), so masks and running maxima are taken on scores that grow with the scaled ones.
 
 #include <hip/hip_runtime.h>
 
@@ -76,8 +81,10 @@ struct PrefillArgs {
   int32_t window;             // 0 = none
   int32_t causal;
   int32_t out_fp32;
-  float scale_log2;
-  float v_scale;              // NVFP4: tensor-wide V scale (1 otherwise)
+  float scale_log2;           // |sm_scale * k_scale| * log2(e) (1 * log2(e) for a zero scale)
+  uint32_t q_and;             // applied to every Q dword: zero for a zero scale
+  uint32_t q_xor;             // then this: the bf16 sign bits for a negative scale
+  float v_scale;              // FP8 / NVFP4: tensor-wide V scale (1 for bf16)
   const char* k_sf;           // NVFP4 block scales, else null
   const char* v_sf;
   int64_t ks_sp, ks_sh, ks_st;  // block-scale byte strides
@@ -156,8 +163,10 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <int DQK, int DVO, int PM, bool FP4>
+template <int DQK, int DVO, int PM, int KV>
 __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
+  constexpr bool CONV = KV != kKvBf16;  // stages pass through registers and are converted
+  constexpr bool FP4 = KV == kKvFp4;
   constexpr int NW = kPrefillWaves;
   constexpr int KS = kKeyStage;
   constexpr int QSTEPS = DQK / 32;          // MFMA K-steps of S^T
@@ -170,9 +179,9 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   static_assert(RPW == 4, "each wave copies four key rows per stage");
   // Read-ahead of the software pipelines (steps of S^T, tiles of O^T), bounded by the
   // registers left beside Q (DQK / 8 per lane) and O (DVO / 4 per lane).  Two steps of K at
-  // 512/512 fit in 253 VGPRs and measured ~1 % faster than one; the NVFP4 kernel, which
-  // already spills there, keeps one.
-  constexpr int KD = DVO == 512 ? (FP4 ? 1 : 2) : 4;
+  // 512/512 fit in 253 VGPRs and measured ~1 % faster than one; the converting kernels,
+  // which also hold a stage's codes in registers, keep one.
+  constexpr int KD = DVO == 512 ? (CONV ? 1 : 2) : 4;
   constexpr int VD = DVO == 512 ? 2 : 4;
 
   // K stages are double-buffered, V stages triple-buffered: half of the waves use a stage's
@@ -243,6 +252,8 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < QSTEPS; ++j)
       qf[j] = *(const u32x4_t*)(src + 32 * j);
+#pragma unroll
+    for (int j = 0; j < QSTEPS; ++j) qf[j] = (qf[j] & a.q_and) ^ a.q_xor;
   }
 
   // Copies key stage `st` into buffer SLOT.  Wave w moves key rows 4w .. 4w+3 of the stage
@@ -396,10 +407,66 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   };
 
-  // Copies stage st: K into buffer slot_c, V into v_lds + vo.
+  // FP8: lane l holds key row my_row + l / 16 of the stage and the sixteenth l % 16 of its
+  // K row (DQK / 16 codes, one or two 16-byte loads) and of its V row.  Key rows are clamped
+  // into the tile's range like the copies' (clamped keys are masked out).
+  constexpr int NK8 = DQK / 256, NV8 = DVO / 256;
+  u32x4_t f8k[NK8], f8v[NV8];
+  auto fp8_load = [&](int st) {
+    const int part = lane & 15;
+    int t = st * KS + my_row + (lane >> 4);
+    t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
+    const int j = t / a.page_size;
+    const int64_t pg = pages[j];
+    const int64_t sl = t - j * a.page_size;
+    const char* kd = a.k + pg * a.k_sp + (int64_t)kvh * a.k_sh + sl * a.k_st + (DQK / 16) * part;
+    const char* vd = a.v + pg * a.v_sp + (int64_t)kvh * a.v_sh + sl * a.v_st + (DVO / 16) * part;
+#pragma unroll
+    for (int i = 0; i < NK8; ++i) f8k[i] = *(const u32x4_t*)(kd + 16 * i);
+#pragma unroll
+    for (int i = 0; i < NV8; ++i) f8v[i] = *(const u32x4_t*)(vd + 16 * i);
+  };
+  // Widens the loaded codes to bf16 (exact) and writes them: the 16 codes of load i are the
+  // 8-element chunks (D / 128) * part + 2i and + 2i + 1 of the row, at chunk position
+  // chunk ^ swizzle(row).
+  auto fp8_store = [&](auto slot_c, int vo) {
+    const int row = my_row + (lane >> 4);
+    const int part = lane & 15;
+    auto chunk8 = [&](uint32_t w0, uint32_t w1) {
+      const u32x2_t lo = fp8x4_to_bf16x4(w0), hi = fp8x4_to_bf16x4(w1);
+      return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    };
+    uint16_t* kd = k_buf(slot_c) + row * DQK;
+#pragma unroll
+    for (int i = 0; i < NK8; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = (DQK / 128) * part + 2 * i + h;
+        *(u32x4_t*)(kd + 8 * (c ^ k_swz(row))) = chunk8(f8k[i][2 * h], f8k[i][2 * h + 1]);
+      }
+    uint16_t* vd = v_lds + vo + row * DVO;
+#pragma unroll
+    for (int i = 0; i < NV8; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = (DVO / 128) * part + 2 * i + h;
+        *(u32x4_t*)(vd + 8 * (c ^ v_swz(row))) = chunk8(f8v[i][2 * h], f8v[i][2 * h + 1]);
+      }
+    // The writes complete before this wave reaches the barrier that hands the stage over.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  };
+  auto conv_store = [&](auto slot_c, int vo) {
+    if constexpr (FP4) fp4_store(slot_c, vo);
+    else fp8_store(slot_c, vo);
+  };
+
+  // Copies stage st: K into buffer slot_c, V into v_lds + vo (converting formats: loads the
+  // codes into registers; conv_store then writes them).
   auto copy_stage = [&](int st, auto slot_c, int vo) {
     if constexpr (FP4) {
       fp4_load(st);
+    } else if constexpr (CONV) {
+      fp8_load(st);
     } else if constexpr (PM == kPagesStage) {
       copy_prep(st);
       static_for<NCOPY>([&](auto idx_c) { copy_one(idx_c, slot_c, vo); });
@@ -448,7 +515,11 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   // the MFMAs run; the second group issues none (as bursts at the interval start they stall
   // the issuing waves).  Other page sizes: every wave copies its own rows at the interval
   // start.
-  constexpr bool SPREAD = PM == kPagesStage && !FP4;
+  constexpr bool SPREAD = PM == kPagesStage && !CONV;
+  // Converting formats at 512/512: the first group loads the next stage's codes after its
+  // S^T (not before), and the second group stores them before its S^T, so the codes are
+  // never live beside the K operands of S^T, where the registers peak.
+  constexpr bool LATE = CONV && DQK == 512 && DVO == 512;
   // ---- S^T = K Q^T from K buffer kslot_c into s0 (keys 0..15) and s1 (keys 16..31); lane
   // holds keys 4*g4 + i.  With COPY the next stage's copies (K into the other buffer, V into
   // v_lds + vo_next) are issued among the steps.
@@ -596,7 +667,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   int vo_prev = 2 * VSTAGE, vo_cur = 0, vo_next = VSTAGE;
   if (st_first < st_end) {
     copy_stage(st_first, std::integral_constant<int, 0>{}, 0);
-    if constexpr (FP4) fp4_store(std::integral_constant<int, 0>{}, 0);
+    if constexpr (CONV) conv_store(std::integral_constant<int, 0>{}, 0);
   }
   auto interval = [&](int st, auto kslot_c, auto second_c) {
     wait_vmcnt<0>();
@@ -609,6 +680,9 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
         softmax(st - 1);
         pv(vo_prev);
       }
+      if constexpr (LATE) {
+        if (has_next) conv_store(other_c, vo_next);
+      }
       qk(kslot_c, std::false_type{}, vo_next);
     } else {
       if constexpr (SPREAD) {
@@ -618,6 +692,9 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
         } else {
           qk(kslot_c, std::false_type{}, vo_next);
         }
+      } else if constexpr (LATE) {
+        qk(kslot_c, std::false_type{}, vo_next);
+        if (has_next) copy_stage(st + 1, other_c, vo_next);
       } else {
         if (has_next) copy_stage(st + 1, other_c, vo_next);
         qk(kslot_c, std::false_type{}, vo_next);
@@ -625,8 +702,8 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
       softmax(st);
       pv(vo_cur);
     }
-    if constexpr (FP4) {
-      if (has_next) fp4_store(other_c, vo_next);
+    if constexpr (CONV && !(LATE && decltype(second_c)::value)) {
+      if (has_next) conv_store(other_c, vo_next);
     }
     const int t = vo_prev;
     vo_prev = vo_cur;
@@ -655,7 +732,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   const float l_bf_tot = sum_xor32(sum_xor16(l_bf));
   if (!row_valid) return;
   float inv = l_bf_tot > 0.f ? 1.f / l_bf_tot : 0.f;
-  if constexpr (FP4) inv *= a.v_scale;
+  if constexpr (CONV) inv *= a.v_scale;
   if (it.slot >= 0) {
     // One key chunk of a split tile: its normalised output and two log-sum-exps, over the
     // bf16-rounded weights (the merge weights, so the merged output is normalised by the
@@ -754,11 +831,12 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeArgs a) 
 }
 
 template <int DQK, int DVO>
-static void launch_prefill(const PrefillArgs& a, int pm, bool fp4, int grid, hipStream_t s) {
-  if (fp4) prefill_kernel<DQK, DVO, kPagesAny, true><<<grid, 512, 0, s>>>(a);
-  else if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, false><<<grid, 512, 0, s>>>(a);
-  else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2, false><<<grid, 512, 0, s>>>(a);
-  else prefill_kernel<DQK, DVO, kPagesAny, false><<<grid, 512, 0, s>>>(a);
+static void launch_prefill(const PrefillArgs& a, int pm, int kv, int grid, hipStream_t s) {
+  if (kv == kKvFp4) prefill_kernel<DQK, DVO, kPagesAny, kKvFp4><<<grid, 512, 0, s>>>(a);
+  else if (kv == kKvFp8) prefill_kernel<DQK, DVO, kPagesAny, kKvFp8><<<grid, 512, 0, s>>>(a);
+  else if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvBf16><<<grid, 512, 0, s>>>(a);
+  else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2, kKvBf16><<<grid, 512, 0, s>>>(a);
+  else prefill_kernel<DQK, DVO, kPagesAny, kKvBf16><<<grid, 512, 0, s>>>(a);
 }
 
 }  // namespace pa
@@ -771,9 +849,9 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
                                       void* workspace, size_t workspace_bytes, void* stream) {
   pa_status st = check_cache(cache, true);
   if (st != PA_OK) return st;
-  if (cache->kv_dtype != PA_DTYPE_BF16 && cache->kv_dtype != PA_DTYPE_NVFP4)
-    return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 and nvfp4 KV");
-  const bool fp4 = cache->kv_dtype == PA_DTYPE_NVFP4;
+  const int kv = cache->kv_dtype == PA_DTYPE_NVFP4        ? kKvFp4
+                 : cache->kv_dtype == PA_DTYPE_FP8_E4M3FN ? kKvFp8
+                                                          : kKvBf16;
   if ((st = check_params(params, cache, kMaxPrefillGroup)) != PA_OK) return st;
   if ((st = check_plan_matches(plan, 2, params, cache, table, workspace_bytes)) != PA_OK) return st;
   if (plan->num_items == 0) return PA_OK;
@@ -787,14 +865,14 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   a.q = (const uint16_t*)q;
   a.k = (const char*)cache->k;
   a.v = (const char*)cache->v;
-  const int64_t unit = fp4 ? 1 : 2;  // bytes per stride unit
+  const int64_t unit = kv == kKvBf16 ? 2 : 1;  // bytes per stride unit
   a.k_sp = unit * cache->k_stride_page; a.k_sh = unit * cache->k_stride_head; a.k_st = unit * cache->k_stride_token;
   a.v_sp = unit * cache->v_stride_page; a.v_sh = unit * cache->v_stride_head; a.v_st = unit * cache->v_stride_token;
   a.k_sf = (const char*)cache->k_sf;
   a.v_sf = (const char*)cache->v_sf;
   a.ks_sp = cache->k_sf_stride_page; a.ks_sh = cache->k_sf_stride_head; a.ks_st = cache->k_sf_stride_token;
   a.vs_sp = cache->v_sf_stride_page; a.vs_sh = cache->v_sf_stride_head; a.vs_st = cache->v_sf_stride_token;
-  a.v_scale = fp4 ? cache->v_scale : 1.f;
+  a.v_scale = cache->v_scale;  // 1 for bf16 (checked)
   a.kv_indptr = table->kv_indptr;
   a.kv_indices = table->kv_indices;
   a.items = (const PrefillItem*)(ws + plan->items_offset);
@@ -810,7 +888,12 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   a.window = params->window > 0 ? params->window : 0;
   a.causal = params->causal ? 1 : 0;
   a.out_fp32 = params->out_dtype == PA_DTYPE_FP32;
-  a.scale_log2 = params->sm_scale * (fp4 ? cache->k_scale : 1.f) * kLog2e;
+  // Scores are sm_scale * k_scale * q.k (k_scale is 1 for bf16).  The kernel takes |scale|
+  // and transforms Q: sign bits flipped for a negative scale, zeroed for a zero one.
+  const float sc = params->sm_scale * cache->k_scale;
+  a.scale_log2 = (sc == 0.f ? 1.f : fabsf(sc)) * kLog2e;
+  a.q_and = sc == 0.f ? 0u : 0xFFFFFFFFu;
+  a.q_xor = sc < 0.f ? 0x80008000u : 0u;
   const int grid = plan->num_items * cache->num_kv_heads;
   hipStream_t s = (hipStream_t)stream;
   const int dqk = cache->head_dim_qk, dvo = cache->head_dim_vo;
@@ -823,9 +906,9 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   const int pm = P % kKeyStage == 0 && page_fits_u32
                      ? kPagesStage
                      : ((P & (P - 1)) == 0 ? kPagesPow2 : kPagesAny);
-  if (dqk == 512 && dvo == 512) launch_prefill<512, 512>(a, pm, fp4, grid, s);
-  else if (dqk == 256 && dvo == 256) launch_prefill<256, 256>(a, pm, fp4, grid, s);
-  else launch_prefill<512, 256>(a, pm, fp4, grid, s);
+  if (dqk == 512 && dvo == 512) launch_prefill<512, 512>(a, pm, kv, grid, s);
+  else if (dqk == 256 && dvo == 256) launch_prefill<256, 256>(a, pm, kv, grid, s);
+  else launch_prefill<512, 256>(a, pm, kv, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
   count_launches(1);

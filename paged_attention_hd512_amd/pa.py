@@ -106,6 +106,7 @@ SIGNATURES = {
     "pa_debug_fp8_to_f32": (c_int32, [_P, _P, c_int32, _P]),
     "pa_last_error": (c_char_p, []),
     "pa_launch_count": (c_uint64, []),
+    "pa_debug_launch_count": (c_uint64, []),
     "pa_version": (c_char_p, []),
 }
 
@@ -147,6 +148,10 @@ def pa_last_error():
 
 def pa_launch_count():
     return int(lib().pa_launch_count())
+
+
+def pa_debug_launch_count():
+    return int(lib().pa_debug_launch_count())
 
 
 def pa_version():

@@ -353,6 +353,10 @@ WORKLOADS = {
     "causal_prefill": dict(kind="prefill", batch=4, qo_len=4096, prefix=1024,
                            num_qo_heads=16, num_kv_heads=8, head_dim_qk=512, page_size=64,
                            variants=[512, 256], seed=1005),
+    # The causal prefill geometry over an FP8 E4M3FN cache (cast on load).
+    "fp8_prefill": dict(kind="prefill", batch=4, qo_len=4096, prefix=1024,
+                        num_qo_heads=16, num_kv_heads=8, head_dim_qk=512, page_size=64,
+                        kv_dtype="fp8", variants=[512, 256], seed=1009),
     # The NVFP4 page's shape: asymmetric qk 512 / vo 256 prefill over an NVFP4 cache.
     "nvfp4_prefill": dict(kind="prefill", batch=4, qo_len=4096, prefix=1024,
                           num_qo_heads=16, num_kv_heads=8, head_dim_qk=512, page_size=64,

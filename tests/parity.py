@@ -140,3 +140,12 @@ def bf16_rne_bits(x):
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return u.astype(np.uint16)
+
+
+def repad(t, extra):
+    """The same values in a new allocation whose rows are `extra` elements longer: a
+    strided view with its own stride family."""
+    parent = torch.zeros(tuple(t.shape[:-1]) + (t.shape[-1] + extra,), dtype=t.dtype,
+                         device=t.device)
+    parent[..., :t.shape[-1]] = t
+    return parent[..., :t.shape[-1]]

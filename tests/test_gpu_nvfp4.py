@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from synth import make_decode_case, decode_workload
-from parity import say, compare, oracle_decode, gpu_decode, out_to_np, pool_to_np
+from parity import say, compare, oracle_decode, gpu_decode, out_to_np, pool_to_np, repad
 
 pytestmark = pytest.mark.gpu
 
@@ -93,17 +93,17 @@ def test_split_and_unsplit_nvfp4_decode_agree_on_long_kv():
 
 
 @pytest.mark.slow
-def test_full_size_nvfp4_workload_on_sampled_requests():
+def test_full_size_nvfp4_workload_on_every_request():
     say("full-size nvfp4_decode")
     c = decode_workload("nvfp4_decode", device=dev())
     _, o, lse = gpu_decode(c)
-    lens = c.kv_lens
-    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)),
-                     int(np.random.default_rng(0).integers(0, c.batch))})
-    ref, ref_lse = oracle_decode(c, requests=sample)
-    compare(f"nvfp4_decode requests {sample}", out_to_np(o[sample]), ref,
-            lse[sample].cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
-    assert torch.isfinite(o.float()).all()
+    _, o32, lse32 = gpu_decode(c, out_dtype="fp32")
+    everyone = list(range(c.batch))
+    ref, ref_lse = oracle_decode(c, requests=everyone)
+    compare(f"nvfp4_decode all {c.batch} requests, bf16 out", out_to_np(o), ref,
+            lse.cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
+    compare(f"nvfp4_decode all {c.batch} requests, fp32 out", out_to_np(o32), ref,
+            lse32.cpu().numpy(), ref_lse, out_dtype="fp32")
 
 
 # --------------------------------------------------------------------------- prefill
@@ -164,27 +164,16 @@ def test_split_nvfp4_prefill_of_one_token_equals_unsplit_decode():
 
 
 @pytest.mark.slow
-def test_full_size_nvfp4_prefill_on_sampled_rows():
+def test_full_size_nvfp4_prefill_on_256_rows_per_request():
     say("full-size nvfp4_prefill (qk 512, vo 256)")
+    from test_gpu_prefill import full_size_rows
     c = prefill_workload("nvfp4_prefill", device=dev(), head_dim_vo=256)
     _, o, lse = gpu_prefill(c)
-    # The oracle runs one row per request at the start, middle and end of its new tokens.
-    tokens = []
-    for b in range(c.batch):
-        q0, q1 = int(c.qo_indptr[b]), int(c.qo_indptr[b + 1])
-        tokens += [q0, (q0 + q1) // 2, q1 - 1]
-    ref, ref_lse = oracle_prefill(c, tokens=tokens)
-    compare("nvfp4_prefill sampled rows", out_to_np(o[tokens]), ref,
-            lse[tokens].cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
-
-
-def _repad(t, extra):
-    """The same values in a new allocation whose rows are `extra` bytes longer: a strided
-    view with its own stride family."""
-    parent = torch.zeros(tuple(t.shape[:-1]) + (t.shape[-1] + extra,), dtype=t.dtype,
-                         device=t.device)
-    parent[..., :t.shape[-1]] = t
-    return parent[..., :t.shape[-1]]
+    toks = full_size_rows(c, 256, 7)
+    ref, ref_lse = oracle_prefill(c, tokens=toks)
+    idx = torch.as_tensor(toks).to(o.device)
+    compare(f"nvfp4_prefill {len(toks)} rows", out_to_np(o.index_select(0, idx)), ref,
+            lse.index_select(0, idx).cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
 
 
 @pytest.mark.parametrize("dqk,dvo,page", [(512, 256, 16), (512, 512, 1), (256, 256, 64)])
@@ -197,8 +186,8 @@ def test_nvfp4_pools_with_different_stride_families(dqk, dvo, page):
     from synth import make_decode_case
     d = make_decode_case([37, 300, 1000, 5], 8, 2, dqk, page, head_dim_vo=dvo, kv_dtype="nvfp4",
                          out_dtype="fp32", num_splits=2, seed=51, device=dev())
-    d.k_pool, d.v_pool = _repad(d.k_pool, 16), _repad(d.v_pool, 48)
-    d.k_sf, d.v_sf = _repad(d.k_sf, 16), _repad(d.v_sf, 48)
+    d.k_pool, d.v_pool = repad(d.k_pool, 16), repad(d.v_pool, 48)
+    d.k_sf, d.v_sf = repad(d.k_sf, 16), repad(d.v_sf, 48)
     d.cache = None
     assert d.k_pool.stride(2) != d.v_pool.stride(2) and d.k_sf.stride(2) != d.v_sf.stride(2)
     _, o, lse = gpu_decode(d)
@@ -206,8 +195,8 @@ def test_nvfp4_pools_with_different_stride_families(dqk, dvo, page):
     compare(f"nvfp4 padded decode {dqk}/{dvo}", out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
     p = make_prefill_case([40, 3], [300, 900], 8, 2, dqk, page, head_dim_vo=dvo,
                           kv_dtype="nvfp4", out_dtype="fp32", seed=52, device=dev())
-    p.k_pool, p.v_pool = _repad(p.k_pool, 48), _repad(p.v_pool, 16)
-    p.k_sf, p.v_sf = _repad(p.k_sf, 32), _repad(p.v_sf, 16)
+    p.k_pool, p.v_pool = repad(p.k_pool, 48), repad(p.v_pool, 16)
+    p.k_sf, p.v_sf = repad(p.k_sf, 32), repad(p.v_sf, 16)
     p.cache = None
     _, o, lse = gpu_prefill(p)
     ref, ref_lse = oracle_prefill(p)

@@ -56,6 +56,85 @@ def test_prefill_sweep(qo, kv, hq, hkv, dqk, dvo, page, causal, window, out):
     compare(name, out_to_np(o), ref, lse.cpu().numpy(), ref_lse, out_dtype=out)
 
 
+FP8_SWEEP = [
+    # qo_lens, kv_lens, hq, hkv, dqk, dvo, page, causal, window, out
+    ([130, 64, 1], [300, 64, 1], 16, 8, 512, 512, 64, True, 0, "fp32"),
+    ([40, 7], [100, 7], 4, 2, 512, 256, 16, True, 0, "fp32"),
+    ([130, 64, 1], [300, 64, 1], 16, 8, 256, 256, 1, True, 0, "bf16"),
+    ([200, 33], [1100, 40], 6, 2, 512, 512, 1, True, 100, "fp32"),
+    ([200, 33], [1100, 40], 6, 2, 512, 256, 64, True, 0, "bf16"),
+    ([150], [150], 16, 1, 256, 256, 16, True, 17, "fp32"),
+    ([77, 5], [77, 9], 8, 1, 512, 512, 16, False, 0, "fp32"),
+    ([64, 0, 65], [64, 10, 200], 3, 1, 256, 256, 64, True, 0, "fp32"),
+    ([260, 70], [1000, 300], 4, 2, 512, 512, 128, True, 0, "bf16"),
+    # short queries over long KV (split-K prefill: key chunks merged per tile)
+    ([3, 1, 16], [3000, 5000, 2100], 4, 2, 512, 512, 64, True, 0, "fp32"),
+    ([16] * 4, [6000] * 4, 16, 8, 512, 256, 64, True, 0, "bf16"),
+    ([5, 2], [2500, 4000], 6, 2, 256, 256, 3, True, 0, "fp32"),
+]
+
+
+@pytest.mark.parametrize("qo,kv,hq,hkv,dqk,dvo,page,causal,window,out", FP8_SWEEP)
+def test_fp8_prefill_sweep(qo, kv, hq, hkv, dqk, dvo, page, causal, window, out):
+    """FP8 E4M3FN KV, cast on load (the Triton page, section "Approach"), against the
+    oracle run on the stored codes, which it dequantises itself."""
+    name = (f"fp8 prefill qo={qo} kv={kv} heads={hq}/{hkv} dims={dqk}/{dvo} page={page} "
+            f"causal={causal} window={window} out={out}")
+    say(name)
+    c = make_prefill_case(qo, kv, hq, hkv, dqk, page, head_dim_vo=dvo, causal=causal,
+                          window=window, out_dtype=out, kv_dtype="fp8",
+                          seed=sum(qo) + hq + 3, device=dev())
+    assert c.k_scale != 1.0 and c.v_scale != 1.0
+    before = pa.pa_launch_count()
+    runner, o, lse = gpu_prefill(c)
+    assert pa.pa_launch_count() > before
+    ref, ref_lse = oracle_prefill(c)
+    compare(name, out_to_np(o), ref, lse.cpu().numpy(), ref_lse, out_dtype=out)
+
+
+@pytest.mark.parametrize("dqk,dvo,page", [(512, 512, 64), (256, 256, 1), (512, 256, 3)])
+def test_fp8_prefill_single_key_rows_return_every_value_code_exactly(dqk, dvo, page):
+    """One new token over one key: its weight is 1, so the fp32 output is the key's V row
+    widened (E4M3FN to bf16 is exact) times v_scale, one rounding -- bit for bit the
+    oracle's value rounded to fp32.  The V rows are rewritten so that every finite code
+    appears at many head_dim positions, which checks the stage conversion code by code."""
+    say(f"fp8 prefill single-key rows, all codes, dims={dqk}/{dvo} page={page}")
+    c = make_prefill_case([1] * 48, [1] * 48, 8, 2, dqk, page, head_dim_vo=dvo,
+                          kv_dtype="fp8", out_dtype="fp32", seed=24, device=dev())
+    for b in range(c.batch):
+        pg = int(c.kv_indices[c.kv_indptr[b]])
+        for h in range(c.num_kv_heads):
+            row = (np.arange(dvo) + 5 * (b * c.num_kv_heads + h)) % 256
+            row[(row & 0x7F) == 0x7F] = 0  # the NaN codes
+            c.v_pool[pg, h, 0, :] = torch.as_tensor(row.astype(np.uint8)).to(dev())
+    _, o, lse = gpu_prefill(c)
+    ref, ref_lse = oracle_prefill(c)
+    assert np.array_equal(o.cpu().numpy(), ref.astype(np.float32)), "FP8 V widening is not exact"
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() < 1e-4
+
+
+def test_fp8_prefill_of_one_token_equals_fp8_decode():
+    """Prefill with one new token per request and decode read the same FP8 cache; both
+    cast on load, so they agree with each other and with the oracle."""
+    say("fp8 prefill q_len 1 vs fp8 decode")
+    from parity import gpu_decode, oracle_decode
+    from synth import make_decode_case
+    lens = [37, 3000, 64]
+    d = make_decode_case(lens, 12, 4, 512, 64, kv_dtype="fp8", num_splits=1, out_dtype="fp32",
+                         seed=25, device=dev())
+    from paged_attention_hd512_amd import PagedPrefill
+    pre = PagedPrefill(d.k_pool, d.v_pool, np.arange(len(lens) + 1, dtype=np.int32),
+                       d.kv_indptr, d.kv_indices, d.kv_last_page_len, d.num_qo_heads,
+                       kv_dtype="fp8", k_scale=d.k_scale, v_scale=d.v_scale,
+                       sm_scale=d.sm_scale, out_dtype="fp32")
+    po, pl = pre.run(d.q.contiguous())
+    _, do, dl = gpu_decode(d)
+    ref, ref_lse = oracle_decode(d)
+    compare("fp8 prefill, one token", out_to_np(po), ref, pl.cpu().numpy(), ref_lse)
+    assert np.abs(out_to_np(po) - out_to_np(do)).max() < 2e-3
+    assert np.abs(pl.cpu().numpy() - dl.cpu().numpy()).max() < 1e-4
+
+
 @pytest.mark.parametrize("dqk,dvo,page", [(512, 512, 64), (512, 256, 16), (256, 256, 3)])
 def test_scores_far_above_the_first_stage_max(dqk, dvo, page):
     """Keys from position 100 on get 40x larger K rows, so their scores exceed every
@@ -93,26 +172,39 @@ def test_prefill_with_one_new_token_equals_decode():
     assert np.abs(ld.cpu().numpy() - lp.cpu().numpy()).max() < 1e-4
 
 
-@pytest.mark.slow
-@pytest.mark.parametrize("dvo", [512, 256])
-def test_full_size_causal_prefill_on_sampled_rows(dvo):
-    """The benchmark's prefill (4 x 4096 new tokens over a 1024-token prefix, 16/8 heads,
-    page 64) in its launch configuration; the oracle checks 96 rows spread over the first
-    and last request (first, last and random positions), all heads."""
-    say(f"full-size causal prefill vo={dvo}")
-    c = prefill_workload("causal_prefill", device=dev(), head_dim_vo=dvo)
-    _, o, lse = gpu_prefill(c)
-    rng = np.random.default_rng(dvo)
+def full_size_rows(c, per_request, seed):
+    """Query tokens checked in a full-size prefill: per request its first and last two and
+    random ones, `per_request` in all (every head of each)."""
+    rng = np.random.default_rng(seed)
     toks = []
-    for b in (0, c.batch - 1):
+    for b in range(c.batch):
         q0, q1 = int(c.qo_indptr[b]), int(c.qo_indptr[b + 1])
-        toks += [q0, q0 + 1, q1 - 1, q1 - 2] + list(rng.integers(q0, q1, size=44))
-    toks = np.array(sorted(set(toks)))
+        fixed = {q0, q0 + 1, q1 - 2, q1 - 1}
+        rest = rng.choice(np.arange(q0 + 2, q1 - 2), size=per_request - len(fixed), replace=False)
+        toks += sorted(fixed | set(int(x) for x in rest))
+    return np.array(toks)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,dvo", [("causal_prefill", 512), ("causal_prefill", 256),
+                                      ("fp8_prefill", 512), ("fp8_prefill", 256)])
+def test_full_size_causal_prefill_on_256_rows_per_request(name, dvo):
+    """The benchmark's prefill (4 x 4096 new tokens over a 1024-token prefix, 16/8 heads,
+    page 64) in its launch configuration (bf16 output) and with fp32 output: the oracle
+    checks 256 query tokens (all heads) of every request, the fp32 output against the
+    literal max-abs bound of 1e-2."""
+    say(f"full-size {name} vo={dvo}")
+    c = prefill_workload(name, device=dev(), head_dim_vo=dvo)
+    _, o, lse = gpu_prefill(c)
+    _, o32, lse32 = gpu_prefill(c, out_dtype="fp32")
+    toks = full_size_rows(c, 256, dvo)
     ref, ref_lse = oracle_prefill(c, tokens=toks)
     idx = torch.as_tensor(toks).to(o.device)
-    compare(f"prefill vo={dvo} rows {len(toks)}", out_to_np(o.index_select(0, idx)), ref,
-            lse.index_select(0, idx).cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
-    assert torch.isfinite(o.float()).all()
+    compare(f"{name} vo={dvo} {len(toks)} rows, bf16 out", out_to_np(o.index_select(0, idx)),
+            ref, lse.index_select(0, idx).cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
+    compare(f"{name} vo={dvo} {len(toks)} rows, fp32 out", out_to_np(o32.index_select(0, idx)),
+            ref, lse32.index_select(0, idx).cpu().numpy(), ref_lse, out_dtype="fp32")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(o32).all()
 
 
 @pytest.mark.slow

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (pa_[a-z0-9_]+)$", out, flags=re.M))
@@ -39,6 +39,7 @@ def test_every_declared_function_is_exported():
 def test_version_and_counter():
     assert "gfx950" in pa.pa_version()
     assert pa.pa_launch_count() >= 0
+    assert pa.pa_debug_launch_count() == pa.pa_launch_count()
 
 
 def params(hq=8, window=0, causal=1, out=pa.PA_DTYPE_FP32, scale=0.05):
@@ -277,7 +278,7 @@ def test_misaligned_strides_are_rejected_and_aligned_padding_is_accepted():
     assert e.value.status == pa.PA_ERR_UNSUPPORTED and "v_stride_token" in e.value.message
 
 
-def test_prefill_rejects_more_new_tokens_than_keys_and_fp8():
+def test_prefill_rejects_more_new_tokens_than_keys_and_plans_every_kv_format():
     P = 16
     ip, la = lens_to_table([10], P)
     c = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, 10, 2, P, 512)
@@ -285,9 +286,19 @@ def test_prefill_rejects_more_new_tokens_than_keys_and_fp8():
     with pytest.raises(pa.PaError) as e:
         pa.pa_prefill_plan(params(hq=4), c, [0, 11], ip, la)
     assert e.value.status == pa.PA_ERR_INVALID_ARG
-    c8 = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_FP8_E4M3FN, 10, 2, P, 512, 1.0, 1.0)
+    # FP8 E4M3FN (cast on load in both phases) and NVFP4 plan like bf16: same items.
+    ref, ref_buf = pa.pa_prefill_plan(params(hq=4), c, [0, 10], ip, la)
+    c8 = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_FP8_E4M3FN, 10, 2, P, 512, 0.5, 2.0)
+    c4 = pa.pa_kv_cache_nvfp4_hnd(0x10000, 0x90000, 10, 2, P, 512, 0.5, 2.0)
+    for cq in (c8, c4):
+        plan, buf = pa.pa_prefill_plan(params(hq=4), cq, [0, 10], ip, la)
+        assert plan.kv_dtype == cq.kv_dtype
+        assert np.array_equal(pa.prefill_items(plan, buf), pa.prefill_items(ref, ref_buf))
+    # A KV format the library does not implement is still refused.
+    cf = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, 10, 2, P, 512)
+    cf.kv_dtype = pa.PA_DTYPE_FP32
     with pytest.raises(pa.PaError) as e:
-        pa.pa_prefill_plan(params(hq=4), c8, [0, 10], ip, la)
+        pa.pa_prefill_plan(params(hq=4), cf, [0, 10], ip, la)
     assert e.value.status == pa.PA_ERR_UNSUPPORTED
 
 
