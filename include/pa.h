@@ -271,6 +271,21 @@ pa_status pa_paged_decode(const pa_plan* plan, const void* q, const pa_kv_cache*
                           void* out, float* lse, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* pa_paged_decode for callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and
+ * results, with the workspace taken from a device array inside the library (64 MiB per
+ * GPU, held from the library's load until the process ends) instead of the caller's.
+ * Each call first copies plan->plan_bytes from plan_buf_host into that array
+ * (stream-ordered; the host buffer must stay unchanged until the stream has reached the
+ * call), then launches the partial and merge kernels.  Calls no allocator.  A plan whose
+ * workspace_bytes exceeds 64 MiB is refused with PA_ERR_WORKSPACE_TOO_SMALL.  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race; calls on one stream are ordered. */
+pa_status pa_paged_decode_static(const pa_plan* plan, const void* plan_buf_host, const void* q,
+                                 const pa_kv_cache* cache, const pa_page_table* table,
+                                 const pa_attn_params* params, void* out, float* lse,
+                                 void* stream);
+
 /* The two phases of pa_paged_decode as separate calls, with the same arguments and
  * checks, for callers that schedule or time them apart: _partial launches the split-K
  * kernel (requests with a single chunk get their final out/lse from it), _merge launches

@@ -50,6 +50,7 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "pa_device.hpp"
@@ -727,6 +728,38 @@ static hipError_t launch_decode(const DecodeArgs& a, int dqk, int dvo, int kv_dt
   return launch_decode_kv<kKvFp4>(a, dqk, dvo, gmax, grid, s);
 }
 
+// ---- Workspace for callers that cannot allocate (pa_paged_decode_static).
+// A file-scope device array stands in for the caller's workspace: the uploaded plan and the
+// split partials.  Each GPU the library runs on holds its own copy, zeroed when the code
+// object is loaded and kept until the process ends.  In host code `scratch` is only a
+// stand-in for the symbol; its device address comes from hipGetSymbolAddress, once per
+// device with that device current, and only that address is passed to kernels.
+constexpr size_t kStaticWorkspaceBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kStaticWorkspaceBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static pa_status static_workspace(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, "device %d: the static workspace serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -860,6 +893,32 @@ pa_status pa_paged_decode_merge(const pa_plan* plan, const void* q, const pa_kv_
                                 void* stream) {
   return decode_enqueue(plan, q, cache, table, params, out, lse, workspace, workspace_bytes,
                         stream, false, true);
+}
+
+pa_status pa_paged_decode_static(const pa_plan* plan, const void* plan_buf_host, const void* q,
+                                 const pa_kv_cache* cache, const pa_page_table* table,
+                                 const pa_attn_params* params, void* out, float* lse,
+                                 void* stream) {
+  if (!plan || !plan_buf_host) return fail(PA_ERR_INVALID_ARG, "plan or plan buffer is NULL");
+  if (plan->workspace_bytes < 0 || (uint64_t)plan->workspace_bytes > kStaticWorkspaceBytes)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                "the plan needs a %lld-byte workspace; the static workspace holds %zu bytes "
+                "(use pa_paged_decode with a workspace of your own)",
+                (long long)plan->workspace_bytes, kStaticWorkspaceBytes);
+  void* ws = nullptr;
+  pa_status st = static_workspace(&ws);
+  if (st != PA_OK) return st;
+  bool nothing = false;
+  st = decode_check(plan, q, cache, table, params, out, lse, ws, kStaticWorkspaceBytes, &nothing);
+  if (st != PA_OK || nothing) return st;
+  // The plan goes into the workspace first, in stream order (no allocation).
+  if (plan->plan_bytes > 0) {
+    hipError_t e = hipMemcpyAsync(ws, plan_buf_host, (size_t)plan->plan_bytes,
+                                  hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  }
+  return decode_enqueue(plan, q, cache, table, params, out, lse, ws, kStaticWorkspaceBytes,
+                        stream, true, true);
 }
 
 pa_status pa_debug_gather_kv(const pa_kv_cache* cache, const pa_page_table* table,

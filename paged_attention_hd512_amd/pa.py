@@ -98,6 +98,9 @@ SIGNATURES = {
     "pa_paged_decode_merge": (c_int32, [POINTER(pa_plan), _P, POINTER(pa_kv_cache),
                                         POINTER(pa_page_table), POINTER(pa_attn_params), _P, _P,
                                         _P, c_size_t, _P]),
+    "pa_paged_decode_static": (c_int32, [POINTER(pa_plan), _P, _P, POINTER(pa_kv_cache),
+                                         POINTER(pa_page_table), POINTER(pa_attn_params), _P,
+                                         _P, _P]),
     "pa_paged_prefill": (c_int32, [POINTER(pa_plan), _P, _P, POINTER(pa_kv_cache),
                                    POINTER(pa_page_table), POINTER(pa_attn_params), _P, _P, _P,
                                    c_size_t, _P]),
@@ -239,6 +242,13 @@ def pa_paged_decode(plan, q, cache, table, params, out, lse, workspace, workspac
     _check(lib().pa_paged_decode(ctypes.byref(plan), q, ctypes.byref(cache), ctypes.byref(table),
                                  ctypes.byref(params), out, lse, workspace, workspace_bytes,
                                  stream))
+
+
+def pa_paged_decode_static(plan, plan_buf, q, cache, table, params, out, lse, stream=None):
+    """pa_paged_decode with the library's own workspace; plan_buf is the host plan buffer."""
+    _check(lib().pa_paged_decode_static(ctypes.byref(plan), plan_buf.ctypes.data_as(c_void_p),
+                                        q, ctypes.byref(cache), ctypes.byref(table),
+                                        ctypes.byref(params), out, lse, stream))
 
 
 def pa_paged_decode_partial(plan, q, cache, table, params, out, lse, workspace,
