@@ -18,8 +18,10 @@ Both are counted from the realised seeded lengths.
 Timing: `ms_per_step` (and `value`) come from one pair of HIP events on the launch stream
 around K back-to-back steps; `protocol` gives the median, minimum and mean of 50 further
 iterations timed one by one (an event between consecutive iterations); the dominant
-kernel's average duration (`roofline.kernel_avg_ms`) comes from a pass with events around
-every launch.  The sliding-window workloads at head_dim 256 (about 0.4 GB of visible KV,
+kernel's average duration (`roofline.kernel_avg_ms`): for prefill the step itself (one
+launch, or the split kernel and its merge); for decode the step less the merge kernel, whose
+duration comes from K back-to-back merge launches between one pair of events (consecutive
+launches abut, so no event sits between kernels).  The sliding-window workloads at head_dim 256 (about 0.4 GB of visible KV,
 close to the 256 MB last-level cache) alternate between two copies of the pool in every
 timed loop.  Every line carries the oracle's CPU throughput on a bounded sample of the same
 workload (`cpu_baseline`).
@@ -144,21 +146,6 @@ def time_steps(launch, stream, steps):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def time_kernels(launches, stream, steps):
-    """Average duration (ms) of each launch in `launches` over `steps` steps, from HIP events
-    recorded on the launch stream around every launch."""
-    import torch
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
-          for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record(stream)
-        for j, f in enumerate(launches):
-            f()
-            ev[i][j + 1].record(stream)
-    torch.cuda.synchronize()
-    return [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j in range(len(launches))]
-
-
 def time_protocol(launch, stream, iters=50):
     """Median, minimum and mean (ms) of `iters` iterations timed one by one: one HIP event
     between consecutive iterations on the launch stream."""
@@ -243,9 +230,14 @@ def time_decode(case, steps, warmup, copies=1, profile=False):
         torch.cuda.synchronize()
         return None, None, None, None, runners[0][0].plan, None
     step, wall = time_steps(step_fn, stream, steps)
-    part_fn = Rotation([lambda a=a: pa.pa_paged_decode_partial(*a) for a in argsets])
-    merge_fn = Rotation([lambda a=a: pa.pa_paged_decode_merge(*a) for a in argsets])
-    part, merge = time_kernels([part_fn, merge_fn], stream, steps)
+    # The merge alone, back to back (it is idempotent: it re-reads the partials); consecutive
+    # launches abut, so this average carries none of the few microseconds that an event
+    # recorded between two kernels adds.  The partial kernel's duration inside the step is
+    # then the step time less the merge's.  (Timing the partial kernel alone back to back
+    # would give a shorter time than it takes inside a step, so it is not used.)
+    merge, _ = time_steps(Rotation([lambda a=a: pa.pa_paged_decode_merge(*a) for a in argsets]),
+                          stream, steps) if runners[0][0].plan.num_merges > 0 else (0.0, 0.0)
+    part = step - merge
     proto = time_protocol(step_fn, stream)
     return max(step, 1e-9), part, merge, wall, runners[0][0].plan, proto
 
@@ -310,7 +302,9 @@ def time_prefill(case, steps, warmup, profile=False):
         torch.cuda.synchronize()
         return None, None, None, run.plan, None
     step, wall = time_steps(lambda: pa.pa_paged_prefill(*args), stream, steps)
-    (kern,) = time_kernels([lambda: pa.pa_paged_prefill(*args)], stream, steps)
+    # A prefill step is its kernel launch(es): back-to-back steps abut, so the step average
+    # is the launch duration (events between launches would add a few microseconds each).
+    kern = step
     proto = time_protocol(lambda: pa.pa_paged_prefill(*args), stream)
     return step, kern, wall, run.plan, proto
 

@@ -157,7 +157,8 @@ typedef struct pa_plan {
   int64_t plan_bytes;              /* bytes of the host plan buffer in use              */
   int64_t items_offset;            /* byte offset of the item array in the plan buffer  */
   int64_t merges_offset;           /* byte offset of the merge array in the plan buffer */
-  int64_t workers_offset;          /* decode: byte offset of the per-wave segment ranges */
+  int64_t workers_offset;          /* decode: byte offset of the further segments (the
+                                      head segment of each wave comes first)            */
   int64_t partial_o_offset;        /* byte offset of partial outputs in the workspace   */
   int64_t partial_lse_offset;      /* byte offset of partial lse in the workspace       */
   int64_t workspace_bytes;         /* device workspace the run call needs               */

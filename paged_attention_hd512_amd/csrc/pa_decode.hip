@@ -58,8 +58,6 @@
 
 namespace pa {
 
-constexpr int kDecodeWavesPerGroup = 8;  // the two waves of every SIMD of a CU
-
 struct DecodeArgs {
   const uint16_t* q;           // [B, Hq, DQK] bf16 bits
   const char* k;               // byte base of the K pool
@@ -72,8 +70,7 @@ struct DecodeArgs {
   int64_t vs_sp, vs_sh, vs_st;
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
-  const DecodeSegment* segs;
-  const int32_t* wave_begin;   // wave w runs segments [wave_begin[w], wave_begin[w + 1])
+  const DecodeSegment* segs;   // head segment of wave w at index w, then further segments
   int32_t num_waves;
   void* out;                   // [B, Hq, DVO] fp32 or bf16
   float* lse;                  // [B, Hq] or null
@@ -98,6 +95,8 @@ __device__ __forceinline__ int q_dim_of_step(int j, int g4) {
   else return (DQK / 4) * g4 + 8 * j;
 }
 
+constexpr int kDecodeWavesPerGroup = 8;  // the two waves of every SIMD of a CU
+
 // Eight waves per workgroup, one workgroup per CU: each wave runs its own piece (its
 // segments one after the other) and never waits for the others.  They share LDS only to
 // publish how many blocks each has done: a wave behind the CU's average raises its issue
@@ -106,6 +105,7 @@ __device__ __forceinline__ int q_dim_of_step(int j, int g4) {
 // rest of the kernel.
 template <int DQK, int DVO, int KV, int GMAX>
 __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_kernel(DecodeArgs a) {
+  constexpr int NWG = kDecodeWavesPerGroup;
   constexpr int UNIT = KV == kKvBf16 ? 2 : 1;    // bytes per stride unit
   constexpr int KROW = KV == kKvBf16 ? 2 * DQK : KV == kKvFp8 ? DQK : DQK / 2;  // K row bytes
   constexpr int VB8 = KV == kKvBf16 ? 16 : KV == kKvFp8 ? 8 : 4;  // bytes of 8 V elements
@@ -123,7 +123,6 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
   using ksf_t = typename std::conditional<NKSF == 8, u32x2_t, uint32_t>::type;
   using vq_t = typename std::conditional<TPD == 16, u32x2_t, uint32_t>::type;  // TPD nibbles
 
-  constexpr int NWG = kDecodeWavesPerGroup;
   __shared__ __attribute__((aligned(16))) uint16_t q_all[NWG][GMAX * QPITCH];
   __shared__ __attribute__((aligned(16))) float p_all[NWG][2][16][16];  // P V runs one block behind
   __shared__ __attribute__((aligned(16))) float alpha_all[NWG][2][16];
@@ -139,8 +138,11 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
   float (*p_lds)[16][16] = p_all[wv];
   float (*alpha_lds)[16] = alpha_all[wv];
   const int wave = blockIdx.x * NWG + wv;
-  const int seg_first = wave < a.num_waves ? a.wave_begin[wave] : 0;
-  const int seg_last = wave < a.num_waves ? a.wave_begin[wave + 1] : 0;
+  // The wave's head segment names its further segments; each next record is requested when
+  // the previous segment starts (a clamped index rather than a branch around the load).
+  const bool active = wave < a.num_waves;
+  const DecodeSegment head = a.segs[active ? wave : 0];
+  const int n_seg = active ? 1 + head.more_count : 0;
   if (lane == 0) progress[wv] = 0;
   int done = 0;  // blocks this wave has finished
 
@@ -153,10 +155,12 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
   float acc[GMAX][8];
   f32x4_t acc4[TPD];    // NVFP4: the P V tiles, one MFMA output each
 
-  for (int sgi = seg_first; sgi < seg_last; ++sgi) {
-    const DecodeSegment sg = a.segs[sgi];
+  DecodeSegment sg_cur = head;
+  for (int k = 0; k < n_seg; ++k) {
+    const DecodeSegment sg = sg_cur;
+    sg_cur = a.segs[k + 1 < n_seg ? head.more_begin + k : wave];
     const int t0 = sg.t_begin, t1 = sg.t_end;  // t1 > t0
-    const int32_t* __restrict__ pages = a.kv_indices + a.kv_indptr[sg.b];
+    const int32_t* __restrict__ pages = a.kv_indices + sg.page_base;
     const int64_t k_head = (int64_t)sg.kvh * a.k_sh;
     const int64_t v_head = (int64_t)sg.kvh * a.v_sh;
     const int64_t ks_head = (int64_t)sg.kvh * a.ks_sh;
@@ -833,7 +837,6 @@ static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_
     a.kv_indptr = table->kv_indptr;
     a.kv_indices = table->kv_indices;
     a.segs = (const DecodeSegment*)(ws + plan->items_offset);
-    a.wave_begin = (const int32_t*)(ws + plan->workers_offset);
     a.num_waves = plan->num_workers;
     a.out = out;
     a.lse = lse;

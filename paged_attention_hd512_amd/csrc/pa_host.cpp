@@ -401,6 +401,7 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
       DecodeSegment sg;
       memset(&sg, 0, sizeof(sg));
       sg.b = b; sg.kvh = h; sg.t_begin = (int32_t)t0; sg.t_end = (int32_t)t1; sg.slot = -1;
+      sg.page_base = kv_indptr_host[b];
       piece_segs[k].push_back(sg);
       ++seg_count[pair];
       u = e;
@@ -444,9 +445,11 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
   plan->chunk_blocks = pieces.empty() ? 0 : (int32_t)(pieces[order[0]].second - pieces[order[0]].first);
   plan->num_splits = num_splits;
   plan->max_kv_len = (int32_t)max_len;
+  // Segments: the head segment of every wave (in launch order), then the further segments
+  // of the waves that have several (workers_offset), wave after wave.
   plan->items_offset = 0;
-  plan->workers_offset = align_up(num_segs * (int64_t)sizeof(DecodeSegment), 16);
-  plan->merges_offset = align_up(plan->workers_offset + ((int64_t)pieces.size() + 1) * 4, 16);
+  plan->workers_offset = (int64_t)pieces.size() * (int64_t)sizeof(DecodeSegment);
+  plan->merges_offset = align_up(num_segs * (int64_t)sizeof(DecodeSegment), 16);
   plan->plan_bytes = align_up(plan->merges_offset + (int64_t)merges.size() * sizeof(MergeItem), 256);
   plan->partial_o_offset = plan->plan_bytes;
   const int32_t group = params->num_qo_heads / hkv;
@@ -461,13 +464,15 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
   char* buf = (char*)plan_buf_host;
   memset(buf, 0, (size_t)plan->plan_bytes);
   DecodeSegment* out_segs = (DecodeSegment*)(buf + plan->items_offset);
-  int32_t* wave_begin = (int32_t*)(buf + plan->workers_offset);
-  int32_t n = 0;
+  int32_t more = (int32_t)order.size();  // next free index after the head segments
   for (size_t w = 0; w < order.size(); ++w) {
-    wave_begin[w] = n;
-    for (const DecodeSegment& sg : piece_segs[order[w]]) out_segs[n++] = sg;
+    const std::vector<DecodeSegment>& segs = piece_segs[order[w]];
+    DecodeSegment head = segs[0];
+    head.more_begin = more;
+    head.more_count = (int32_t)segs.size() - 1;
+    out_segs[w] = head;
+    for (size_t k = 1; k < segs.size(); ++k) out_segs[more++] = segs[k];
   }
-  wave_begin[order.size()] = n;
   memcpy(buf + plan->merges_offset, merges.data(), merges.size() * sizeof(MergeItem));
   return PA_OK;
 }

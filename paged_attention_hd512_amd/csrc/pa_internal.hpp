@@ -27,13 +27,18 @@ constexpr int kPrefillKeyStage = 32;  // keys per LDS stage of the prefill kerne
 constexpr int kPrefillSplitItems = 512;
 constexpr int kPrefillMinChunkStages = 8;
 
-struct DecodeSegment {  // 32 bytes: blocks of one (request, KV head) run by one wave
+// Blocks of one (request, KV head) run by one wave.  The plan holds one head segment per
+// wave (index = wave, in launch order), then the waves' further segments; a head segment
+// names where its wave's further segments sit, so a wave starts from one record.
+struct DecodeSegment {  // 32 bytes
   int32_t b;             // request
   int32_t kvh;           // KV head
   int32_t t_begin;       // first key of the segment
   int32_t t_end;         // one past the last key (t_end > t_begin)
   int32_t slot;          // partial slot, or -1: write the final output directly
-  int32_t pad[3];
+  int32_t page_base;     // kv_indptr[b]: the request's first entry in kv_indices
+  int32_t more_begin;    // head segments: index of the wave's next segment
+  int32_t more_count;    // head segments: number of further segments of the wave
 };
 
 struct MergeItem {       // 16 bytes

@@ -429,14 +429,24 @@ class PagedPrefill:
         return out, lse
 
 
+def decode_segments(plan, plan_buf):
+    """Raw segment records of a decode plan as a [num_items, 8] int32 array (b, kv_head,
+    t_begin, t_end, slot, page_base, more_begin, more_count): the head segment of each wave
+    in launch order, then the waves' further segments."""
+    off = plan.items_offset
+    return plan_buf[off:off + 32 * plan.num_items].view(np.int32).reshape(-1, 8)
+
+
 def decode_waves(plan, plan_buf):
     """Segments of a decode plan per wave, in launch order: a list of [k, 5] int32 arrays
     of (b, kv_head, t_begin, t_end, slot)."""
-    segs = plan_buf[plan.items_offset:plan.items_offset + 32 * plan.num_items]
-    segs = segs.view(np.int32).reshape(-1, 8)[:, :5]
-    off = plan.workers_offset
-    begin = plan_buf[off:off + 4 * (plan.num_workers + 1)].view(np.int32)
-    return [segs[begin[w]:begin[w + 1]] for w in range(plan.num_workers)]
+    segs = decode_segments(plan, plan_buf)
+    waves = []
+    for w in range(plan.num_workers):
+        more_begin, more_count = int(segs[w, 6]), int(segs[w, 7])
+        rows = [segs[w]] + [segs[more_begin + k] for k in range(more_count)]
+        waves.append(np.stack(rows)[:, :5])
+    return waves
 
 
 def decode_merges(plan, plan_buf):

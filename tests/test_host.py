@@ -87,6 +87,16 @@ def test_decode_plan_matches_reference_partition(lens, P, window, splits, hkv):
     plan, buf = pa.pa_decode_plan(params(hq=hkv * 2, window=window), cache, indptr, last, splits)
     waves = pa.decode_waves(plan, buf)
     merges = pa.decode_merges(plan, buf)
+    # Record layout: every segment carries its request's first kv_indices entry; the head
+    # segment of wave w sits at index w and names the wave's further segments, which follow
+    # the heads wave after wave.
+    segs = pa.decode_segments(plan, buf)
+    assert (segs[:, 5] == indptr[segs[:, 0]]).all()
+    nxt = plan.num_workers
+    for w in range(plan.num_workers):
+        assert segs[w, 6] == nxt
+        nxt += segs[w, 7]
+    assert nxt == plan.num_items and plan.workers_offset == 32 * plan.num_workers
     ref_waves, ref_merges = decode_partition_ref(lens, window, splits, hkv)
     assert [[tuple(r) for r in w.tolist()] for w in waves] == ref_waves
     assert [tuple(r) for r in merges.tolist()] == ref_merges
