@@ -23,9 +23,17 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-u
          "-I" + os.path.join(ROOT, "include")]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(PKG_DIR, "csrc", src), "-o", obj]
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer (device code is not
+# instrumented): each -fsanitize= applies to the host compilation only.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+SANITIZED_DIR = os.path.join(BUILD_DIR, "sanitized")
+
+
+def _compile(src, out_dir=BUILD_DIR, extra=()):
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + FLAGS + list(extra) + ["-c", os.path.join(PKG_DIR, "csrc", src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l)
@@ -34,22 +42,31 @@ def _compile(src):
     return obj, errs
 
 
-def build(verbose=False):
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose=False, sanitize=False):
+    """Builds libpa.so in the package (or, with sanitize, a host-sanitized copy under
+    _build/sanitized/, for the CPU tests of the host code; load it with the ASan runtime
+    preloaded and PA_LIBRARY pointing at it)."""
+    out_dir = SANITIZED_DIR if sanitize else BUILD_DIR
+    extra = SANITIZE_FLAGS if sanitize else []
+    lib_path = os.path.join(SANITIZED_DIR, "libpa.so") if sanitize else LIB_PATH
+    os.makedirs(out_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda s: _compile(s, out_dir, extra), SOURCES))
     if verbose:
         for _, msg in results:
             if msg.strip():
                 print(msg)
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+    if sanitize:
+        cmd[1:1] = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                    "-shared-libsan"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

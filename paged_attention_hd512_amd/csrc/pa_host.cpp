@@ -473,7 +473,8 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
     out_segs[w] = head;
     for (size_t k = 1; k < segs.size(); ++k) out_segs[more++] = segs[k];
   }
-  memcpy(buf + plan->merges_offset, merges.data(), merges.size() * sizeof(MergeItem));
+  if (!merges.empty())
+    memcpy(buf + plan->merges_offset, merges.data(), merges.size() * sizeof(MergeItem));
   return PA_OK;
 }
 

@@ -11,7 +11,10 @@ from ctypes import (POINTER, Structure, c_char_p, c_float, c_int32, c_int64, c_s
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+# The built library in the package; PA_LIBRARY may name another build of it (the CPU
+# tests load a host-sanitized build that way).
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_OK = 0
 PA_ERR_INVALID_ARG = 1

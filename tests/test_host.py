@@ -209,6 +209,43 @@ def test_prefill_plan_matches_reference_tiles(qo, kv, group, causal, window):
     assert plan.workspace_bytes >= plan.partial_lse_offset + part_rows * 8
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_random_plans_match_the_reference(seed):
+    """Random batches (empty and one-key requests, page sizes 1..128, windows, fixed
+    splits, group sizes 1..8 or 16): both planners' integers equal the reference rule.
+    Run under the host sanitizers too (tests/test_host_sanitized.py)."""
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 40))
+    P = int(rng.choice([1, 3, 16, 32, 64, 128]))
+    lens = [int(x) for x in rng.integers(0, 3000, size=B)]
+    lens[0] = 1
+    if B > 1:
+        lens[1] = 0
+    window = int(rng.choice([0, 0, 1, 17, 1024]))
+    splits = int(rng.choice([0, 0, 1, 3, 8, 64]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    group = int(rng.choice([1, 2, 3, 6, 8]))
+    indptr, last = lens_to_table(lens, P)
+    cache = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, int(indptr[-1]) + 1, hkv, P, 512)
+    plan, buf = pa.pa_decode_plan(params(hq=hkv * group, window=window), cache, indptr, last,
+                                  splits)
+    ref_waves, ref_merges = decode_partition_ref(lens, window, splits, hkv)
+    assert [[tuple(r) for r in w.tolist()] for w in pa.decode_waves(plan, buf)] == ref_waves
+    assert [tuple(r) for r in pa.decode_merges(plan, buf).tolist()] == ref_merges
+    qo = [int(rng.integers(0, L + 1)) for L in lens]
+    causal = bool(rng.integers(0, 2))
+    pgroup = int(rng.choice([1, 2, 6, 16]))
+    qo_indptr = np.zeros(B + 1, np.int32)
+    qo_indptr[1:] = np.cumsum(qo)
+    plan, buf = pa.pa_prefill_plan(params(hq=hkv * pgroup, window=window, causal=int(causal)),
+                                   cache, qo_indptr, indptr, last)
+    ref_items, ref_pmerges = prefill_plan_ref(qo, lens, pgroup, plan.tile_rows, causal, window,
+                                              hkv)
+    items = pa.prefill_items(plan, buf)
+    assert [tuple(r[:5]) + (r[8],) for r in items.tolist()] == [tuple(r) for r in ref_items]
+    assert [tuple(r) for r in pa.prefill_merges(plan, buf).tolist()] == [tuple(r) for r in ref_pmerges]
+
+
 @pytest.mark.parametrize("qo,kv,group,causal,window", PREFILL_CASES)
 def test_prefill_reference_chunks_cover_each_tile_exactly(qo, kv, group, causal, window):
     """A split tile's chunks are contiguous, cover its key range exactly, start on 32-key
