@@ -348,33 +348,46 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
           (__attribute__((address_space(3))) void*)(v_lds + vo + (my_row + i) * DVO), 16, off, 0, 0, 0);
     }
   };
-  // NVFP4: lane l holds key row my_row + l / 16 of the stage and part l % 16 of its packed
-  // row (FKB bytes of K, FVB of V: 2 FKB elements) with the block scales of that part.  Key
-  // rows are clamped into the tile's range like the copies' (clamped keys are masked out).
-  constexpr int FKB = DQK / 32, FVB = DVO / 32;
-  using fk_t = typename std::conditional<FKB == 16, u32x4_t, u32x2_t>::type;
-  using fv_t = typename std::conditional<FVB == 16, u32x4_t, u32x2_t>::type;
-  fk_t fk;
-  fv_t fv;
-  uint32_t fks = 0, fvs = 0;  // FKB / 8 (FVB / 8) block-scale codes, low byte first
-  auto fp4_load = [&](int st) {
-    const int part = lane & 15;
+  // Converting formats: lane l holds key row my_row + l / 16 of the stage and, of its K and
+  // V rows, the 8-element chunks c = l % 16 + 16 k (k < D / 128), so that each store
+  // instruction writes 16 consecutive chunk positions of a row (a bank-conflict-free 256
+  // bytes; chunks strided by four positions per lane conflicted in 4-way groups).  Key rows
+  // are clamped into the tile's range like the copies' (clamped keys are masked out).
+  constexpr int KC = DQK / 128, VC = DVO / 128;  // chunks per lane and row
+  // Byte address of row t's K and V rows (and block-scale rows) in the pages.
+  auto conv_rows = [&](int st, const char*& kd, const char*& vd, const char*& ks, const char*& vs) {
     int t = st * KS + my_row + (lane >> 4);
     t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
     const int j = t / a.page_size;
     const int64_t pg = pages[j];
     const int64_t sl = t - j * a.page_size;
-    const char* kd = a.k + pg * a.k_sp + (int64_t)kvh * a.k_sh + sl * a.k_st + FKB * part;
-    const char* vd = a.v + pg * a.v_sp + (int64_t)kvh * a.v_sh + sl * a.v_st + FVB * part;
-    const char* ks = a.k_sf + pg * a.ks_sp + (int64_t)kvh * a.ks_sh + sl * a.ks_st + (FKB / 8) * part;
-    const char* vs = a.v_sf + pg * a.vs_sp + (int64_t)kvh * a.vs_sh + sl * a.vs_st + (FVB / 8) * part;
-    fk = *(const fk_t*)kd;
-    fv = *(const fv_t*)vd;
-    fks = FKB == 16 ? (uint32_t)*(const uint16_t*)ks : (uint32_t)*(const uint8_t*)ks;
-    fvs = FVB == 16 ? (uint32_t)*(const uint16_t*)vs : (uint32_t)*(const uint8_t*)vs;
+    kd = a.k + pg * a.k_sp + (int64_t)kvh * a.k_sh + sl * a.k_st;
+    vd = a.v + pg * a.v_sp + (int64_t)kvh * a.v_sh + sl * a.v_st;
+    if constexpr (FP4) {
+      ks = a.k_sf + pg * a.ks_sp + (int64_t)kvh * a.ks_sh + sl * a.ks_st;
+      vs = a.v_sf + pg * a.vs_sp + (int64_t)kvh * a.vs_sh + sl * a.vs_st;
+    }
   };
-  // Converts the loaded rows and writes them as bf16: dword i of the part is the 16-byte
-  // chunk (FKB / 4) * part + i of the row, at chunk position chunk ^ swizzle(row).
+  // NVFP4: chunk c is 4 packed bytes at 4 c; its block scale is byte c / 2 of the row's
+  // scales (one E4M3 code per 16 elements).
+  uint32_t fk[KC], fv[VC], fks[KC], fvs[VC];
+  auto fp4_load = [&](int st) {
+    const int part = lane & 15;
+    const char *kd, *vd, *ks, *vs;
+    conv_rows(st, kd, vd, ks, vs);
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      fk[k] = *(const uint32_t*)(kd + 4 * (part + 16 * k));
+      fks[k] = *(const uint8_t*)(ks + ((part + 16 * k) >> 1));
+    }
+#pragma unroll
+    for (int k = 0; k < VC; ++k) {
+      fv[k] = *(const uint32_t*)(vd + 4 * (part + 16 * k));
+      fvs[k] = *(const uint8_t*)(vs + ((part + 16 * k) >> 1));
+    }
+  };
+  // Converts the loaded chunks (e2m1 x block scale, exact in bf16) and writes chunk c at
+  // position c ^ swizzle(row).
   auto fp4_store = [&](auto slot_c, int vo) {
     const int row = my_row + (lane >> 4);
     const int part = lane & 15;
@@ -386,72 +399,45 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
       for (int u = 0; u < 4; ++u) pk[u] = pack_bf16(e[2 * u] * bs, e[2 * u + 1] * bs);
       return pk;
     };
-    float kbs[2], vbs[2];
-    kbs[0] = fp8_to_f32<0>(fks);
-    kbs[1] = fp8_to_f32<1>(fks);
-    vbs[0] = fp8_to_f32<0>(fvs);
-    vbs[1] = fp8_to_f32<1>(fvs);
     uint16_t* kd = k_buf(slot_c) + row * DQK;
 #pragma unroll
-    for (int i = 0; i < FKB / 4; ++i) {
-      const int c = (FKB / 4) * part + i;
-      *(u32x4_t*)(kd + 8 * (c ^ k_swz(row))) = chunk8(fk[i], kbs[i >> 1]);
-    }
+    for (int k = 0; k < KC; ++k)
+      *(u32x4_t*)(kd + 8 * ((part + 16 * k) ^ k_swz(row))) = chunk8(fk[k], fp8_to_f32<0>(fks[k]));
     uint16_t* vd = v_lds + vo + row * DVO;
 #pragma unroll
-    for (int i = 0; i < FVB / 4; ++i) {
-      const int c = (FVB / 4) * part + i;
-      *(u32x4_t*)(vd + 8 * (c ^ v_swz(row))) = chunk8(fv[i], vbs[i >> 1]);
-    }
+    for (int k = 0; k < VC; ++k)
+      *(u32x4_t*)(vd + 8 * ((part + 16 * k) ^ v_swz(row))) = chunk8(fv[k], fp8_to_f32<0>(fvs[k]));
     // The writes complete before this wave reaches the barrier that hands the stage over.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   };
 
-  // FP8: lane l holds key row my_row + l / 16 of the stage and the sixteenth l % 16 of its
-  // K row (DQK / 16 codes, one or two 16-byte loads) and of its V row.  Key rows are clamped
-  // into the tile's range like the copies' (clamped keys are masked out).
-  constexpr int NK8 = DQK / 256, NV8 = DVO / 256;
-  u32x4_t f8k[NK8], f8v[NV8];
+  // FP8: chunk c is 8 codes at 8 c.
+  u32x2_t f8k[KC], f8v[VC];
   auto fp8_load = [&](int st) {
     const int part = lane & 15;
-    int t = st * KS + my_row + (lane >> 4);
-    t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
-    const int j = t / a.page_size;
-    const int64_t pg = pages[j];
-    const int64_t sl = t - j * a.page_size;
-    const char* kd = a.k + pg * a.k_sp + (int64_t)kvh * a.k_sh + sl * a.k_st + (DQK / 16) * part;
-    const char* vd = a.v + pg * a.v_sp + (int64_t)kvh * a.v_sh + sl * a.v_st + (DVO / 16) * part;
+    const char *kd, *vd, *ks = nullptr, *vs = nullptr;
+    conv_rows(st, kd, vd, ks, vs);
 #pragma unroll
-    for (int i = 0; i < NK8; ++i) f8k[i] = *(const u32x4_t*)(kd + 16 * i);
+    for (int k = 0; k < KC; ++k) f8k[k] = *(const u32x2_t*)(kd + 8 * (part + 16 * k));
 #pragma unroll
-    for (int i = 0; i < NV8; ++i) f8v[i] = *(const u32x4_t*)(vd + 16 * i);
+    for (int k = 0; k < VC; ++k) f8v[k] = *(const u32x2_t*)(vd + 8 * (part + 16 * k));
   };
-  // Widens the loaded codes to bf16 (exact) and writes them: the 16 codes of load i are the
-  // 8-element chunks (D / 128) * part + 2i and + 2i + 1 of the row, at chunk position
-  // chunk ^ swizzle(row).
+  // Widens the loaded codes to bf16 (exact) and writes chunk c at position c ^ swizzle(row).
   auto fp8_store = [&](auto slot_c, int vo) {
     const int row = my_row + (lane >> 4);
     const int part = lane & 15;
-    auto chunk8 = [&](uint32_t w0, uint32_t w1) {
-      const u32x2_t lo = fp8x4_to_bf16x4(w0), hi = fp8x4_to_bf16x4(w1);
+    auto chunk8 = [&](u32x2_t w) {
+      const u32x2_t lo = fp8x4_to_bf16x4(w[0]), hi = fp8x4_to_bf16x4(w[1]);
       return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
     };
     uint16_t* kd = k_buf(slot_c) + row * DQK;
 #pragma unroll
-    for (int i = 0; i < NK8; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = (DQK / 128) * part + 2 * i + h;
-        *(u32x4_t*)(kd + 8 * (c ^ k_swz(row))) = chunk8(f8k[i][2 * h], f8k[i][2 * h + 1]);
-      }
+    for (int k = 0; k < KC; ++k)
+      *(u32x4_t*)(kd + 8 * ((part + 16 * k) ^ k_swz(row))) = chunk8(f8k[k]);
     uint16_t* vd = v_lds + vo + row * DVO;
 #pragma unroll
-    for (int i = 0; i < NV8; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = (DVO / 128) * part + 2 * i + h;
-        *(u32x4_t*)(vd + 8 * (c ^ v_swz(row))) = chunk8(f8v[i][2 * h], f8v[i][2 * h + 1]);
-      }
+    for (int k = 0; k < VC; ++k)
+      *(u32x4_t*)(vd + 8 * ((part + 16 * k) ^ v_swz(row))) = chunk8(f8v[k]);
     // The writes complete before this wave reaches the barrier that hands the stage over.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   };
