@@ -154,6 +154,11 @@ typedef struct pa_plan {
   int32_t total_q;                 /* prefill: number of query tokens                   */
   int32_t max_kv_len;
   int32_t num_workers;             /* decode: waves the partial kernel launches         */
+  int32_t deferred_partials;       /* decode: 1 when a wave keeps the split result of a
+                                      non-final segment in LDS and stores it after its
+                                      last segment (the planner sets it when at least a
+                                      quarter of the waves have such a segment); a speed
+                                      choice only: either value gives the same bits      */
   int64_t plan_bytes;              /* bytes of the host plan buffer in use              */
   int64_t items_offset;            /* byte offset of the item array in the plan buffer  */
   int64_t merges_offset;           /* byte offset of the merge array in the plan buffer */

@@ -72,6 +72,7 @@ struct DecodeArgs {
   const int32_t* kv_indices;
   const DecodeSegment* segs;   // head segment of wave w at index w, then further segments
   int32_t num_waves;
+  int32_t park;                // the plan's deferred_partials
   void* out;                   // [B, Hq, DVO] fp32 or bf16
   float* lse;                  // [B, Hq] or null
   float* part_o;               // [slots, G, DVO] fp32
@@ -96,6 +97,7 @@ __device__ __forceinline__ int q_dim_of_step(int j, int g4) {
 }
 
 constexpr int kDecodeWavesPerGroup = 8;  // the two waves of every SIMD of a CU
+constexpr int kLdsBytesPerCu = 160 * 1024;  // gfx950: LDS of one CU, all of it one workgroup's
 
 // Eight waves per workgroup, one workgroup per CU: each wave runs its own piece (its
 // segments one after the other) and never waits for the others.  They share LDS only to
@@ -122,11 +124,25 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
       KV == kKvBf16, u32x4_t, typename std::conditional<KV == kKvFp8, u32x2_t, uint32_t>::type>::type;
   using ksf_t = typename std::conditional<NKSF == 8, u32x2_t, uint32_t>::type;
   using vq_t = typename std::conditional<TPD == 16, u32x2_t, uint32_t>::type;  // TPD nibbles
+  // A split segment that is not the wave's last parks its result in LDS, and the wave writes
+  // it to the workspace after its last segment: on this GPU a wave's loads and stores share
+  // one in-order completion counter, so partial-result stores issued between segments made
+  // the next segment's first loads wait for them under the full read load.  Parking needs
+  // G x DVO floats per wave; where LDS is short, the P buffer keeps only the columns the
+  // P V step reads, and instances that still do not fit store at once.
+  constexpr int PARK = GMAX * DVO + GMAX;         // floats: the outputs, then the log-sum-exps
+  constexpr auto lds_bytes = [](int pc) {
+    return NWG * (GMAX * QPITCH * 2 + 2 * 16 * pc * 4 + 2 * 16 * 4 + 4 + PARK * 4) + 1024;
+  };
+  constexpr int PC_NARROW = KV == kKvFp4 ? 8 : GMAX;
+  constexpr int PC = lds_bytes(16) <= kLdsBytesPerCu ? 16 : PC_NARROW;  // P columns kept
+  constexpr bool DEFER = lds_bytes(PC) <= kLdsBytesPerCu;
 
   __shared__ __attribute__((aligned(16))) uint16_t q_all[NWG][GMAX * QPITCH];
-  __shared__ __attribute__((aligned(16))) float p_all[NWG][2][16][16];  // P V runs one block behind
+  __shared__ __attribute__((aligned(16))) float p_all[NWG][2][16][PC];  // P V runs one block behind
   __shared__ __attribute__((aligned(16))) float alpha_all[NWG][2][16];
   __shared__ __attribute__((aligned(16))) int progress[NWG];
+  __shared__ __attribute__((aligned(16))) float park_all[DEFER ? NWG : 1][DEFER ? PARK : 4];
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -135,7 +151,9 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
   const int G = a.group;
   const int qrow = n < G ? n : G - 1;  // MFMA columns past the group repeat the last head
   uint16_t* q_lds = q_all[wv];
-  float (*p_lds)[16][16] = p_all[wv];
+  float (*p_lds)[16][PC] = p_all[wv];
+  float* park = park_all[DEFER ? wv : 0];
+  int parked_slot = -1;  // partial slot whose result waits in `park`
   float (*alpha_lds)[16] = alpha_all[wv];
   const int wave = blockIdx.x * NWG + wv;
   // The wave's head segment names its further segments; each next record is requested when
@@ -431,7 +449,7 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
       for (int i = 0; i < 4; ++i) {
         const float p = exp2f(sc[i] - m_new);
         psum += p;
-        p_lds[cur][4 * g4 + i][n] = p;
+        if (n < PC) p_lds[cur][4 * g4 + i][n] = p;
       }
       l_run = l_run * alpha + psum;
       m_run = m_new;
@@ -464,6 +482,7 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
         for (int e = 0; e < 8; ++e) acc[h][e] += shfl_xor_f(acc[h][e], 32);
     }
     const int h0 = sg.kvh * G;
+    const bool to_park = DEFER && a.park && sg.slot >= 0 && k + 1 < n_seg && parked_slot < 0;
     if constexpr (KV == kKvFp4) {
       // Lane (g4, n): head n & 7 at the 4 TPD columns from DVO/2 (n >> 3) + 4 TPD g4.
       const int h = n & 7;
@@ -477,7 +496,11 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int t = 0; t < TPD; ++t) o[TPD * r + t] = acc4[t][r] * inv;
-        if (sg.slot >= 0) {
+        if (to_park) {
+#pragma unroll
+          for (int c = 0; c < TPD; ++c)
+            *(f32x4_t*)(park + h * DVO + d0 + 4 * c) = f32x4_t{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
+        } else if (sg.slot >= 0) {
           float* dst = a.part_o + ((int64_t)sg.slot * G + h) * DVO + d0;
 #pragma unroll
           for (int c = 0; c < TPD; ++c)
@@ -508,7 +531,11 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = acc[h][e] * inv;
-        if (sg.slot >= 0) {
+        if (to_park) {
+          float* dst = park + h * DVO + lane * 8;
+          *(f32x4_t*)dst = f32x4_t{o[0], o[1], o[2], o[3]};
+          *(f32x4_t*)(dst + 4) = f32x4_t{o[4], o[5], o[6], o[7]};
+        } else if (sg.slot >= 0) {
           float* dst = a.part_o + ((int64_t)sg.slot * G + h) * DVO + lane * 8;
           *(f32x4_t*)dst = f32x4_t{o[0], o[1], o[2], o[3]};
           *(f32x4_t*)(dst + 4) = f32x4_t{o[4], o[5], o[6], o[7]};
@@ -529,8 +556,19 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
     }
     if (lane < G) {
       const float lg = m_run + log2f(l_run);  // log2 domain; l_run > 0 here
-      if (sg.slot >= 0) a.part_lse[(int64_t)sg.slot * G + lane] = lg;
+      if (to_park) park[GMAX * DVO + lane] = lg;
+      else if (sg.slot >= 0) a.part_lse[(int64_t)sg.slot * G + lane] = lg;
       else if (a.lse) a.lse[(int64_t)sg.b * a.num_qo_heads + h0 + lane] = lg * kLn2;
+    }
+    if (to_park) parked_slot = sg.slot;
+  }
+  if constexpr (DEFER) {
+    if (parked_slot >= 0) {
+      // The parked rows of heads 0 .. G-1 are contiguous, as in the workspace slot.
+      wave_lds_sync();
+      float* dst = a.part_o + (int64_t)parked_slot * G * DVO;
+      for (int i = 4 * lane; i < G * DVO; i += 256) *(f32x4_t*)(dst + i) = *(const f32x4_t*)(park + i);
+      if (lane < G) a.part_lse[(int64_t)parked_slot * G + lane] = park[GMAX * DVO + lane];
     }
   }
 }
@@ -838,6 +876,7 @@ static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_
     a.kv_indices = table->kv_indices;
     a.segs = (const DecodeSegment*)(ws + plan->items_offset);
     a.num_waves = plan->num_workers;
+    a.park = plan->deferred_partials;
     a.out = out;
     a.lse = lse;
     a.part_o = part_o;

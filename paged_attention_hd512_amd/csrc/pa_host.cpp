@@ -445,6 +445,18 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
   plan->chunk_blocks = pieces.empty() ? 0 : (int32_t)(pieces[order[0]].second - pieces[order[0]].first);
   plan->num_splits = num_splits;
   plan->max_kv_len = (int32_t)max_len;
+  // Waves that finish a split segment before their last one would store its result while
+  // their next segment streams.  Such stores in a quarter or more of the waves slowed every
+  // wave's reads (GQA batch at split-K 8, 46 % of the waves: 226 -> 206 us when the results
+  // wait in LDS until the wave ends); with an eighth of the waves the wait cost ~1 % (FP8
+  // batch), so the kernel parks them only when they are common.
+  int64_t mid_partials = 0;
+  for (auto& segs : piece_segs) {
+    bool any = false;
+    for (size_t k = 0; k + 1 < segs.size(); ++k) any = any || segs[k].slot >= 0;
+    mid_partials += any ? 1 : 0;
+  }
+  plan->deferred_partials = 4 * mid_partials >= (int64_t)pieces.size() && !pieces.empty() ? 1 : 0;
   // Segments: the head segment of every wave (in launch order), then the further segments
   // of the waves that have several (workers_offset), wave after wave.
   plan->items_offset = 0;

@@ -220,3 +220,29 @@ def test_bf16_output_is_the_rounded_fp32_output(splits):
     _, o16, l16 = gpu_decode(c, out_dtype="bf16")
     assert np.array_equal(bf16_to_np(o16), bf16_rne_bits(o32.cpu().numpy()))
     assert torch.equal(l32, l16)
+
+
+@pytest.mark.parametrize("kv_dtype,hq,hkv,dim,dvo,page", [
+    ("bf16", 24, 4, 512, 512, 16), ("fp8", 12, 4, 512, 512, 64), ("nvfp4", 12, 4, 512, 256, 16),
+    ("bf16", 16, 2, 512, 512, 16), ("bf16", 16, 8, 256, 256, 1)])
+def test_split_results_parked_in_lds_equal_results_stored_at_once(kv_dtype, hq, hkv, dim, dvo,
+                                                                   page):
+    """Fixed split-K 8 over short requests: most waves finish split segments before their
+    last one, so the plan parks those results in LDS (deferred_partials = 1).  A wave parks
+    the first of them and stores any further ones at once (waves here hold up to seven);
+    the group of 8 at 512 wide has no LDS to spare and stores them all at once.  The output
+    must match the oracle, and the same plan with parking cleared must give the same bits."""
+    say(f"parked split results {kv_dtype} G={hq // hkv} dims={dim}/{dvo} page={page}")
+    c = make_decode_case([700, 1500, 37, 3000, 900], hq, hkv, dim, page, head_dim_vo=dvo,
+                         kv_dtype=kv_dtype, num_splits=8, out_dtype="fp32", seed=70,
+                         device=dev())
+    run, o, lse = gpu_decode(c)
+    assert run.plan.deferred_partials == 1
+    waves = pa.decode_waves(run.plan, run.plan_buf)
+    assert max(sum(s[4] >= 0 for s in w[:-1]) for w in waves) >= 4
+    ref, ref_lse = oracle_decode(c)
+    compare(f"parked {kv_dtype} G={hq // hkv}", out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
+    run.plan.deferred_partials = 0
+    o2, lse2 = run.run(c.q)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)

@@ -80,6 +80,13 @@ DECODE_CASES = [
 ]
 
 
+def deferred_rule(waves):
+    """The planner parks split results in LDS when at least a quarter of the waves finish a
+    split segment (slot >= 0) before their last segment."""
+    mid = sum(any(seg[4] >= 0 for seg in w[:-1]) for w in waves)
+    return int(len(waves) > 0 and 4 * mid >= len(waves))
+
+
 @pytest.mark.parametrize("lens,P,window,splits,hkv", DECODE_CASES)
 def test_decode_plan_matches_reference_partition(lens, P, window, splits, hkv):
     indptr, last = lens_to_table(lens, P)
@@ -103,6 +110,7 @@ def test_decode_plan_matches_reference_partition(lens, P, window, splits, hkv):
     assert plan.num_workers == len(ref_waves) and plan.num_merges == len(ref_merges)
     assert plan.num_items == sum(len(w) for w in ref_waves)
     assert plan.num_slots == sum(m[3] for m in ref_merges)
+    assert plan.deferred_partials == deferred_rule(ref_waves)
     group, dvo = 2, 512
     assert plan.partial_lse_offset - plan.partial_o_offset >= plan.num_slots * group * dvo * 4
     assert plan.workspace_bytes >= plan.partial_lse_offset + plan.num_slots * group * 4
@@ -232,6 +240,7 @@ def test_random_plans_match_the_reference(seed):
     ref_waves, ref_merges = decode_partition_ref(lens, window, splits, hkv)
     assert [[tuple(r) for r in w.tolist()] for w in pa.decode_waves(plan, buf)] == ref_waves
     assert [tuple(r) for r in pa.decode_merges(plan, buf).tolist()] == ref_merges
+    assert plan.deferred_partials == deferred_rule(ref_waves)
     qo = [int(rng.integers(0, L + 1)) for L in lens]
     causal = bool(rng.integers(0, 2))
     pgroup = int(rng.choice([1, 2, 6, 16]))
