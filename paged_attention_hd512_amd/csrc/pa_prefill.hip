@@ -27,14 +27,18 @@
 //     max, so the result is unchanged.
 // Every wave reads the whole K and V stage from LDS (64 KB at 512/512) for its 16 rows: 1 KB
 // of LDS reads per 16-clock MFMA, so the MFMA pipes run only as fast as the LDS delivers
-// (256 B per clock per CU at most) and as its latency is hidden.
+// (measured per CU: ~230 B per clock for 16-byte reads, ~150 for the 8-byte and
+// transposing reads that V takes) and as its latency is hidden.
 // FP8 E4M3FN KV (the Triton page, section "Approach": FP8 caches are cast on load by the
-// same kernels in both phases) and NVFP4 KV (the FlashInfer page, sections "Summary" and
-// "What's in it": packed E2M1 with one E4M3 block scale per 16 head_dim elements): a
-// direct-to-LDS copy cannot convert, so each wave loads its key rows' codes (and block
-// scales) into registers and writes them to LDS as bf16 (exact for both formats), in the
-// same swizzled layout, before the barrier that hands the stage over.  k_scale folds into
-// the score scale and v_scale into the final normalisation.
+// same kernels in both phases): the stages hold the codes themselves, copied direct to LDS
+// like bf16 rows (half the bytes), and every operand read from LDS is widened to bf16 in
+// registers (exact) just before its MFMA: K with ds_read_b64 (8 codes), V with
+// ds_read_b64_tr_b8 (8 keys of one dim).  NVFP4 KV (the FlashInfer page, sections "Summary"
+// and "What's in it": packed E2M1 with one E4M3 block scale per 16 head_dim elements): a
+// direct-to-LDS copy cannot convert, so each wave loads its key rows' codes and block
+// scales into registers and writes them to LDS as bf16 (exact), in the same swizzled
+// layout, before the barrier that hands the stage over.  k_scale folds into the score
+// scale and v_scale into the final normalisation.
 // The score scale may have any sign: the kernel works with |scale| and flips the sign bits
 // of Q when the scale is negative (a zero scale zeroes Q, so every visible key weighs the
 // same), so masks and running maxima are taken on scores that grow with the scaled ones.
@@ -97,6 +101,10 @@ struct PrefillArgs {
 // transpose read and its neighbouring lane block.
 __device__ __forceinline__ int k_swz(int row) { return row & 15; }
 __device__ __forceinline__ int v_swz(int row) { return 2 * (row & 7); }
+// FP8 stages: a V-operand read (ds_read_b64_tr_b8) touches key rows 4g .. 4g+3 and
+// 16+4g .. 16+4g+3 of a lane block g at one chunk; this swizzle gives each of the 16 rows
+// of two neighbouring blocks its own chunk position.
+__device__ __forceinline__ int v_swz_fp8(int row) { return (row & 7) | ((row & 16) >> 1); }
 
 // Waits until at most N of this wave's vector memory operations are outstanding.
 template <int N>
@@ -125,6 +133,15 @@ __device__ __forceinline__ u32x2_t lds_read_tr16_at(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
 }
+// ds_read_b64_tr_b8, likewise: within each 16-lane block, lane 8c + e receives byte e of
+// the 8-byte segments addressed by lanes c, c + 2, .., c + 14 (in that order; measured on
+// the GPU with an in-bounds probe).
+template <int OFF>
+__device__ __forceinline__ u32x2_t lds_read_tr8_at(uint32_t addr) {
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
 // Waits until at most N LDS (or scalar memory) operations of this wave are outstanding.
 // The registers that the awaited reads fill pass through the statement, so the compiler
 // cannot use or copy them before it.
@@ -132,6 +149,21 @@ template <int N>
 __device__ __forceinline__ void lds_wait(u32x2_t& a, u32x2_t& b) {
   static_assert(N >= 0 && N < 16, "lgkmcnt range");
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2_t& a) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+
+// Eight FP8 E4M3FN codes (byte i = element i) as eight bf16 values, exact (every E4M3FN
+// value is a bf16 value); the conversion's scale operand is 1.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(u32x2_t c) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[0], 1.0f, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[0], 1.0f, true);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[1], 1.0f, false);
+  const auto e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[1], 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
 }
 
 // Page and slot of a wave-uniform logical token, through a scalar load.
@@ -165,15 +197,17 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
 
 template <int DQK, int DVO, int PM, int KV>
 __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
-  constexpr bool CONV = KV != kKvBf16;  // stages pass through registers and are converted
   constexpr bool FP4 = KV == kKvFp4;
+  constexpr bool CONV = FP4;                // stages pass through registers and are converted
+  constexpr bool F8 = KV == kKvFp8;         // stages hold the FP8 codes; operands widen after the read
+  constexpr int EB = F8 ? 1 : 2;            // bytes per staged element
   constexpr int NW = kPrefillWaves;
   constexpr int KS = kKeyStage;
   constexpr int QSTEPS = DQK / 32;          // MFMA K-steps of S^T
   constexpr int OT = DVO / 16;              // 16-wide head_dim tiles of O^T
-  constexpr int KCH = DQK / 8;              // 16-byte chunks per K row
-  constexpr int VCH = DVO / 8;
-  constexpr int KRPI = 64 / KCH;            // K rows per copy instruction (1 or 2)
+  constexpr int KCH = DQK * EB / 16;        // 16-byte chunks per K row
+  constexpr int VCH = DVO * EB / 16;
+  constexpr int KRPI = 64 / KCH;            // K rows per copy instruction (1, 2 or 4)
   constexpr int VRPI = 64 / VCH;
   constexpr int RPW = KS / NW;              // key rows each wave copies per stage
   static_assert(RPW == 4, "each wave copies four key rows per stage");
@@ -182,7 +216,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   // 512/512 fit in 253 VGPRs and measured ~1 % faster than one; the converting kernels,
   // which also hold a stage's codes in registers, keep one.
   constexpr int KD = DVO == 512 ? (CONV ? 1 : 2) : 4;
-  constexpr int VD = DVO == 512 ? 2 : 4;
+  constexpr int VD = DVO == 512 ? (F8 ? 4 : 2) : 4;
 
   // K stages are double-buffered, V stages triple-buffered: half of the waves use a stage's
   // V one interval after its K (see the stage loop below).  One array per K buffer: the
@@ -190,10 +224,12 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   // the other, and does not make them wait for those copies (V is read by inline assembly,
   // which the compiler does not track).  1 KB alignment: the swizzled read addresses below
   // differ from a per-lane base only in bits the base leaves zero, so one XOR forms each.
+  using st_t = typename std::conditional<F8, uint8_t, uint16_t>::type;  // staged element
   constexpr int VSTAGE = KS * DVO;  // elements of one V buffer
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[KS * DQK], k_lds1[KS * DQK];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[3 * VSTAGE];
-  auto k_buf = [&](auto slot_c) -> uint16_t* { if constexpr (decltype(slot_c)::value == 0) return k_lds0; else return k_lds1; };
+  __shared__ __attribute__((aligned(1024))) st_t k_lds0[KS * DQK], k_lds1[KS * DQK];
+  __shared__ __attribute__((aligned(1024))) st_t v_lds[3 * VSTAGE];
+  auto k_buf = [&](auto slot_c) -> st_t* { if constexpr (decltype(slot_c)::value == 0) return k_lds0; else return k_lds1; };
+  auto vswz = [](int row) { return F8 ? v_swz_fp8(row) : v_swz(row); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -343,7 +379,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
       constexpr int i = (IDX - NKC) * VRPI;
       const int row = my_row + i + (VRPI == 1 ? 0 : (int)((uint32_t)ln / VCH));
       const uint32_t off = (uint32_t)min(row, c_last_row) * (uint32_t)a.v_st +
-                           16u * (((uint32_t)ln % VCH) ^ v_swz(row));
+                           16u * (((uint32_t)ln % VCH) ^ vswz(row));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c_vr,
           (__attribute__((address_space(3))) void*)(v_lds + vo + (my_row + i) * DVO), 16, off, 0, 0, 0);
     }
@@ -399,11 +435,11 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
       for (int u = 0; u < 4; ++u) pk[u] = pack_bf16(e[2 * u] * bs, e[2 * u + 1] * bs);
       return pk;
     };
-    uint16_t* kd = k_buf(slot_c) + row * DQK;
+    st_t* kd = k_buf(slot_c) + row * DQK;
 #pragma unroll
     for (int k = 0; k < KC; ++k)
       *(u32x4_t*)(kd + 8 * ((part + 16 * k) ^ k_swz(row))) = chunk8(fk[k], fp8_to_f32<0>(fks[k]));
-    uint16_t* vd = v_lds + vo + row * DVO;
+    st_t* vd = v_lds + vo + row * DVO;
 #pragma unroll
     for (int k = 0; k < VC; ++k)
       *(u32x4_t*)(vd + 8 * ((part + 16 * k) ^ v_swz(row))) = chunk8(fv[k], fp8_to_f32<0>(fvs[k]));
@@ -411,48 +447,13 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   };
 
-  // FP8: chunk c is 8 codes at 8 c.
-  u32x2_t f8k[KC], f8v[VC];
-  auto fp8_load = [&](int st) {
-    const int part = lane & 15;
-    const char *kd, *vd, *ks = nullptr, *vs = nullptr;
-    conv_rows(st, kd, vd, ks, vs);
-#pragma unroll
-    for (int k = 0; k < KC; ++k) f8k[k] = *(const u32x2_t*)(kd + 8 * (part + 16 * k));
-#pragma unroll
-    for (int k = 0; k < VC; ++k) f8v[k] = *(const u32x2_t*)(vd + 8 * (part + 16 * k));
-  };
-  // Widens the loaded codes to bf16 (exact) and writes chunk c at position c ^ swizzle(row).
-  auto fp8_store = [&](auto slot_c, int vo) {
-    const int row = my_row + (lane >> 4);
-    const int part = lane & 15;
-    auto chunk8 = [&](u32x2_t w) {
-      const u32x2_t lo = fp8x4_to_bf16x4(w[0]), hi = fp8x4_to_bf16x4(w[1]);
-      return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-    };
-    uint16_t* kd = k_buf(slot_c) + row * DQK;
-#pragma unroll
-    for (int k = 0; k < KC; ++k)
-      *(u32x4_t*)(kd + 8 * ((part + 16 * k) ^ k_swz(row))) = chunk8(f8k[k]);
-    uint16_t* vd = v_lds + vo + row * DVO;
-#pragma unroll
-    for (int k = 0; k < VC; ++k)
-      *(u32x4_t*)(vd + 8 * ((part + 16 * k) ^ v_swz(row))) = chunk8(f8v[k]);
-    // The writes complete before this wave reaches the barrier that hands the stage over.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  };
-  auto conv_store = [&](auto slot_c, int vo) {
-    if constexpr (FP4) fp4_store(slot_c, vo);
-    else fp8_store(slot_c, vo);
-  };
+  auto conv_store = [&](auto slot_c, int vo) { fp4_store(slot_c, vo); };
 
   // Copies stage st: K into buffer slot_c, V into v_lds + vo (converting formats: loads the
   // codes into registers; conv_store then writes them).
   auto copy_stage = [&](int st, auto slot_c, int vo) {
     if constexpr (FP4) {
       fp4_load(st);
-    } else if constexpr (CONV) {
-      fp8_load(st);
     } else if constexpr (PM == kPagesStage) {
       copy_prep(st);
       static_for<NCOPY>([&](auto idx_c) { copy_one(idx_c, slot_c, vo); });
@@ -468,11 +469,21 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
       };
       int ln = lane;
       asm volatile("" : "+v"(ln));
+      // Row base of lane sub-row `sub` when one instruction covers RPI rows.
+      auto sub_base = [&](auto rpi_c, int i, uint32_t sub, const char* base, int64_t sp, int64_t stt) {
+        constexpr int RPI = decltype(rpi_c)::value;
+        const char* rb = row_base(i, base, sp, stt);
+#pragma unroll
+        for (int u = 1; u < RPI; ++u) {
+          const char* ru = row_base(i + u, base, sp, stt);
+          rb = sub == (uint32_t)u ? ru : rb;
+        }
+        return rb;
+      };
 #pragma unroll
       for (int i = 0; i < RPW; i += KRPI) {
         const uint32_t sub = KRPI == 1 ? 0u : (uint32_t)ln / KCH;
-        const char* rb = row_base(i, k_base, a.k_sp, a.k_st);
-        if constexpr (KRPI == 2) rb = sub ? row_base(i + 1, k_base, a.k_sp, a.k_st) : rb;
+        const char* rb = sub_base(std::integral_constant<int, KRPI>{}, i, sub, k_base, a.k_sp, a.k_st);
         const uint32_t off = 16u * (((uint32_t)ln % KCH) ^ k_swz(my_row + i + (int)sub));
         __builtin_amdgcn_global_load_lds((const void*)(rb + off),
             (__attribute__((address_space(3))) void*)(k_buf(slot_c) + (my_row + i) * DQK), 16, 0, 0);
@@ -480,9 +491,8 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < RPW; i += VRPI) {
         const uint32_t sub = VRPI == 1 ? 0u : (uint32_t)ln / VCH;
-        const char* rb = row_base(i, v_base, a.v_sp, a.v_st);
-        if constexpr (VRPI == 2) rb = sub ? row_base(i + 1, v_base, a.v_sp, a.v_st) : rb;
-        const uint32_t off = 16u * (((uint32_t)ln % VCH) ^ v_swz(my_row + i + (int)sub));
+        const char* rb = sub_base(std::integral_constant<int, VRPI>{}, i, sub, v_base, a.v_sp, a.v_st);
+        const uint32_t off = 16u * (((uint32_t)ln % VCH) ^ vswz(my_row + i + (int)sub));
         __builtin_amdgcn_global_load_lds((const void*)(rb + off),
             (__attribute__((address_space(3))) void*)(v_lds + vo + (my_row + i) * DVO), 16, 0, 0);
       }
@@ -512,19 +522,48 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   f32x4_t s0, s1;
   auto qk = [&](auto kslot_c, auto copy_c, int vo_next) {
     constexpr bool COPY = decltype(copy_c)::value;
-    const uint16_t* kt = k_buf(kslot_c);
+    const st_t* kt = k_buf(kslot_c);
     s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
     s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // With COPY this wave issues the copies of its own rows and of its SIMD partner's.
     constexpr int NQC = 2 * NCOPY;
     constexpr int CSTEP = QSTEPS / NQC > 0 ? QSTEPS / NQC : 1;
     static_assert(!COPY || (QSTEPS + CSTEP - 1) / CSTEP >= NQC, "copy slots");
+    if constexpr (F8) {
+      // Lane (g4, n): codes 32j + 8 g4 .. +7 of key rows n and 16 + n, i.e. half g4 & 1 of
+      // chunk 2j + (g4 >> 1), which sits at chunk position (2j + (g4 >> 1)) ^ n.  Bits 5-7
+      // of kb hold n >> 1 and nothing else, so step j's byte offset is kb ^ 32 (j & 7), plus
+      // 256 (j >> 3).  Eight codes widen to the eight bf16 values of the A operand.
+      constexpr int KD8 = 4;
+      int kb = n * DQK + 16 * ((g4 >> 1) ^ (n & 1)) + 8 * (g4 & 1) + 32 * (n >> 1);
+      asm volatile("" : "+v"(kb));
+      auto ld = [&](int j, u32x2_t& k0, u32x2_t& k1) {
+        const st_t* src = kt + ((kb ^ (32 * (j & 7))) + 256 * (j >> 3));
+        k0 = *(const u32x2_t*)src;
+        k1 = *(const u32x2_t*)(src + 16 * DQK);
+      };
+      u32x2_t kr0[KD8 + 1], kr1[KD8 + 1];
+#pragma unroll
+      for (int j = 0; j < KD8; ++j) ld(j, kr0[j], kr1[j]);
+      static_for<QSTEPS>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        if constexpr (j + KD8 < QSTEPS) ld(j + KD8, kr0[(j + KD8) % (KD8 + 1)], kr1[(j + KD8) % (KD8 + 1)]);
+        if constexpr (COPY && j % CSTEP == 0 && j / CSTEP < NQC)
+          copy_one(std::integral_constant<int, j / CSTEP>{},
+                   std::integral_constant<int, decltype(kslot_c)::value ^ 1>{}, vo_next);
+        const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, qf[j]);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(kr0[j % (KD8 + 1)]), qb, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(kr1[j % (KD8 + 1)]), qb, s1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      return;
+    }
     // Element index of the step-j chunk: kb ^ 32*(j & 3) (bits 5-6 of kb hold n >> 2 and
     // nothing else does), plus 128*(j >> 2).
     int kb = n * DQK + 8 * (g4 ^ (n & 3)) + 32 * (n >> 2);
     asm volatile("" : "+v"(kb));
     auto ld = [&](int j, u32x4_t& k0, u32x4_t& k1) {
-      const uint16_t* src = kt + ((kb ^ (32 * (j & 3))) + 128 * (j >> 2));
+      const st_t* src = kt + ((kb ^ (32 * (j & 3))) + 128 * (j >> 2));
       k0 = *(const u32x4_t*)src;
       k1 = *(const u32x4_t*)(src + 16 * DQK);
     };
@@ -615,8 +654,38 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)(
           v_lds + tr_row * DVO + 4 * (n & 1) + 8 * ((n & 3) >> 1)) +
       32u * (uint32_t)(tr_row & 7);
+  // FP8 stages: the A operand's k-slots follow P's, keys 4 g4 + 0..3 then 16 + 4 g4 + 0..3.
+  // Lane (g4, n) of a transpose read addresses the key row of k-slot n >> 1, half n & 1 of
+  // tile t's chunk (the 16 codes of dims 16t .. 16t + 15), at chunk position t ^ swizzle;
+  // it receives dim 16t + n of the eight k-slot keys: one read per tile gives the eight
+  // codes of the A operand.  Bits 4-7 of vb8_lane hold the swizzle and nothing else, so
+  // tile t's address is vb8_lane ^ 16 (t & 15), plus 256 (t >> 4) as the instruction offset.
+  const int tr8_row = 4 * g4 + ((n >> 1) & 3) + 16 * (n >> 3);
+  const uint32_t vb8_lane =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const st_t*)(
+          v_lds + tr8_row * DVO + (F8 ? 8 * (n & 1) : 0)) +
+      16u * (uint32_t)v_swz_fp8(tr8_row);
   auto pv = [&](int vo) {
     const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pf);
+    if constexpr (F8) {
+      uint32_t vb = vb8_lane + (uint32_t)vo;
+      asm volatile("" : "+v"(vb));
+      u32x2_t vr[VD + 1];
+      auto ld = [&](auto t_c) {
+        constexpr int t = decltype(t_c)::value;
+        vr[t % (VD + 1)] = lds_read_tr8_at<256 * (t >> 4)>(vb ^ (16u * (t & 15)));
+      };
+      static_for<VD>([&](auto t_c) { ld(t_c); });
+      static_for<OT>([&](auto t_c) {
+        constexpr int t = decltype(t_c)::value;
+        constexpr int r = t % (VD + 1);
+        if constexpr (t + VD < OT) ld(std::integral_constant<int, t + VD>{});
+        lds_wait<(t + VD < OT ? VD : OT - 1 - t)>(vr[r]);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(vr[r]), pb, o[t], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      return;
+    }
     uint32_t vb = vb_lane + 2u * (uint32_t)vo;
     asm volatile("" : "+v"(vb));
     u32x2_t vlo[VD + 1], vhi[VD + 1];
@@ -718,7 +787,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   const float l_bf_tot = sum_xor32(sum_xor16(l_bf));
   if (!row_valid) return;
   float inv = l_bf_tot > 0.f ? 1.f / l_bf_tot : 0.f;
-  if constexpr (CONV) inv *= a.v_scale;
+  if constexpr (KV != kKvBf16) inv *= a.v_scale;
   if (it.slot >= 0) {
     // One key chunk of a split tile: its normalised output and two log-sum-exps, over the
     // bf16-rounded weights (the merge weights, so the merged output is normalised by the
@@ -819,8 +888,11 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeArgs a) 
 template <int DQK, int DVO>
 static void launch_prefill(const PrefillArgs& a, int pm, int kv, int grid, hipStream_t s) {
   if (kv == kKvFp4) prefill_kernel<DQK, DVO, kPagesAny, kKvFp4><<<grid, 512, 0, s>>>(a);
-  else if (kv == kKvFp8) prefill_kernel<DQK, DVO, kPagesAny, kKvFp8><<<grid, 512, 0, s>>>(a);
-  else if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvBf16><<<grid, 512, 0, s>>>(a);
+  else if (kv == kKvFp8) {
+    if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvFp8><<<grid, 512, 0, s>>>(a);
+    else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2, kKvFp8><<<grid, 512, 0, s>>>(a);
+    else prefill_kernel<DQK, DVO, kPagesAny, kKvFp8><<<grid, 512, 0, s>>>(a);
+  } else if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvBf16><<<grid, 512, 0, s>>>(a);
   else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2, kKvBf16><<<grid, 512, 0, s>>>(a);
   else prefill_kernel<DQK, DVO, kPagesAny, kKvBf16><<<grid, 512, 0, s>>>(a);
 }

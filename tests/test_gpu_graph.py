@@ -49,15 +49,18 @@ def replay_and_check(name, g, q, new_qs, eager, out_g, lse_g):
         assert torch.equal(lse_g, lse_e), f"{name}: replay {i} lse differs from eager"
 
 
-@pytest.mark.parametrize("splits", [0, 8])
-def test_decode_step_replays_from_a_graph(splits):
-    name = f"graph decode splits={splits}"
+@pytest.mark.parametrize("lens,splits,parked", [([37, 300, 1024, 5000, 16], 0, 0),
+                                                 ([37, 300, 1024, 5000, 16], 8, 0),
+                                                 ([700, 1500, 37, 3000, 900], 8, 1)])
+def test_decode_step_replays_from_a_graph(lens, splits, parked):
+    """The last case's plan parks split results in LDS (deferred_partials)."""
+    name = f"graph decode splits={splits} parked={parked}"
     say(name)
-    c = make_decode_case([37, 300, 1024, 5000, 16], 24, 4, 512, 16, num_splits=splits,
-                         seed=41, device=dev())
+    c = make_decode_case(lens, 24, 4, 512, 16, num_splits=splits, seed=41, device=dev())
     run = PagedDecode(c.k_pool, c.v_pool, c.kv_indptr, c.kv_indices, c.kv_last_page_len,
                       c.num_qo_heads, kv_dtype=c.kv_dtype, sm_scale=c.sm_scale,
                       window=c.window, num_splits=c.num_splits, out_dtype=c.out_dtype)
+    assert run.plan.deferred_partials == parked
     q = c.q.clone()
     out_g, lse_g = run.run(q)
     torch.cuda.synchronize()

@@ -1,0 +1,77 @@
+"""CPU models of the FP8 prefill stage layout and operand reads (no GPU, no library).
+
+The FP8 prefill kernel keeps each 32-key stage's codes in LDS (16-byte chunk c of key row r
+at chunk position c ^ swizzle(r)) and widens every MFMA operand after reading it.  These
+models restate its address formulas and the measured lane layout of ds_read_b64_tr_b8
+(within each 16-lane block, lane 8c + e receives byte e of the 8-byte segments addressed by
+lanes c, c + 2, .., c + 14), and check that:
+
+* the K operand of S^T = K Q^T gives lane (g4, n) dims 32j + 8 g4 .. +7 of keys n and
+  16 + n (the 16x16x32 MFMA's A layout, keys on M);
+* the V^T operand of O^T += V^T P^T gives lane (g4, n) dim 16t + n of the keys of P's
+  k-slots, 4 g4 + 0..3 then 16 + 4 g4 + 0..3 (the order the S^T output leaves P in);
+* within a 16-lane block no two lanes read the same 8-byte bank slot of a 256-byte row.
+"""
+
+import pytest
+
+
+def k_swz(row):
+    return row & 15
+
+
+def v_swz_fp8(row):
+    return (row & 7) | ((row & 16) >> 1)
+
+
+def stage(width, swz):
+    """Byte address -> (key, dim) of a 32-key FP8 stage of rows `width` bytes wide."""
+    m = {}
+    for r in range(32):
+        for c in range(width // 16):
+            for b in range(16):
+                m[r * width + 16 * (c ^ swz(r)) + b] = (r, 16 * c + b)
+    return m
+
+
+@pytest.mark.parametrize("dqk", [512, 256])
+def test_fp8_k_operand_reads(dqk):
+    lds = stage(dqk, k_swz)
+    for j in range(dqk // 32):
+        for g4 in range(4):
+            slots = set()
+            for n in range(16):
+                kb = n * dqk + 16 * ((g4 >> 1) ^ (n & 1)) + 8 * (g4 & 1) + 32 * (n >> 1)
+                off = (kb ^ (32 * (j & 7))) + 256 * (j >> 3)
+                assert [lds[off + e] for e in range(8)] == [(n, 32 * j + 8 * g4 + e) for e in range(8)]
+                assert [lds[off + 16 * dqk + e] for e in range(8)] == \
+                    [(16 + n, 32 * j + 8 * g4 + e) for e in range(8)]
+                slots.add((off % 256) // 8)
+            assert len(slots) == 16
+
+
+@pytest.mark.parametrize("dvo", [512, 256])
+def test_fp8_v_operand_transpose_reads(dvo):
+    lds = stage(dvo, v_swz_fp8)
+    for t in range(dvo // 16):
+        for g4 in range(4):
+            addr = []
+            for n in range(16):
+                row = 4 * g4 + ((n >> 1) & 3) + 16 * (n >> 3)
+                base = row * dvo + 8 * (n & 1) + 16 * v_swz_fp8(row)
+                addr.append((base ^ (16 * (t & 15))) + 256 * (t >> 4))
+            keys = [4 * g4 + i for i in range(4)] + [16 + 4 * g4 + i for i in range(4)]
+            for n in range(16):
+                c, e = n // 8, n % 8
+                got = [lds[addr[c + 2 * j] + e] for j in range(8)]
+                assert got == [(k, 16 * t + n) for k in keys]
+            assert len({(a % 256) // 8 for a in addr}) == 16
+
+
+def test_the_plain_key_order_would_be_wrong():
+    """Positive control: reading keys 8 g4 .. 8 g4 + 7 (the natural order of the transpose
+    read) does not give P's k-slot order, which is the mistake these models guard."""
+    g4 = 1
+    natural = [8 * g4 + j for j in range(8)]
+    slots = [4 * g4 + i for i in range(4)] + [16 + 4 * g4 + i for i in range(4)]
+    assert natural != slots
