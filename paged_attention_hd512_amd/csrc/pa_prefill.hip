@@ -282,12 +282,14 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
 
   // Q^T operand for the whole tile: step j holds dims 32j + 8*g4 .. +7 of row n.  Loaded
   // before any stage copy, so waiting for a copy also covers it.
+  // FP8 stages pair the steps (see qk): step j holds dims 64 (j >> 1) + 16 g4 + 8 (j & 1)
+  // .. +7 instead.
   u32x4_t qf[QSTEPS];
   {
-    const uint16_t* src = a.q + q_row * DQK + 8 * g4;
+    const uint16_t* src = a.q + q_row * DQK + (F8 ? 16 : 8) * g4;
 #pragma unroll
     for (int j = 0; j < QSTEPS; ++j)
-      qf[j] = *(const u32x4_t*)(src + 32 * j);
+      qf[j] = *(const u32x4_t*)(src + (F8 ? 64 * (j >> 1) + 8 * (j & 1) : 32 * j));
 #pragma unroll
     for (int j = 0; j < QSTEPS; ++j) qf[j] = (qf[j] & a.q_and) ^ a.q_xor;
   }
@@ -530,30 +532,36 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     constexpr int CSTEP = QSTEPS / NQC > 0 ? QSTEPS / NQC : 1;
     static_assert(!COPY || (QSTEPS + CSTEP - 1) / CSTEP >= NQC, "copy slots");
     if constexpr (F8) {
-      // Lane (g4, n): codes 32j + 8 g4 .. +7 of key rows n and 16 + n, i.e. half g4 & 1 of
-      // chunk 2j + (g4 >> 1), which sits at chunk position (2j + (g4 >> 1)) ^ n.  Bits 5-7
-      // of kb hold n >> 1 and nothing else, so step j's byte offset is kb ^ 32 (j & 7), plus
-      // 256 (j >> 3).  Eight codes widen to the eight bf16 values of the A operand.
-      constexpr int KD8 = 4;
-      int kb = n * DQK + 16 * ((g4 >> 1) ^ (n & 1)) + 8 * (g4 & 1) + 32 * (n >> 1);
+      // The contraction order over head_dim is free as long as K and Q agree: steps 2p and
+      // 2p + 1 take lane group g4's dims 64p + 16 g4 .. +15, so one 16-byte read of key row
+      // n (and 16 + n) serves both (codes 0-7, then 8-15).  That chunk, 4p + g4, sits at
+      // position (4p + g4) ^ n; bits 6-7 of kb hold n >> 2 and nothing else, so pair p's
+      // byte offset is kb ^ 64 (p & 3), plus 256 (p >> 2).  Eight codes widen to the
+      // eight bf16 values of an A operand.
+      constexpr int KP = 2;  // pairs read ahead
+      int kb = n * DQK + 16 * (g4 ^ (n & 3)) + 64 * (n >> 2);
       asm volatile("" : "+v"(kb));
-      auto ld = [&](int j, u32x2_t& k0, u32x2_t& k1) {
-        const st_t* src = kt + ((kb ^ (32 * (j & 7))) + 256 * (j >> 3));
-        k0 = *(const u32x2_t*)src;
-        k1 = *(const u32x2_t*)(src + 16 * DQK);
+      auto ld = [&](int p, u32x4_t& k0, u32x4_t& k1) {
+        const st_t* src = kt + ((kb ^ (64 * (p & 3))) + 256 * (p >> 2));
+        k0 = *(const u32x4_t*)src;
+        k1 = *(const u32x4_t*)(src + 16 * DQK);
       };
-      u32x2_t kr0[KD8 + 1], kr1[KD8 + 1];
+      u32x4_t kr0[KP + 1], kr1[KP + 1];
 #pragma unroll
-      for (int j = 0; j < KD8; ++j) ld(j, kr0[j], kr1[j]);
+      for (int p = 0; p < KP; ++p) ld(p, kr0[p], kr1[p]);
       static_for<QSTEPS>([&](auto j_c) {
         constexpr int j = decltype(j_c)::value;
-        if constexpr (j + KD8 < QSTEPS) ld(j + KD8, kr0[(j + KD8) % (KD8 + 1)], kr1[(j + KD8) % (KD8 + 1)]);
+        constexpr int p = j >> 1, r = p % (KP + 1);
+        if constexpr ((j & 1) == 0 && p + KP < QSTEPS / 2)
+          ld(p + KP, kr0[(p + KP) % (KP + 1)], kr1[(p + KP) % (KP + 1)]);
         if constexpr (COPY && j % CSTEP == 0 && j / CSTEP < NQC)
           copy_one(std::integral_constant<int, j / CSTEP>{},
                    std::integral_constant<int, decltype(kslot_c)::value ^ 1>{}, vo_next);
         const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, qf[j]);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(kr0[j % (KD8 + 1)]), qb, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(kr1[j % (KD8 + 1)]), qb, s1, 0, 0, 0);
+        const u32x2_t c0 = {kr0[r][2 * (j & 1)], kr0[r][2 * (j & 1) + 1]};
+        const u32x2_t c1 = {kr1[r][2 * (j & 1)], kr1[r][2 * (j & 1) + 1]};
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(c0), qb, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(c1), qb, s1, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       });
       return;

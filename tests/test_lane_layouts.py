@@ -6,8 +6,9 @@ models restate its address formulas and the measured lane layout of ds_read_b64_
 (within each 16-lane block, lane 8c + e receives byte e of the 8-byte segments addressed by
 lanes c, c + 2, .., c + 14), and check that:
 
-* the K operand of S^T = K Q^T gives lane (g4, n) dims 32j + 8 g4 .. +7 of keys n and
-  16 + n (the 16x16x32 MFMA's A layout, keys on M);
+* the K operand of S^T = K Q^T: steps 2p and 2p + 1 take lane group g4's dims
+  64p + 16 g4 .. +15 (Q is loaded in the same order), so one 16-byte read gives lane
+  (g4, n) those 16 codes of keys n and 16 + n (the 16x16x32 MFMA's A layout, keys on M);
 * the V^T operand of O^T += V^T P^T gives lane (g4, n) dim 16t + n of the keys of P's
   k-slots, 4 g4 + 0..3 then 16 + 4 g4 + 0..3 (the order the S^T output leaves P in);
 * within a 16-lane block no two lanes read the same 8-byte bank slot of a 256-byte row.
@@ -37,16 +38,16 @@ def stage(width, swz):
 @pytest.mark.parametrize("dqk", [512, 256])
 def test_fp8_k_operand_reads(dqk):
     lds = stage(dqk, k_swz)
-    for j in range(dqk // 32):
+    for p in range(dqk // 64):
         for g4 in range(4):
             slots = set()
             for n in range(16):
-                kb = n * dqk + 16 * ((g4 >> 1) ^ (n & 1)) + 8 * (g4 & 1) + 32 * (n >> 1)
-                off = (kb ^ (32 * (j & 7))) + 256 * (j >> 3)
-                assert [lds[off + e] for e in range(8)] == [(n, 32 * j + 8 * g4 + e) for e in range(8)]
-                assert [lds[off + 16 * dqk + e] for e in range(8)] == \
-                    [(16 + n, 32 * j + 8 * g4 + e) for e in range(8)]
-                slots.add((off % 256) // 8)
+                kb = n * dqk + 16 * (g4 ^ (n & 3)) + 64 * (n >> 2)
+                off = (kb ^ (64 * (p & 3))) + 256 * (p >> 2)
+                want = [64 * p + 16 * g4 + e for e in range(16)]
+                assert [lds[off + e] for e in range(16)] == [(n, d) for d in want]
+                assert [lds[off + 16 * dqk + e] for e in range(16)] == [(16 + n, d) for d in want]
+                slots.add((off % 256) // 16)
             assert len(slots) == 16
 
 
