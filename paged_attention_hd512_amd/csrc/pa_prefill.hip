@@ -213,8 +213,9 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   static_assert(RPW == 4, "each wave copies four key rows per stage");
   // Read-ahead of the software pipelines (steps of S^T, tiles of O^T), bounded by the
   // registers left beside Q (DQK / 8 per lane) and O (DVO / 4 per lane).  Two steps of K at
-  // 512/512 fit in 253 VGPRs and measured ~1 % faster than one; the converting kernels,
-  // which also hold a stage's codes in registers, keep one.
+  // 512/512 fit in 253 VGPRs and measured ~1 % faster than one; the NVFP4 kernel, which
+  // also holds a stage's codes in registers, keeps one.  FP8 V tiles are half as wide in
+  // registers (read-ahead depths 2 to 6 of either measured within 1 %).
   constexpr int KD = DVO == 512 ? (CONV ? 1 : 2) : 4;
   constexpr int VD = DVO == 512 ? (F8 ? 4 : 2) : 4;
 
@@ -386,11 +387,12 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
           (__attribute__((address_space(3))) void*)(v_lds + vo + (my_row + i) * DVO), 16, off, 0, 0, 0);
     }
   };
-  // Converting formats: lane l holds key row my_row + l / 16 of the stage and, of its K and
-  // V rows, the 8-element chunks c = l % 16 + 16 k (k < D / 128), so that each store
-  // instruction writes 16 consecutive chunk positions of a row (a bank-conflict-free 256
-  // bytes; chunks strided by four positions per lane conflicted in 4-way groups).  Key rows
-  // are clamped into the tile's range like the copies' (clamped keys are masked out).
+  // NVFP4 (converted on the way in): lane l holds key row my_row + l / 16 of the stage
+  // and, of its K and V rows, the 8-element chunks c = l % 16 + 16 k (k < D / 128), so that
+  // each store instruction writes 16 consecutive chunk positions of a row (a
+  // bank-conflict-free 256 bytes; chunks strided by four positions per lane conflicted in
+  // 4-way groups).  Key rows are clamped into the tile's range like the copies' (clamped
+  // keys are masked out).
   constexpr int KC = DQK / 128, VC = DVO / 128;  // chunks per lane and row
   // Byte address of row t's K and V rows (and block-scale rows) in the pages.
   auto conv_rows = [&](int st, const char*& kd, const char*& vd, const char*& ks, const char*& vs) {
@@ -514,7 +516,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   // the issuing waves).  Other page sizes: every wave copies its own rows at the interval
   // start.
   constexpr bool SPREAD = PM == kPagesStage && !CONV;
-  // Converting formats at 512/512: the first group loads the next stage's codes after its
+  // NVFP4 at 512/512: the first group loads the next stage's codes after its
   // S^T (not before), and the second group stores them before its S^T, so the codes are
   // never live beside the K operands of S^T, where the registers peak.
   constexpr bool LATE = CONV && DQK == 512 && DVO == 512;
