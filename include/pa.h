@@ -329,7 +329,8 @@ pa_status pa_debug_gather_kv(const pa_kv_cache* cache, const pa_page_table* tabl
                              int32_t request, int32_t kv_len, int32_t kv_head, void* k_out,
                              void* v_out, void* stream);
 
-/* Converts n FP8 E4M3FN codes to fp32 with the same conversion the kernels use. */
+/* Converts n FP8 E4M3FN codes to fp32 with the decode kernels' conversion (prefill widens
+ * codes to bf16 with the FP8-to-bf16 conversion instruction; both are exact). */
 pa_status pa_debug_fp8_to_f32(const uint8_t* codes, float* out, int32_t n, void* stream);
 
 const char* pa_last_error(void);        /* thread-local message of the last failing call */
