@@ -31,9 +31,9 @@
 // transposing reads that V takes) and as its latency is hidden.
 // FP8 E4M3FN KV (the Triton page, section "Approach": FP8 caches are cast on load by the
 // same kernels in both phases): the stages hold the codes themselves, copied direct to LDS
-// like bf16 rows (half the bytes), and every operand read from LDS is widened to bf16 in
-// registers (exact) just before its MFMA: K with ds_read_b64 (8 codes), V with
-// ds_read_b64_tr_b8 (8 keys of one dim).  NVFP4 KV (the FlashInfer page, sections "Summary"
+// like bf16 rows (half the bytes).  V operands are widened to bf16 in registers (exact)
+// after each LDS read (ds_read_b64_tr_b8, 8 keys of one dim); S^T runs on the FP8 MFMA
+// with the K codes as they are and Q as two E4M3 terms (see qk).  NVFP4 KV (the FlashInfer page, sections "Summary"
 // and "What's in it": packed E2M1 with one E4M3 block scale per 16 head_dim elements): a
 // direct-to-LDS copy cannot convert, so each wave loads its key rows' codes and block
 // scales into registers and writes them to LDS as bf16 (exact), in the same swizzled
@@ -156,6 +156,8 @@ __device__ __forceinline__ void lds_wait(u32x2_t& a) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
 }
 
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
 // Eight FP8 E4M3FN codes (byte i = element i) as eight bf16 values, exact (every E4M3FN
 // value is a bf16 value); the conversion's scale operand is 1.
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(u32x2_t c) {
@@ -200,6 +202,10 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   constexpr bool FP4 = KV == kKvFp4;
   constexpr bool CONV = FP4;                // stages pass through registers and are converted
   constexpr bool F8 = KV == kKvFp8;         // stages hold the FP8 codes; operands widen after the read
+  // FP8 S^T on the FP8 MFMA (K codes as they are, Q in two E4M3 terms), except at 512/512
+  // with per-row page lookups, whose addressing leaves no registers for it (it spilled);
+  // there K widens to bf16 like V.
+  constexpr bool F8MF = F8 && (PM == kPagesStage || DQK != 512 || DVO != 512);
   constexpr int EB = F8 ? 1 : 2;            // bytes per staged element
   constexpr int NW = kPrefillWaves;
   constexpr int KS = kKeyStage;
@@ -283,10 +289,57 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
 
   // Q^T operand for the whole tile: step j holds dims 32j + 8*g4 .. +7 of row n.  Loaded
   // before any stage copy, so waiting for a copy also covers it.
-  // FP8 stages pair the steps (see qk): step j holds dims 64 (j >> 1) + 16 g4 + 8 (j & 1)
-  // .. +7 instead.
-  u32x4_t qf[QSTEPS];
-  {
+  u32x4_t qf[F8MF ? 1 : QSTEPS];
+  // FP8 stages: S^T runs on the FP8 MFMA (16x16x128, see qk), whose B operand holds, in
+  // lane (g4, n) at step s, dims 128 s + 32 g4 .. +31 of row n as E4M3 codes.  The 128
+  // dims of a (row, step) are scaled by 2^e8 so that their largest magnitude lies in
+  // [128, 256), and split into two E4M3 terms, hi = e4m3(q 2^e8) and lo = e4m3(q 2^e8 -
+  // hi): their sum is q 2^e8 exactly for every element of at least 1/2 (the top ~9
+  // binades), and within 2^-10 of it below.  The MFMA's E8M0 B scale, 2^-e8, undoes the
+  // factor.  One exponent per (row, step): the MFMA applies the scale of lane group j to a
+  // block of 32 k-slots that spans two lane groups' halves (measured), so the four lane
+  // groups of a row carry the same scale.
+  constexpr int QS8 = DQK / 128;
+  i32x8_t qh[F8MF ? QS8 : 1], ql[F8MF ? QS8 : 1];
+  uint32_t qscale = 0;  // E8M0 byte of step s at bits 8 s
+  if constexpr (F8MF) {
+    const uint16_t* src = a.q + q_row * DQK + 32 * g4;
+#pragma unroll
+    for (int st8 = 0; st8 < QS8; ++st8) {
+      u32x4_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = (*(const u32x4_t*)(src + 128 * st8 + 8 * u) & a.q_and) ^ a.q_xor;
+      float mx = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[u][e])), fabsf(bf16_hi(v[u][e]))));
+      mx = max_xor32(max_xor16(mx));  // the row's four lane groups
+      int ex = 0;
+      frexpf(mx, &ex);  // mx < 2^ex
+      const int e8 = mx > 0.f ? min(max(8 - ex, -127), 127) : 0;
+      const float up = __builtin_ldexpf(1.f, e8);
+      qscale |= (uint32_t)(127 - e8) << (8 * st8);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float x0 = bf16_lo(v[u][2 * e]) * up, x1 = bf16_hi(v[u][2 * e]) * up;
+          const float x2 = bf16_lo(v[u][2 * e + 1]) * up, x3 = bf16_hi(v[u][2 * e + 1]) * up;
+          int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+          h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
+          const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+          const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+          int l = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01[0], x1 - h01[1], 0, false);
+          l = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23[0], x3 - h23[1], l, true);
+          qh[st8][2 * u + e] = h;
+          ql[st8][2 * u + e] = l;
+        }
+      }
+    }
+  } else {
+    // bf16 operands: step j holds dims 32j + 8 g4 .. +7 of row n; FP8 stages widened to
+    // bf16 pair the steps instead (see qk): dims 64 (j >> 1) + 16 g4 + 8 (j & 1) .. +7.
     const uint16_t* src = a.q + q_row * DQK + (F8 ? 16 : 8) * g4;
 #pragma unroll
     for (int j = 0; j < QSTEPS; ++j)
@@ -533,13 +586,56 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     constexpr int NQC = 2 * NCOPY;
     constexpr int CSTEP = QSTEPS / NQC > 0 ? QSTEPS / NQC : 1;
     static_assert(!COPY || (QSTEPS + CSTEP - 1) / CSTEP >= NQC, "copy slots");
+    if constexpr (F8MF) {
+      // v_mfma_scale_f32_16x16x128_f8f6f4 on the codes as they are: step s contracts over
+      // dims 128 s .. +127, lane (g4, n) holding dims 128 s + 32 g4 .. +31 of key row n (A)
+      // and the query's hi and lo terms (B; one MFMA each, measured: A's lane/byte k-slot
+      // pairs with B's at the same lane group and byte).  The 32 codes are chunks 8s + 2 g4
+      // and 8s + 2 g4 + 1 of the row, at positions (8s + 2 g4 + h) ^ n, i.e.
+      // 8 (s ^ (n >> 3)) + ((2 g4 + h) ^ (n & 7)): with bit 7 of kb holding n >> 3 (DQK 256:
+      // s < 2) and bit 4 the low bit of (2 g4) ^ (n & 7), the reads are at kb ^ 128 s and
+      // kb ^ 16 ^ 128 s.
+      constexpr int CPS = (NQC + QS8 - 1) / QS8;  // copies issued per step
+      int kb = n * DQK + 128 * (n >> 3) + 16 * ((2 * g4) ^ (n & 7));
+      asm volatile("" : "+v"(kb));
+      // Key rows n (tile 0) and 16 + n (tile 1): one operand buffer each, refilled with the
+      // next step's codes right after the two MFMAs that read it.
+      auto ld = [&](int st8, int tile) {
+        const st_t* p0 = kt + (kb ^ (128 * st8)) + 16 * DQK * tile;
+        const st_t* p1 = kt + ((kb ^ 16) ^ (128 * st8)) + 16 * DQK * tile;
+        const u32x4_t a0 = *(const u32x4_t*)p0, a1 = *(const u32x4_t*)p1;
+        return i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+      };
+      i32x8_t k0 = ld(0, 0), k1 = ld(0, 1);
+      static_for<QS8>([&](auto s_c) {
+        constexpr int st8 = decltype(s_c)::value;
+        if constexpr (COPY) {
+          static_for<CPS>([&](auto u_c) {
+            constexpr int ci = st8 * CPS + decltype(u_c)::value;
+            if constexpr (ci < NQC)
+              copy_one(std::integral_constant<int, ci>{},
+                       std::integral_constant<int, decltype(kslot_c)::value ^ 1>{}, vo_next);
+          });
+        }
+        constexpr int sa = 0x7F7F7F7F;  // E8M0 1.0 for the codes
+        s0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k0, qh[st8], s0, 0, 0, 0, sa, st8, (int)qscale);
+        s0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k0, ql[st8], s0, 0, 0, 0, sa, st8, (int)qscale);
+        s1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k1, qh[st8], s1, 0, 0, 0, sa, st8, (int)qscale);
+        s1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k1, ql[st8], s1, 0, 0, 0, sa, st8, (int)qscale);
+        if constexpr (st8 + 1 < QS8) {
+          k0 = ld(st8 + 1, 0);
+          k1 = ld(st8 + 1, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      return;
+    }
     if constexpr (F8) {
-      // The contraction order over head_dim is free as long as K and Q agree: steps 2p and
-      // 2p + 1 take lane group g4's dims 64p + 16 g4 .. +15, so one 16-byte read of key row
-      // n (and 16 + n) serves both (codes 0-7, then 8-15).  That chunk, 4p + g4, sits at
-      // position (4p + g4) ^ n; bits 6-7 of kb hold n >> 2 and nothing else, so pair p's
-      // byte offset is kb ^ 64 (p & 3), plus 256 (p >> 2).  Eight codes widen to the
-      // eight bf16 values of an A operand.
+      // K widened to bf16 after the read.  The contraction order over head_dim is free as
+      // long as K and Q agree: steps 2p and 2p + 1 take lane group g4's dims 64p + 16 g4 ..
+      // +15, so one 16-byte read of key row n (and 16 + n) serves both (codes 0-7, then
+      // 8-15).  That chunk, 4p + g4, sits at position (4p + g4) ^ n; bits 6-7 of kb hold
+      // n >> 2 and nothing else, so pair p's byte offset is kb ^ 64 (p & 3), plus 256 (p >> 2).
       constexpr int KP = 2;  // pairs read ahead
       int kb = n * DQK + 16 * (g4 ^ (n & 3)) + 64 * (n >> 2);
       asm volatile("" : "+v"(kb));

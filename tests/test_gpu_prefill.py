@@ -115,7 +115,9 @@ def test_fp8_prefill_single_key_rows_return_every_value_code_exactly(dqk, dvo, p
 
 def test_fp8_prefill_of_one_token_equals_fp8_decode():
     """Prefill with one new token per request and decode read the same FP8 cache; both
-    cast on load, so they agree with each other and with the oracle."""
+    cast on load, so they agree with each other and with the oracle.  Their outputs differ
+    by the prefill's bf16-rounded weights in P V (up to 2^-9 relative each; decode applies
+    fp32 weights), a few 1e-3 at most for these values, hence 5e-3."""
     say("fp8 prefill q_len 1 vs fp8 decode")
     from parity import gpu_decode, oracle_decode
     from synth import make_decode_case
@@ -131,7 +133,7 @@ def test_fp8_prefill_of_one_token_equals_fp8_decode():
     _, do, dl = gpu_decode(d)
     ref, ref_lse = oracle_decode(d)
     compare("fp8 prefill, one token", out_to_np(po), ref, pl.cpu().numpy(), ref_lse)
-    assert np.abs(out_to_np(po) - out_to_np(do)).max() < 2e-3
+    assert np.abs(out_to_np(po) - out_to_np(do)).max() < 5e-3
     assert np.abs(pl.cpu().numpy() - dl.cpu().numpy()).max() < 1e-4
 
 

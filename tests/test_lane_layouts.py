@@ -9,6 +9,9 @@ lanes c, c + 2, .., c + 14), and check that:
 * the K operand of S^T = K Q^T: steps 2p and 2p + 1 take lane group g4's dims
   64p + 16 g4 .. +15 (Q is loaded in the same order), so one 16-byte read gives lane
   (g4, n) those 16 codes of keys n and 16 + n (the 16x16x32 MFMA's A layout, keys on M);
+* the K operand of the FP8-MFMA form (v_mfma_scale_f32_16x16x128_f8f6f4, the one-lookup
+  path): lane (g4, n) holds dims 128 s + 32 g4 .. +31 of keys n and 16 + n, two 16-byte
+  reads per step;
 * the V^T operand of O^T += V^T P^T gives lane (g4, n) dim 16t + n of the keys of P's
   k-slots, 4 g4 + 0..3 then 16 + 4 g4 + 0..3 (the order the S^T output leaves P in);
 * within a 16-lane block no two lanes read the same 8-byte bank slot of a 256-byte row.
@@ -76,3 +79,20 @@ def test_the_plain_key_order_would_be_wrong():
     natural = [8 * g4 + j for j in range(8)]
     slots = [4 * g4 + i for i in range(4)] + [16 + 4 * g4 + i for i in range(4)]
     assert natural != slots
+
+
+@pytest.mark.parametrize("dqk", [512, 256])
+def test_fp8_mfma_k_operand_reads(dqk):
+    lds = stage(dqk, k_swz)
+    for s in range(dqk // 128):
+        for g4 in range(4):
+            for tile in (0, 1):
+                slots = set()
+                for n in range(16):
+                    kb = n * dqk + 128 * (n >> 3) + 16 * ((2 * g4) ^ (n & 7))
+                    p0 = (kb ^ (128 * s)) + 16 * dqk * tile
+                    p1 = ((kb ^ 16) ^ (128 * s)) + 16 * dqk * tile
+                    got = [lds[p0 + e] for e in range(16)] + [lds[p1 + e] for e in range(16)]
+                    assert got == [(16 * tile + n, 128 * s + 32 * g4 + b) for b in range(32)]
+                    slots.add((p0 % 256) // 16)
+                assert len(slots) == 16
