@@ -159,6 +159,13 @@ typedef struct pa_plan {
                                       last segment (the planner sets it when at least a
                                       quarter of the waves have such a segment); a speed
                                       choice only: either value gives the same bits      */
+  int32_t short_tiles;             /* prefill: 1 when tiles too short to give each of the
+                                      eight 16-row waves rows hold at least an eighth of
+                                      the wave-stages (the planner sets it); the run then
+                                      launches the kernel form whose waves without rows
+                                      only copy stages; a speed choice only: either value
+                                      gives the same bits                                */
+  int32_t reserved0;               /* zero                                              */
   int64_t plan_bytes;              /* bytes of the host plan buffer in use              */
   int64_t items_offset;            /* byte offset of the item array in the plan buffer  */
   int64_t merges_offset;           /* byte offset of the merge array in the plan buffer */

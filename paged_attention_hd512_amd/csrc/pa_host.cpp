@@ -588,6 +588,17 @@ pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache
   plan->num_slots = (int32_t)num_slots;
   plan->chunk_blocks = (int32_t)chunk;
   plan->tile_rows = kPrefillTileRows;
+  // Wave-stages of waves left without rows (a tile of rows r holds ceil(r / 16) busy
+  // waves); from an eighth of all wave-stages on, the kernel form that lets such waves
+  // skip the arithmetic is launched.
+  int64_t wave_stages = 0, idle_stages = 0;
+  for (const Tmp& t : items) {
+    const int64_t s = stages_of(t.it);
+    const int64_t busy = (t.it.row_end - t.it.row_begin + kPrefillWaveRows - 1) / kPrefillWaveRows;
+    wave_stages += s * kPrefillWaves;
+    idle_stages += s * (kPrefillWaves - busy);
+  }
+  plan->short_tiles = wave_stages > 0 && 8 * idle_stages >= wave_stages ? 1 : 0;
   plan->total_q = batch > 0 ? qo_indptr_host[batch] : 0;
   plan->max_kv_len = (int32_t)max_len;
   plan->items_offset = 0;

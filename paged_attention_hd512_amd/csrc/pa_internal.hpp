@@ -17,8 +17,10 @@ constexpr int kMaxSplits = 64;
 constexpr int kMaxDecodeGroup = 8;       // query heads per KV head in decode
 constexpr int kMaxPrefillGroup = 16;
 
-// Prefill: query rows per tile ((token, head) pairs of one head group).
+// Prefill: query rows per tile ((token, head) pairs of one head group), 16 per wave.
 constexpr int kPrefillTileRows = 128;
+constexpr int kPrefillWaveRows = 16;
+constexpr int kPrefillWaves = kPrefillTileRows / kPrefillWaveRows;
 constexpr int kPrefillKeyStage = 32;  // keys per LDS stage of the prefill kernel
 // Split-K prefill (a short query over a long KV): when the tiles give fewer than
 // kPrefillSplitItems workgroups (tiles x KV heads), tile key ranges longer than the chunk

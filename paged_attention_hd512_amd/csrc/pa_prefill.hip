@@ -55,7 +55,6 @@
 
 namespace pa {
 
-constexpr int kPrefillWaves = 8;          // 16 query rows each: 128 rows per tile
 constexpr int kKeyStage = kPrefillKeyStage;  // keys per LDS stage
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
@@ -197,7 +196,10 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <int DQK, int DVO, int PM, int KV>
+// SHORT: the form for plans rich in short tiles, whose waves without rows skip the
+// arithmetic (below); kept apart because the branch costs full tiles ~2 % (register
+// assignment and scheduling of the whole kernel shift with it).
+template <int DQK, int DVO, int PM, int KV, bool SHORT>
 __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   constexpr bool FP4 = KV == kKvFp4;
   constexpr bool CONV = FP4;                // stages pass through registers and are converted
@@ -885,6 +887,38 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
       }
     }
   };
+  // SHORT form: a wave whose 16 rows all lie past the tile's end (a tile of a few new
+  // tokens, a request's last tile) computes nothing: it only moves its share of each next
+  // stage and meets the same barriers.
+  auto idle_interval = [&](int st, auto kslot_c) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    constexpr auto other_c = std::integral_constant<int, decltype(kslot_c)::value ^ 1>{};
+    if (st + 1 < st_end) {
+      if constexpr (SPREAD) {
+        if (!second) {
+          copy_prep(st + 1);
+          static_for<2 * NCOPY>([&](auto idx_c) { copy_one(idx_c, other_c, vo_next); });
+        }
+      } else {
+        copy_stage(st + 1, other_c, vo_next);
+        if constexpr (CONV) conv_store(other_c, vo_next);
+      }
+    }
+    const int t = vo_prev;
+    vo_prev = vo_cur;
+    vo_cur = vo_next;
+    vo_next = t;
+  };
+  if constexpr (SHORT) {
+    if (it.row_begin + 16 * w >= it.row_end) {  // wave-uniform
+      for (int st = st_first; st < st_end; st += 2) {
+        idle_interval(st, std::integral_constant<int, 0>{});
+        if (st + 1 < st_end) idle_interval(st + 1, std::integral_constant<int, 1>{});
+      }
+      return;
+    }
+  }
   if (second) run(std::true_type{});
   else run(std::false_type{});
 
@@ -991,16 +1025,22 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeArgs a) 
   if (a.lse && lane == 0) a.lse[q_row] = so > 0.f ? (mo + log2f(so)) * kLn2 : -INFINITY;
 }
 
-template <int DQK, int DVO>
+template <int DQK, int DVO, bool SHORT>
 static void launch_prefill(const PrefillArgs& a, int pm, int kv, int grid, hipStream_t s) {
-  if (kv == kKvFp4) prefill_kernel<DQK, DVO, kPagesAny, kKvFp4><<<grid, 512, 0, s>>>(a);
+  if (kv == kKvFp4) prefill_kernel<DQK, DVO, kPagesAny, kKvFp4, SHORT><<<grid, 512, 0, s>>>(a);
   else if (kv == kKvFp8) {
-    if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvFp8><<<grid, 512, 0, s>>>(a);
-    else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2, kKvFp8><<<grid, 512, 0, s>>>(a);
-    else prefill_kernel<DQK, DVO, kPagesAny, kKvFp8><<<grid, 512, 0, s>>>(a);
-  } else if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvBf16><<<grid, 512, 0, s>>>(a);
-  else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2, kKvBf16><<<grid, 512, 0, s>>>(a);
-  else prefill_kernel<DQK, DVO, kPagesAny, kKvBf16><<<grid, 512, 0, s>>>(a);
+    if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvFp8, SHORT><<<grid, 512, 0, s>>>(a);
+    else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2, kKvFp8, SHORT><<<grid, 512, 0, s>>>(a);
+    else prefill_kernel<DQK, DVO, kPagesAny, kKvFp8, SHORT><<<grid, 512, 0, s>>>(a);
+  } else if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvBf16, SHORT><<<grid, 512, 0, s>>>(a);
+  else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2, kKvBf16, SHORT><<<grid, 512, 0, s>>>(a);
+  else prefill_kernel<DQK, DVO, kPagesAny, kKvBf16, SHORT><<<grid, 512, 0, s>>>(a);
+}
+
+template <int DQK, int DVO>
+static void launch_prefill(const PrefillArgs& a, int pm, int kv, bool short_tiles, int grid, hipStream_t s) {
+  if (short_tiles) launch_prefill<DQK, DVO, true>(a, pm, kv, grid, s);
+  else launch_prefill<DQK, DVO, false>(a, pm, kv, grid, s);
 }
 
 }  // namespace pa
@@ -1070,9 +1110,10 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   const int pm = P % kKeyStage == 0 && page_fits_u32
                      ? kPagesStage
                      : ((P & (P - 1)) == 0 ? kPagesPow2 : kPagesAny);
-  if (dqk == 512 && dvo == 512) launch_prefill<512, 512>(a, pm, kv, grid, s);
-  else if (dqk == 256 && dvo == 256) launch_prefill<256, 256>(a, pm, kv, grid, s);
-  else launch_prefill<512, 256>(a, pm, kv, grid, s);
+  const bool short_tiles = plan->short_tiles != 0;
+  if (dqk == 512 && dvo == 512) launch_prefill<512, 512>(a, pm, kv, short_tiles, grid, s);
+  else if (dqk == 256 && dvo == 256) launch_prefill<256, 256>(a, pm, kv, short_tiles, grid, s);
+  else launch_prefill<512, 256>(a, pm, kv, short_tiles, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
   count_launches(1);

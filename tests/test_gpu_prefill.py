@@ -229,6 +229,29 @@ def test_full_size_extend_prefill_is_split_and_matches():
     assert torch.isfinite(o.float()).all()
 
 
+@pytest.mark.parametrize("kv_dtype,dqk,dvo,page", [
+    ("bf16", 512, 512, 64), ("bf16", 256, 256, 1), ("fp8", 512, 256, 16), ("fp8", 512, 512, 32),
+    ("nvfp4", 512, 256, 16)])
+def test_short_tile_form_equals_the_plain_form(kv_dtype, dqk, dvo, page):
+    """Tiles of 32, 6 and 80 rows (group 2) keep 2, 1 and 5 of the 8 waves busy, so the
+    plan picks the kernel form whose waves without rows only copy stages (short_tiles = 1).
+    The output must match the oracle, and the same plan run by the plain form must give the
+    same bits."""
+    say(f"short-tile form {kv_dtype} dims={dqk}/{dvo} page={page}")
+    c = make_prefill_case([16, 3, 40], [3000, 5000, 700], 8, 4, dqk, page, head_dim_vo=dvo,
+                          kv_dtype=kv_dtype, causal=True, out_dtype="fp32", seed=71,
+                          device=dev())
+    run, o, lse = gpu_prefill(c)
+    assert run.plan.short_tiles == 1
+    ref, ref_lse = oracle_prefill(c)
+    compare(f"short tiles {kv_dtype} {dqk}/{dvo}", out_to_np(o), ref, lse.cpu().numpy(), ref_lse,
+            out_dtype="fp32")
+    run.plan.short_tiles = 0
+    o2, lse2 = run.run(c.q)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
 def test_bf16_output_is_the_rounded_fp32_output():
     say("prefill bf16 output = RNE(fp32 output)")
     c = make_prefill_case([130, 64], [300, 64], 16, 8, 512, 64, seed=6, device=dev())

@@ -191,6 +191,18 @@ PREFILL_CASES = [
 ]
 
 
+def short_tiles_rule(items):
+    """The planner's choice of the prefill kernel form for short tiles: 1 when waves left
+    without rows (a tile of r rows keeps ceil(r / 16) of its 8 waves busy) hold at least an
+    eighth of the wave-stages (32-key stages x 8 waves, summed over the items)."""
+    total = idle = 0
+    for b, r0, r1, k0, k1, slot in items:
+        stages = (k1 + 31) // 32 - k0 // 32 if k1 > k0 else 0
+        total += 8 * stages
+        idle += (8 - (r1 - r0 + 15) // 16) * stages
+    return int(total > 0 and 8 * idle >= total)
+
+
 @pytest.mark.parametrize("qo,kv,group,causal,window", PREFILL_CASES)
 def test_prefill_plan_matches_reference_tiles(qo, kv, group, causal, window):
     P = 16
@@ -210,6 +222,7 @@ def test_prefill_plan_matches_reference_tiles(qo, kv, group, causal, window):
         b = r[0]
         assert (r[5], r[6], r[7]) == (qo_indptr[b], kv[b], qo[b])
     assert plan.total_q == sum(qo)
+    assert plan.short_tiles == short_tiles_rule(ref_items)
     assert plan.num_merges == len(ref_merges)
     assert plan.num_slots == sum(m[5] for m in ref_merges)
     part_rows = plan.num_slots * hkv * plan.tile_rows
@@ -253,6 +266,21 @@ def test_random_plans_match_the_reference(seed):
     items = pa.prefill_items(plan, buf)
     assert [tuple(r[:5]) + (r[8],) for r in items.tolist()] == [tuple(r) for r in ref_items]
     assert [tuple(r) for r in pa.prefill_merges(plan, buf).tolist()] == [tuple(r) for r in ref_pmerges]
+    assert plan.short_tiles == short_tiles_rule(ref_items)
+
+
+def test_short_tile_form_is_chosen_for_tiles_of_few_rows():
+    """16 new tokens x group 2 fill 2 of a tile's 8 waves: the short-tile form; 4096 new
+    tokens fill whole tiles: the plain form."""
+    def plan_of(qo, kv):
+        indptr, last = lens_to_table(kv, 64)
+        qo_indptr = np.zeros(len(qo) + 1, np.int32)
+        qo_indptr[1:] = np.cumsum(qo)
+        cache = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, int(indptr[-1]) + 1, 8, 64, 512)
+        return pa.pa_prefill_plan(params(hq=16), cache, qo_indptr, indptr, last)[0]
+    assert plan_of([16] * 8, [16384] * 8).short_tiles == 1
+    assert plan_of([4096] * 4, [5120] * 4).short_tiles == 0
+    assert plan_of([4096, 16], [5120, 16384]).short_tiles == 0  # 1 % of the wave-stages idle
 
 
 @pytest.mark.parametrize("qo,kv,group,causal,window", PREFILL_CASES)
