@@ -419,9 +419,28 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   };
   // Instruction IDX % NCOPY of the rows of wave w (IDX < NCOPY) or of wave w + NW/2 (the
   // wave sharing this SIMD, IDX >= NCOPY).
+  const uint32_t lane16 = 16u * (uint32_t)lane;
   auto copy_one = [&](auto idx_c, auto slot_c, int vo) {
     constexpr int IDX = decltype(idx_c)::value % NCOPY;
     const int my_row = RPW * w + (decltype(idx_c)::value / NCOPY) * RPW * (NW / 2);
+    // One row per instruction: the row is wave-uniform, so its offset goes in the scalar
+    // operand and the lane's chunk is 16 lane ^ 16 swizzle (the empty asm hides the swizzle
+    // from loop-invariant hoisting, which would hold one register per instruction).
+    constexpr bool ONE_ROW = IDX < NKC ? KRPI == 1 : VRPI == 1;
+    if constexpr (ONE_ROW) {
+      constexpr int i = IDX < NKC ? IDX : IDX - NKC;
+      const int row = my_row + i;
+      uint32_t sw = 16u * (uint32_t)(IDX < NKC ? k_swz(row) : vswz(row));
+      asm volatile("" : "+s"(sw));
+      const uint32_t soff = (uint32_t)min(row, c_last_row) * (uint32_t)(IDX < NKC ? a.k_st : a.v_st);
+      if constexpr (IDX < NKC)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c_kr,
+            (__attribute__((address_space(3))) void*)(k_buf(slot_c) + row * DQK), 16, lane16 ^ sw, soff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c_vr,
+            (__attribute__((address_space(3))) void*)(v_lds + vo + row * DVO), 16, lane16 ^ sw, soff, 0, 0);
+      return;
+    }
     // The lane terms are rebuilt from one register each time (the empty asm hides the value
     // from loop-invariant hoisting, which would hold one register per instruction).
     int ln = lane;
@@ -670,10 +689,12 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     // nothing else does), plus 128*(j >> 2).
     int kb = n * DQK + 8 * (g4 ^ (n & 3)) + 32 * (n >> 2);
     asm volatile("" : "+v"(kb));
+    // Tile 1's row is read first: the wait for tile 0's read then covers both, so the two
+    // MFMAs of a step follow one wait.
     auto ld = [&](int j, u32x4_t& k0, u32x4_t& k1) {
       const st_t* src = kt + ((kb ^ (32 * (j & 3))) + 128 * (j >> 2));
-      k0 = *(const u32x4_t*)src;
       k1 = *(const u32x4_t*)(src + 16 * DQK);
+      k0 = *(const u32x4_t*)src;
     };
     u32x4_t kr0[KD + 1], kr1[KD + 1];
 #pragma unroll
