@@ -828,8 +828,11 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     static_for<OT>([&](auto t_c) {
       constexpr int t = decltype(t_c)::value;
       constexpr int r = t % (VD + 1);
+      // Wait for tile t's reads before issuing tile t + VD's: those reads then separate the
+      // wait (which the compiler takes as writing the operand registers) from the MFMA, in
+      // place of a wait state.
+      lds_wait<2 * (t + VD - 1 < OT ? VD - 1 : OT - 1 - t)>(vlo[r], vhi[r]);
       if constexpr (t + VD < OT) ld(std::integral_constant<int, t + VD>{});
-      lds_wait<2 * (t + VD < OT ? VD : OT - 1 - t)>(vlo[r], vhi[r]);
       const u32x4_t vf = {vlo[r][0], vlo[r][1], vhi[r][0], vhi[r][1]};
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf), pb, o[t], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
