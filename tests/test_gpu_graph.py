@@ -71,7 +71,7 @@ def test_decode_step_replays_from_a_graph(lens, splits, parked):
     replay_and_check(name, g, q, new_qs, lambda x: run.run(x), out_g, lse_g)
 
 
-@pytest.mark.parametrize("qo,kv", [([130, 64], [300, 64]), ([3, 16], [3000, 5000])])
+@pytest.mark.parametrize("qo,kv", [([128, 64], [300, 64]), ([3, 16], [3000, 5000])])
 def test_prefill_replays_from_a_graph(qo, kv):
     name = f"graph prefill qo={qo} kv={kv}"
     say(name)
@@ -90,3 +90,5 @@ def test_prefill_replays_from_a_graph(qo, kv):
     replay_and_check(name, g, q, new_qs, lambda x: run.run(x), out_g, lse_g)
     if kv[0] > 1000:
         assert run.plan.num_merges > 0  # the split-K path (two kernels) is the one captured
+    # Whole tiles run the plain kernel form, tiles of a few rows the short-tile form.
+    assert run.plan.short_tiles == (1 if qo[0] < 16 else 0)
