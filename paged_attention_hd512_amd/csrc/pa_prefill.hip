@@ -470,6 +470,28 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int KC = DQK / 128, VC = DVO / 128;  // chunks per lane and row
   // Byte address of row t's K and V rows (and block-scale rows) in the pages.
   auto conv_rows = [&](int st, const char*& kd, const char*& vd, const char*& ks, const char*& vs) {
+    if constexpr (PM == kPagesStage) {
+      // The stage lies in one page: one lookup, tracked in stage order like the copies'
+      // (stages are loaded in order), and rows at fixed strides.  Rows at or past the
+      // request's length re-read its last key (same page; masked out).
+      const int jj = min(nxt_j, last_j);
+      if (jj - pwin_base >= 64) {
+        pwin_base = jj;
+        pwin = pages[min(pwin_base + lane, last_j)];
+      }
+      const int64_t pg = __builtin_amdgcn_readlane(pwin, jj - pwin_base);
+      const int row = min(my_row + (lane >> 4), max(it.kv_len - 1 - st * KS, 0));
+      const int64_t sl = (int64_t)nxt_r * KS + row;
+      kd = a.k + pg * a.k_sp + (int64_t)kvh * a.k_sh + sl * a.k_st;
+      vd = a.v + pg * a.v_sp + (int64_t)kvh * a.v_sh + sl * a.v_st;
+      ks = a.k_sf + pg * a.ks_sp + (int64_t)kvh * a.ks_sh + sl * a.ks_st;
+      vs = a.v_sf + pg * a.vs_sp + (int64_t)kvh * a.vs_sh + sl * a.vs_st;
+      if (++nxt_r == stages_per_page) {
+        nxt_r = 0;
+        ++nxt_j;
+      }
+      return;
+    }
     int t = st * KS + my_row + (lane >> 4);
     t = t < kv_lo ? kv_lo : (t >= kv_hi ? kv_hi - 1 : t);
     const int j = t / a.page_size;
@@ -1051,8 +1073,10 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeArgs a) 
 
 template <int DQK, int DVO, bool SHORT>
 static void launch_prefill(const PrefillArgs& a, int pm, int kv, int grid, hipStream_t s) {
-  if (kv == kKvFp4) prefill_kernel<DQK, DVO, kPagesAny, kKvFp4, SHORT><<<grid, 512, 0, s>>>(a);
-  else if (kv == kKvFp8) {
+  if (kv == kKvFp4) {
+    if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvFp4, SHORT><<<grid, 512, 0, s>>>(a);
+    else prefill_kernel<DQK, DVO, kPagesAny, kKvFp4, SHORT><<<grid, 512, 0, s>>>(a);
+  } else if (kv == kKvFp8) {
     if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvFp8, SHORT><<<grid, 512, 0, s>>>(a);
     else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2, kKvFp8, SHORT><<<grid, 512, 0, s>>>(a);
     else prefill_kernel<DQK, DVO, kPagesAny, kKvFp8, SHORT><<<grid, 512, 0, s>>>(a);
