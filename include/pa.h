@@ -165,7 +165,11 @@ typedef struct pa_plan {
                                       launches the kernel form whose waves without rows
                                       only copy stages; a speed choice only: either value
                                       gives the same bits                                */
-  int32_t reserved0;               /* zero                                              */
+  int32_t grouped_partials;        /* decode: 1 when the split results of neighbouring
+                                      waves of one workgroup that belong to one (request,
+                                      kv head) are combined in LDS into one slot (the
+                                      planner sets it where the kernel can hold a split
+                                      result per wave in LDS); changes rounding order only */
   int64_t plan_bytes;              /* bytes of the host plan buffer in use              */
   int64_t items_offset;            /* byte offset of the item array in the plan buffer  */
   int64_t merges_offset;           /* byte offset of the merge array in the plan buffer */

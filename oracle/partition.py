@@ -24,11 +24,16 @@ Decode rule (units of 16-token logical blocks, block j = tokens [16j, 16j+16)):
 * A piece is cut at (b, h) boundaries and at chunk boundaries into segments, so every
   chunk is computed by one or more whole segments; blocks [j0, j1) of (b, h) cover the
   keys [max(s_b, 16 (fb + j0)), min(L_b, 16 (fb + j1))).
-* A (b, h) with several segments owns that many consecutive workspace slots, in segment
-  order, slots numbered in (b, h) order, and gets a merge entry (b, h, first slot, count);
-  a (b, h) with one segment writes its output directly (slot -1); an empty request gets a
-  merge entry with no slots for each h (zero output, lse -inf).
-* Waves run by piece length descending, ties in piece order.
+* Waves run by piece length descending, ties in piece order; consecutive runs of
+  WAVES_PER_GROUP waves form workgroups.
+* Grouping (when the kernel holds split results in LDS): the last segments of a run of two
+  or more consecutive waves of one workgroup that belong to one (b, h) with several
+  segments form a group, whose results are combined into one slot.
+* A (b, h) with several segments owns one consecutive workspace slot per segment (one per
+  group for grouped segments), in piece order, slots numbered in (b, h) order, and gets a
+  merge entry (b, h, first slot, count); a (b, h) with one segment writes its output
+  directly (slot -1); an empty request gets a merge entry with no slots for each h (zero
+  output, lse -inf).
 
 Prefill rule: the query rows of one (request, KV head) are the q_len * G pairs
 (token i, head g) flattened as i * G + g; tiles of ``tile_rows`` consecutive rows;
@@ -47,6 +52,7 @@ order.
 
 BLOCK_TOKENS = 16
 WAVE_SLOTS = 2048
+WAVES_PER_GROUP = 8
 MIN_PIECE_BLOCKS = 8
 MAX_SPLITS = 64
 PREFILL_STAGE = 32
@@ -58,12 +64,14 @@ def _ceil_div(a, b):
     return -(-a // b)
 
 
-def decode_partition_ref(kv_lens, window, num_splits, num_kv_heads):
-    """Returns (waves, merges).
+def decode_partition_ref(kv_lens, window, num_splits, num_kv_heads, group_last=False):
+    """Returns (waves, merges, groups).
 
     waves:  in launch order, each a list of segments (b, h, t_begin, t_end, slot).
     merges: (b, h, slot_begin, num_slots) for every (request, KV head) that has several
             segments or no keys at all, in (b, h) order.
+    groups: per wave in launch order, (size, first wave of the group within its
+            workgroup) when its last segment is grouped, else (0, 0).
     """
     lens = [int(x) for x in kv_lens]
     starts, nblk = [], []
@@ -115,6 +123,36 @@ def decode_partition_ref(kv_lens, window, num_splits, num_kv_heads):
     for segs in piece_segs:
         for sg in segs:
             count[(sg[0], sg[1])] = count.get((sg[0], sg[1]), 0) + 1
+    order = sorted(range(len(pieces)), key=lambda k: (-(pieces[k][1] - pieces[k][0]), k))
+
+    # Groups: runs of consecutive waves (launch order) inside one workgroup whose last
+    # segments belong to the same split (b, h).
+    lead, gsize, gpos = {}, {}, {}
+    if group_last:
+        last_key = [tuple(piece_segs[k][-1][:2]) for k in order]
+        s = 0
+        while s < len(order):
+            e = s + 1
+            if count[last_key[s]] > 1:
+                while (e < len(order) and e // WAVES_PER_GROUP == s // WAVES_PER_GROUP
+                       and last_key[e] == last_key[s]):
+                    e += 1
+            if e - s >= 2:
+                for t in range(s, e):
+                    lead[order[t]] = order[s]
+                    gsize[order[t]] = e - s
+                    gpos[order[t]] = s % WAVES_PER_GROUP
+            s = e
+
+    def grouped(k, j):
+        return j == len(piece_segs[k]) - 1 and k in lead
+
+    units = {}
+    for k, segs in enumerate(piece_segs):
+        for j, sg in enumerate(segs):
+            key = (sg[0], sg[1])
+            if count[key] > 1 and (not grouped(k, j) or lead[k] == k):
+                units[key] = units.get(key, 0) + 1
     first_slot, merges, next_slot = {}, [], 0
     for b, h in pairs:
         k = count.get((b, h), 0)
@@ -122,19 +160,25 @@ def decode_partition_ref(kv_lens, window, num_splits, num_kv_heads):
             merges.append((b, h, next_slot, 0))
         elif k > 1:
             first_slot[(b, h)] = next_slot
-            merges.append((b, h, next_slot, k))
-            next_slot += k
-    used = {}
-    for segs in piece_segs:
-        for sg in segs:
+            merges.append((b, h, next_slot, units[(b, h)]))
+            next_slot += units[(b, h)]
+    used, group_slot = {}, {}
+    for k, segs in enumerate(piece_segs):
+        for j, sg in enumerate(segs):
             key = (sg[0], sg[1])
-            if key in first_slot:
-                sg[4] = first_slot[key] + used.get(key, 0)
-                used[key] = used.get(key, 0) + 1
+            if key not in first_slot:
+                continue
+            if grouped(k, j) and lead[k] in group_slot:
+                sg[4] = group_slot[lead[k]]
+                continue
+            sg[4] = first_slot[key] + used.get(key, 0)
+            used[key] = used.get(key, 0) + 1
+            if grouped(k, j):
+                group_slot[lead[k]] = sg[4]
 
-    order = sorted(range(len(pieces)), key=lambda k: (-(pieces[k][1] - pieces[k][0]), k))
     waves = [[tuple(sg) for sg in piece_segs[k]] for k in order]
-    return waves, merges
+    groups = [(gsize[k], gpos[k]) if k in lead else (0, 0) for k in order]
+    return waves, merges, groups
 
 
 def prefill_plan_ref(qo_lens, kv_lens, group, tile_rows, causal, window, num_kv_heads):

@@ -73,6 +73,7 @@ struct DecodeArgs {
   const DecodeSegment* segs;   // head segment of wave w at index w, then further segments
   int32_t num_waves;
   int32_t park;                // the plan's deferred_partials
+  int32_t group_last;          // the plan's grouped_partials
   void* out;                   // [B, Hq, DVO] fp32 or bf16
   float* lse;                  // [B, Hq] or null
   float* part_o;               // [slots, G, DVO] fp32
@@ -96,8 +97,6 @@ __device__ __forceinline__ int q_dim_of_step(int j, int g4) {
   else return (DQK / 4) * g4 + 8 * j;
 }
 
-constexpr int kDecodeWavesPerGroup = 8;  // the two waves of every SIMD of a CU
-constexpr int kLdsBytesPerCu = 160 * 1024;  // gfx950: LDS of one CU, all of it one workgroup's
 
 // Eight waves per workgroup, one workgroup per CU: each wave runs its own piece (its
 // segments one after the other) and never waits for the others.  They share LDS only to
@@ -129,19 +128,20 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
   // one in-order completion counter, so partial-result stores issued between segments made
   // the next segment's first loads wait for them under the full read load.  Parking needs
   // G x DVO floats per wave; where LDS is short, the P buffer keeps only the columns the
-  // P V step reads, and instances that still do not fit store at once.
+  // P V step reads, and instances that still do not fit store at once.  The same buffers
+  // combine grouped last segments: consecutive waves of the workgroup whose last segments
+  // belong to one split (request, KV head) each leave their result in LDS, and the last of
+  // them to finish merges the group (in wave order) into one workspace slot.
   constexpr int PARK = GMAX * DVO + GMAX;         // floats: the outputs, then the log-sum-exps
-  constexpr auto lds_bytes = [](int pc) {
-    return NWG * (GMAX * QPITCH * 2 + 2 * 16 * pc * 4 + 2 * 16 * 4 + 4 + PARK * 4) + 1024;
-  };
-  constexpr int PC_NARROW = KV == kKvFp4 ? 8 : GMAX;
-  constexpr int PC = lds_bytes(16) <= kLdsBytesPerCu ? 16 : PC_NARROW;  // P columns kept
-  constexpr bool DEFER = lds_bytes(PC) <= kLdsBytesPerCu;
+  constexpr int PC = decode_p_columns(DQK, DVO, GMAX, KV == kKvFp4);  // P columns kept
+  constexpr bool DEFER = decode_parks(DQK, DVO, GMAX, KV == kKvFp4);
+  static_assert(QPITCH == DQK + 8, "the LDS budget assumes this Q pitch");
 
   __shared__ __attribute__((aligned(16))) uint16_t q_all[NWG][GMAX * QPITCH];
   __shared__ __attribute__((aligned(16))) float p_all[NWG][2][16][PC];  // P V runs one block behind
   __shared__ __attribute__((aligned(16))) float alpha_all[NWG][2][16];
   __shared__ __attribute__((aligned(16))) int progress[NWG];
+  __shared__ __attribute__((aligned(16))) int grp_arrived[NWG];  // per group, at its first wave
   __shared__ __attribute__((aligned(16))) float park_all[DEFER ? NWG : 1][DEFER ? PARK : 4];
 
   const int lane = threadIdx.x & 63;
@@ -154,14 +154,83 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
   float (*p_lds)[16][PC] = p_all[wv];
   float* park = park_all[DEFER ? wv : 0];
   int parked_slot = -1;  // partial slot whose result waits in `park`
+  // Writes the parked result to its workspace slot (the rows of heads 0 .. G-1 are
+  // contiguous in both).
+  auto flush_park = [&](int slot) {
+    wave_lds_sync();
+    float* dst = a.part_o + (int64_t)slot * G * DVO;
+    for (int i = 4 * lane; i < G * DVO; i += 256) *(f32x4_t*)(dst + i) = *(const f32x4_t*)(park + i);
+    if (lane < G) a.part_lse[(int64_t)slot * G + lane] = park[GMAX * DVO + lane];
+  };
+  // This wave's grouped result is in `park`: count it in, and if it is the group's last,
+  // merge the members' results (waves first .. first + cnt - 1, in that order, whoever
+  // finishes last) by the log-sum-exp rule into the group's slot.
+  auto group_merge = [&](int slot, int cnt, int first) {
+    wave_lds_sync();  // every lane's share of the result is in LDS before the count
+    int before = 0;
+    if (lane == 0)
+      before = __hip_atomic_fetch_add(&grp_arrived[first], 1, __ATOMIC_ACQ_REL,
+                                      __HIP_MEMORY_SCOPE_WORKGROUP);
+    before = __builtin_amdgcn_readfirstlane(before);
+    if (before != cnt - 1) return;
+    wave_lds_sync();
+    // Weights: lane 8 h + j takes member j's log-sum-exp of head h; the eight lanes of a
+    // head reduce their max and sum, and each keeps its member's normalised weight.
+    static_assert(GMAX * NWG <= 64, "one lane per (head, member)");
+    const int wh = lane >> 3, wj = lane & 7;
+    const bool wlive = wh < G && wj < cnt;
+    const float l = wlive ? park_all[DEFER ? first + wj : 0][GMAX * DVO + wh] : -INFINITY;
+    float mx = l;
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    mx = fmaxf(mx, __shfl_xor(mx, 4));
+    float w = wlive ? exp2f(l - mx) : 0.f;
+    float wsum = w;
+    wsum += __shfl_xor(wsum, 1);
+    wsum += __shfl_xor(wsum, 2);
+    wsum += __shfl_xor(wsum, 4);
+    if (wj == 0 && wh < G) a.part_lse[(int64_t)slot * G + wh] = mx + log2f(wsum);
+    w = wlive ? w / wsum : 0.f;
+    // Outputs: 256 floats per pass, all of one head (DVO is a multiple of 256); every
+    // member's four floats are read before any is used, members past the group's size
+    // repeating the last one with weight 0.
+    float* dst = a.part_o + (int64_t)slot * G * DVO;
+#pragma unroll
+    for (int it = 0; it < GMAX * DVO / 256; ++it) {
+      if (256 * it >= G * DVO) break;
+      const int i = 256 * it + 4 * lane;
+      const int h = 256 * it / DVO;
+      f32x4_t v[NWG];
+#pragma unroll
+      for (int j = 0; j < NWG; ++j)
+        v[j] = *(const f32x4_t*)(park_all[DEFER ? first + (j < cnt ? j : cnt - 1) : 0] + i);
+      f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NWG; ++j) {
+        const float wj_s = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), 8 * h + j));
+        o[0] += wj_s * v[j][0];
+        o[1] += wj_s * v[j][1];
+        o[2] += wj_s * v[j][2];
+        o[3] += wj_s * v[j][3];
+      }
+      *(f32x4_t*)(dst + i) = o;
+    }
+  };
   float (*alpha_lds)[16] = alpha_all[wv];
   const int wave = blockIdx.x * NWG + wv;
   // The wave's head segment names its further segments; each next record is requested when
   // the previous segment starts (a clamped index rather than a branch around the load).
   const bool active = wave < a.num_waves;
   const DecodeSegment head = a.segs[active ? wave : 0];
-  const int n_seg = active ? 1 + head.more_count : 0;
+  const int n_seg = active ? 1 + (head.more_count & 0xFFFF) : 0;
   if (lane == 0) progress[wv] = 0;
+  if constexpr (DEFER) {
+    if (a.group_last) {  // uniform: every wave reaches this barrier
+      if (lane == 0) grp_arrived[wv] = 0;
+      lds_barrier();
+    }
+  }
   int done = 0;  // blocks this wave has finished
 
   u32x4_t kbuf[NKL];
@@ -482,7 +551,18 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
         for (int e = 0; e < 8; ++e) acc[h][e] += shfl_xor_f(acc[h][e], 32);
     }
     const int h0 = sg.kvh * G;
-    const bool to_park = DEFER && a.park && sg.slot >= 0 && k + 1 < n_seg && parked_slot < 0;
+    // The last segment carries its group: bits 16-23 of more_count its size (0: none),
+    // bits 24-31 its first wave within the workgroup.
+    const int grp_n = (sg.more_count >> 16) & 0xFF;
+    const bool to_group = DEFER && k + 1 == n_seg && grp_n >= 2;
+    if constexpr (DEFER) {
+      if (to_group && parked_slot >= 0) {  // the buffer takes this result: write out the last
+        flush_park(parked_slot);
+        parked_slot = -1;
+      }
+    }
+    const bool to_park =
+        DEFER && sg.slot >= 0 && (to_group || (a.park && k + 1 < n_seg && parked_slot < 0));
     if constexpr (KV == kKvFp4) {
       // Lane (g4, n): head n & 7 at the 4 TPD columns from DVO/2 (n >> 3) + 4 TPD g4.
       const int h = n & 7;
@@ -560,16 +640,14 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
       else if (sg.slot >= 0) a.part_lse[(int64_t)sg.slot * G + lane] = lg;
       else if (a.lse) a.lse[(int64_t)sg.b * a.num_qo_heads + h0 + lane] = lg * kLn2;
     }
-    if (to_park) parked_slot = sg.slot;
+    if (to_group) {
+      if constexpr (DEFER) group_merge(sg.slot, grp_n, (uint32_t)sg.more_count >> 24);
+    } else if (to_park) {
+      parked_slot = sg.slot;
+    }
   }
   if constexpr (DEFER) {
-    if (parked_slot >= 0) {
-      // The parked rows of heads 0 .. G-1 are contiguous, as in the workspace slot.
-      wave_lds_sync();
-      float* dst = a.part_o + (int64_t)parked_slot * G * DVO;
-      for (int i = 4 * lane; i < G * DVO; i += 256) *(f32x4_t*)(dst + i) = *(const f32x4_t*)(park + i);
-      if (lane < G) a.part_lse[(int64_t)parked_slot * G + lane] = park[GMAX * DVO + lane];
-    }
+    if (parked_slot >= 0) flush_park(parked_slot);
   }
 }
 
@@ -855,7 +933,7 @@ static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_
   if (st != PA_OK || nothing) return st;
 
   const int group = params->num_qo_heads / cache->num_kv_heads;
-  const int gmax = group <= 4 ? group : group <= 6 ? 6 : 8;
+  const int gmax = decode_gmax(group);
   char* ws = (char*)workspace;
   hipStream_t s = (hipStream_t)stream;
   const bool out_fp32 = params->out_dtype == PA_DTYPE_FP32;
@@ -877,6 +955,7 @@ static pa_status decode_enqueue(const pa_plan* plan, const void* q, const pa_kv_
     a.segs = (const DecodeSegment*)(ws + plan->items_offset);
     a.num_waves = plan->num_workers;
     a.park = plan->deferred_partials;
+    a.group_last = plan->grouped_partials;
     a.out = out;
     a.lse = lse;
     a.part_o = part_o;

@@ -407,7 +407,51 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
       u = e;
     }
   }
-  // Slots, numbered in (b, h) order; merge entries for split and for empty pairs.
+  // Launch order: longest piece first, ties in piece order.
+  std::vector<int32_t> order(pieces.size());
+  for (size_t k = 0; k < order.size(); ++k) order[k] = (int32_t)k;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    return pieces[x].second - pieces[x].first > pieces[y].second - pieces[y].first;
+  });
+  // Grouped split results: where the kernel holds split results in LDS, the last segments
+  // of consecutive waves of one workgroup (launch order, kDecodeWavesPerGroup waves each)
+  // that belong to one split (b, h) form a group; the last of its waves to finish combines
+  // the group's results and writes one partial.  grp_lead[k] is the group's first piece in
+  // launch order (-1: piece k's last segment is in no group).
+  const bool group_last = decode_parks(cache->head_dim_qk, cache->head_dim_vo,
+                                       decode_gmax(params->num_qo_heads / hkv),
+                                       cache->kv_dtype == PA_DTYPE_NVFP4);
+  std::vector<int32_t> grp_lead(pieces.size(), -1), grp_pos(pieces.size(), 0), grp_size(pieces.size(), 0);
+  if (group_last) {
+    const size_t np = order.size();
+    auto last_pair = [&](size_t s) {
+      const DecodeSegment& L = piece_segs[order[s]].back();
+      return (int64_t)L.b * hkv + L.kvh;
+    };
+    for (size_t s = 0; s < np;) {
+      const int64_t i = last_pair(s);
+      size_t e = s + 1;
+      if (seg_count[i] > 1)
+        while (e < np && e / kDecodeWavesPerGroup == s / kDecodeWavesPerGroup && last_pair(e) == i) ++e;
+      if (e - s >= 2)
+        for (size_t t = s; t < e; ++t) {
+          grp_lead[order[t]] = order[s];
+          grp_pos[order[t]] = (int32_t)(s % kDecodeWavesPerGroup);
+          grp_size[order[t]] = (int32_t)(e - s);
+        }
+      s = e;
+    }
+  }
+  // Slots, numbered in (b, h) order; within a (b, h), one per segment (one per group for
+  // grouped segments), in piece order.  Merge entries for split and for empty pairs.
+  std::vector<int32_t> units(npairs, 0);
+  for (size_t k = 0; k < piece_segs.size(); ++k)
+    for (size_t j = 0; j < piece_segs[k].size(); ++j) {
+      const DecodeSegment& sg = piece_segs[k][j];
+      const int64_t i = (int64_t)sg.b * hkv + sg.kvh;
+      const bool grouped = j + 1 == piece_segs[k].size() && grp_lead[k] >= 0;
+      if (seg_count[i] > 1 && (!grouped || grp_lead[k] == (int32_t)k)) ++units[i];
+    }
   std::vector<int32_t> first_slot(npairs, -1);
   std::vector<MergeItem> merges;
   int32_t next_slot = 0;
@@ -417,22 +461,24 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
       merges.push_back(MergeItem{b, h, next_slot, 0});
     } else if (seg_count[i] > 1) {
       first_slot[i] = next_slot;
-      merges.push_back(MergeItem{b, h, next_slot, seg_count[i]});
-      next_slot += seg_count[i];
+      merges.push_back(MergeItem{b, h, next_slot, units[i]});
+      next_slot += units[i];
     }
   }
-  std::vector<int32_t> used(npairs, 0);
-  for (auto& segs : piece_segs)
-    for (auto& sg : segs) {
+  std::vector<int32_t> used(npairs, 0), grp_slot(pieces.size(), -1);
+  for (size_t k = 0; k < piece_segs.size(); ++k)
+    for (size_t j = 0; j < piece_segs[k].size(); ++j) {
+      DecodeSegment& sg = piece_segs[k][j];
       const int64_t i = (int64_t)sg.b * hkv + sg.kvh;
-      if (first_slot[i] >= 0) sg.slot = first_slot[i] + used[i]++;
+      if (first_slot[i] < 0) continue;
+      if (j + 1 == piece_segs[k].size() && grp_lead[k] >= 0) {
+        int32_t& gs = grp_slot[grp_lead[k]];
+        if (gs < 0) gs = first_slot[i] + used[i]++;
+        sg.slot = gs;
+      } else {
+        sg.slot = first_slot[i] + used[i]++;
+      }
     }
-  // Launch order: longest piece first, ties in piece order.
-  std::vector<int32_t> order(pieces.size());
-  for (size_t k = 0; k < order.size(); ++k) order[k] = (int32_t)k;
-  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
-    return pieces[x].second - pieces[x].first > pieces[y].second - pieces[y].first;
-  });
   int64_t num_segs = 0;
   for (auto& segs : piece_segs) num_segs += (int64_t)segs.size();
 
@@ -457,6 +503,7 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
     mid_partials += any ? 1 : 0;
   }
   plan->deferred_partials = 4 * mid_partials >= (int64_t)pieces.size() && !pieces.empty() ? 1 : 0;
+  plan->grouped_partials = group_last ? 1 : 0;
   // Segments: the head segment of every wave (in launch order), then the further segments
   // of the waves that have several (workers_offset), wave after wave.
   plan->items_offset = 0;
@@ -478,12 +525,21 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
   DecodeSegment* out_segs = (DecodeSegment*)(buf + plan->items_offset);
   int32_t more = (int32_t)order.size();  // next free index after the head segments
   for (size_t w = 0; w < order.size(); ++w) {
-    const std::vector<DecodeSegment>& segs = piece_segs[order[w]];
+    const int32_t k0 = order[w];
+    const std::vector<DecodeSegment>& segs = piece_segs[k0];
+    // The wave's last segment carries its group (more_count bits 16-23: size, 24-31: the
+    // group's first wave within the workgroup).
+    const int32_t gbits = grp_lead[k0] >= 0 ? (grp_size[k0] << 16) | (grp_pos[k0] << 24) : 0;
     DecodeSegment head = segs[0];
     head.more_begin = more;
     head.more_count = (int32_t)segs.size() - 1;
+    if (segs.size() == 1) head.more_count |= gbits;
     out_segs[w] = head;
-    for (size_t k = 1; k < segs.size(); ++k) out_segs[more++] = segs[k];
+    for (size_t k = 1; k < segs.size(); ++k) {
+      DecodeSegment sg = segs[k];
+      if (k + 1 == segs.size()) sg.more_count |= gbits;
+      out_segs[more++] = sg;
+    }
   }
   if (!merges.empty())
     memcpy(buf + plan->merges_offset, merges.data(), merges.size() * sizeof(MergeItem));

@@ -15,6 +15,28 @@ constexpr int kDecodeWaveSlots = 2048;   // 256 CUs x 4 SIMDs x 2 waves (registe
 constexpr int kMinPieceBlocks = 8;       // balanced pieces hold at least this many blocks
 constexpr int kMaxSplits = 64;
 constexpr int kMaxDecodeGroup = 8;       // query heads per KV head in decode
+constexpr int kDecodeWavesPerGroup = 8;  // waves per workgroup: the two of every SIMD of a CU
+constexpr int kLdsBytesPerCu = 160 * 1024;  // gfx950: LDS of one CU, all of it one workgroup's
+
+// LDS of a decode workgroup (bytes) when its waves keep P buffers of pc columns: per wave
+// the group's Q rows (padded pitch), two P and two alpha buffers, its progress word and
+// group counter, and a parked split result (G x Dvo outputs and G log-sum-exps); plus a
+// margin.  The kernel sizes its buffers with it and the planner decides from it whether
+// the kernel can hold split results in LDS.
+constexpr int decode_lds_bytes(int dqk, int dvo, int gmax, int pc) {
+  return kDecodeWavesPerGroup * (gmax * (dqk + 8) * 2 + 2 * 16 * pc * 4 + 2 * 16 * 4 + 8 +
+                                 (gmax * dvo + gmax) * 4) + 1024;
+}
+// P columns kept: all 16 when they fit, else only those the P V step reads.
+constexpr int decode_p_columns(int dqk, int dvo, int gmax, bool fp4) {
+  return decode_lds_bytes(dqk, dvo, gmax, 16) <= kLdsBytesPerCu ? 16 : (fp4 ? 8 : gmax);
+}
+// Whether the decode kernel has an LDS slot per wave for one split result.
+constexpr bool decode_parks(int dqk, int dvo, int gmax, bool fp4) {
+  return decode_lds_bytes(dqk, dvo, gmax, decode_p_columns(dqk, dvo, gmax, fp4)) <= kLdsBytesPerCu;
+}
+// Query heads the decode kernel computes for a group of `group` (its instantiations).
+constexpr int decode_gmax(int group) { return group <= 4 ? group : group <= 6 ? 6 : 8; }
 constexpr int kMaxPrefillGroup = 16;
 
 // Prefill: query rows per tile ((token, head) pairs of one head group), 16 per wave.

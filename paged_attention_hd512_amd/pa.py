@@ -69,7 +69,7 @@ class pa_plan(Structure):
                 ("num_splits", c_int32), ("tile_rows", c_int32), ("total_q", c_int32),
                 ("max_kv_len", c_int32), ("num_workers", c_int32),
                 ("deferred_partials", c_int32), ("short_tiles", c_int32),
-                ("reserved0", c_int32), ("plan_bytes", c_int64),
+                ("grouped_partials", c_int32), ("plan_bytes", c_int64),
                 ("items_offset", c_int64), ("merges_offset", c_int64),
                 ("workers_offset", c_int64),
                 ("partial_o_offset", c_int64), ("partial_lse_offset", c_int64),
@@ -437,7 +437,10 @@ class PagedPrefill:
 def decode_segments(plan, plan_buf):
     """Raw segment records of a decode plan as a [num_items, 8] int32 array (b, kv_head,
     t_begin, t_end, slot, page_base, more_begin, more_count): the head segment of each wave
-    in launch order, then the waves' further segments."""
+    in launch order, then the waves' further segments.  Bits 0-15 of a head's more_count
+    count the wave's further segments; bits 16-23 of a wave's last segment give the size of
+    its group of combined results (0: none) and bits 24-31 the group's first wave within
+    the workgroup."""
     off = plan.items_offset
     return plan_buf[off:off + 32 * plan.num_items].view(np.int32).reshape(-1, 8)
 
@@ -448,10 +451,23 @@ def decode_waves(plan, plan_buf):
     segs = decode_segments(plan, plan_buf)
     waves = []
     for w in range(plan.num_workers):
-        more_begin, more_count = int(segs[w, 6]), int(segs[w, 7])
+        more_begin, more_count = int(segs[w, 6]), int(segs[w, 7]) & 0xFFFF
         rows = [segs[w]] + [segs[more_begin + k] for k in range(more_count)]
         waves.append(np.stack(rows)[:, :5])
     return waves
+
+
+def decode_groups(plan, plan_buf):
+    """Per wave in launch order, (size, first wave within the workgroup) of the group whose
+    results its last segment joins, or (0, 0)."""
+    segs = decode_segments(plan, plan_buf)
+    out = []
+    for w in range(plan.num_workers):
+        n_more = int(segs[w, 7]) & 0xFFFF
+        last = segs[w] if n_more == 0 else segs[int(segs[w, 6]) + n_more - 1]
+        bits = int(last[7]) & 0xFFFFFFFF
+        out.append(((bits >> 16) & 0xFF, bits >> 24))
+    return out
 
 
 def decode_merges(plan, plan_buf):

@@ -177,11 +177,13 @@ def test_merges_of_more_than_64_segments():
     """Long requests cut into well over 64 balanced segments (129, 130 and 71 with the
     current planner): the merge reads the segments' log-sum-exps 64 at a time and their rows
     8 at a time, so these counts take every path (whole chunks of 64, a partial chunk, a
-    tail shorter than 8 rows)."""
+    tail shorter than 8 rows).  Eight query heads per KV head at 512/512 leave no LDS for
+    grouped results, so every segment keeps a slot of its own."""
     say("merges of more than 64 segments")
-    c = make_decode_case([16464, 9000], 12, 2, 512, 16, num_splits=0, out_dtype="fp32",
+    c = make_decode_case([16464, 9000], 16, 2, 512, 16, num_splits=0, out_dtype="fp32",
                          seed=21, device=dev())
     runner, o, lse = gpu_decode(c)
+    assert runner.plan.grouped_partials == 0
     counts = pa.decode_merges(runner.plan, runner.plan_buf)[:, 3].tolist()
     assert max(counts) > 128 and any(64 < x < 128 for x in counts)
     assert any(x % 8 for x in counts)
@@ -243,6 +245,39 @@ def test_split_results_parked_in_lds_equal_results_stored_at_once(kv_dtype, hq, 
     ref, ref_lse = oracle_decode(c)
     compare(f"parked {kv_dtype} G={hq // hkv}", out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
     run.plan.deferred_partials = 0
+    o2, lse2 = run.run(c.q)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("lens,kv_dtype,hq,hkv,dim,dvo,page,window,splits", [
+    ([5000, 2100, 64, 1, 3333, 800], "bf16", 24, 4, 512, 512, 16, 0, 0),
+    ([5000, 2100, 64, 1, 3333, 800], "bf16", 24, 4, 512, 512, 16, 0, 8),
+    ([1024], "bf16", 6, 1, 512, 512, 16, 0, 0),
+    ([9000, 4100, 700], "fp8", 12, 4, 512, 512, 64, 0, 0),
+    ([9000, 4100, 700], "nvfp4", 12, 4, 512, 256, 16, 0, 0),
+    ([3000, 5000, 17, 2500], "bf16", 16, 8, 256, 256, 1, 1100, 0),
+    ([6000, 33, 4000], "bf16", 4, 4, 512, 256, 16, 0, 3)])
+def test_grouped_split_results(lens, kv_dtype, hq, hkv, dim, dvo, page, window, splits):
+    """Consecutive waves of a workgroup whose last segments belong to one split (request,
+    KV head) combine those results in LDS, the last to finish writing one slot: the output
+    matches the oracle and repeated runs give the same bits (the group merges in wave
+    order, whichever wave finishes last).  1024 keys on one KV head make one group of 8
+    waves that covers the whole request (a merge of one slot)."""
+    say(f"grouped split results {kv_dtype} lens={lens} G={hq // hkv} dims={dim}/{dvo} "
+        f"page={page} window={window} splits={splits}")
+    c = make_decode_case(lens, hq, hkv, dim, page, head_dim_vo=dvo, kv_dtype=kv_dtype,
+                         window=window, num_splits=splits, out_dtype="fp32", seed=71,
+                         device=dev())
+    run, o, lse = gpu_decode(c)
+    assert run.plan.grouped_partials == 1
+    groups = pa.decode_groups(run.plan, run.plan_buf)
+    assert max(n for n, _ in groups) >= 2
+    if lens == [1024]:
+        assert groups == [(8, 0)] * 8
+        assert pa.decode_merges(run.plan, run.plan_buf)[:, 3].tolist() == [1]
+    ref, ref_lse = oracle_decode(c)
+    compare(f"grouped {kv_dtype} G={hq // hkv}", out_to_np(o), ref, lse.cpu().numpy(), ref_lse)
     o2, lse2 = run.run(c.q)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)

@@ -102,11 +102,14 @@ def test_decode_plan_matches_reference_partition(lens, P, window, splits, hkv):
     nxt = plan.num_workers
     for w in range(plan.num_workers):
         assert segs[w, 6] == nxt
-        nxt += segs[w, 7]
+        nxt += segs[w, 7] & 0xFFFF
     assert nxt == plan.num_items and plan.workers_offset == 32 * plan.num_workers
-    ref_waves, ref_merges = decode_partition_ref(lens, window, splits, hkv)
+    assert plan.grouped_partials == 1  # bf16, 2 heads per KV head at 512: results fit LDS
+    ref_waves, ref_merges, ref_groups = decode_partition_ref(lens, window, splits, hkv,
+                                                             group_last=True)
     assert [[tuple(r) for r in w.tolist()] for w in waves] == ref_waves
     assert [tuple(r) for r in merges.tolist()] == ref_merges
+    assert pa.decode_groups(plan, buf) == ref_groups
     assert plan.num_workers == len(ref_waves) and plan.num_merges == len(ref_merges)
     assert plan.num_items == sum(len(w) for w in ref_waves)
     assert plan.num_slots == sum(m[3] for m in ref_merges)
@@ -122,7 +125,7 @@ def test_reference_partition_covers_visible_keys_exactly(lens, P, window, splits
     cuts fall on 16-key blocks; waves differ by at most one block; a fixed split's chunk
     boundaries are segment boundaries; slots of a merged pair are consecutive in key
     order; single-segment pairs write directly."""
-    waves, merges = decode_partition_ref(lens, window, splits, hkv)
+    waves, merges, _ = decode_partition_ref(lens, window, splits, hkv)
     per_pair = {}
     for w in waves:
         for b, h, t0, t1, slot in w:
@@ -166,7 +169,7 @@ def test_balanced_partition_of_the_gqa_decode_shape_gives_equal_pieces():
     2048 pieces would need (ceil(units / 2048) blocks) or one block less, and the fewest
     waves that size allows run, so almost none is short."""
     lens = list(np.random.default_rng(5).integers(1024, 8193, size=32))
-    waves, merges = decode_partition_ref(lens, 0, 0, 4)
+    waves, merges, _ = decode_partition_ref(lens, 0, 0, 4)
     total = 4 * sum(-(-int(L) // 16) for L in lens)
     blocks = [sum(-(-t1 // 16) - t0 // 16 for _, _, t0, t1, _ in w) for w in waves]
     m = -(-total // 2048)
@@ -250,9 +253,13 @@ def test_random_plans_match_the_reference(seed):
     cache = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, int(indptr[-1]) + 1, hkv, P, 512)
     plan, buf = pa.pa_decode_plan(params(hq=hkv * group, window=window), cache, indptr, last,
                                   splits)
-    ref_waves, ref_merges = decode_partition_ref(lens, window, splits, hkv)
+    # bf16 at 512/512: up to 6 heads per KV head leave LDS room for a result per wave
+    assert plan.grouped_partials == int(group <= 6)
+    ref_waves, ref_merges, ref_groups = decode_partition_ref(lens, window, splits, hkv,
+                                                             group_last=group <= 6)
     assert [[tuple(r) for r in w.tolist()] for w in pa.decode_waves(plan, buf)] == ref_waves
     assert [tuple(r) for r in pa.decode_merges(plan, buf).tolist()] == ref_merges
+    assert pa.decode_groups(plan, buf) == ref_groups
     assert plan.deferred_partials == deferred_rule(ref_waves)
     qo = [int(rng.integers(0, L + 1)) for L in lens]
     causal = bool(rng.integers(0, 2))
