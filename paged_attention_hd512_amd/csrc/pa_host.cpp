@@ -480,7 +480,14 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
       }
     }
   int64_t num_segs = 0;
-  for (auto& segs : piece_segs) num_segs += (int64_t)segs.size();
+  for (auto& segs : piece_segs) {
+    // A wave's record counts its further segments in 16 bits (the bits above carry its group).
+    if (segs.size() > 0x10000)
+      return fail(PA_ERR_UNSUPPORTED, "a wave would run %zu segments; at most 65536 are supported",
+                  segs.size());
+    num_segs += (int64_t)segs.size();
+  }
+  if (num_segs > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many decode segments");
 
   plan_header(plan, 1, params, cache, batch);
   plan->num_items = (int32_t)num_segs;
