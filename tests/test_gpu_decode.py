@@ -91,6 +91,9 @@ SWEEP = [
     ([64, 128, 192], 40, 8, 512, 512, 16, "bf16", 0, 64, "bf16"),
     ([300, 1000, 129, 256], 8, 2, 512, 512, 128, "bf16", 0, 0, "bf16"),
     ([300, 1000, 129, 257], 12, 4, 512, 512, 256, "fp8", 500, 3, "fp32"),
+    # groups of 7 and 5 query heads (the 8- and 6-wide instances with idle columns)
+    ([700, 1300, 50], 14, 2, 512, 512, 16, "bf16", 0, 0, "fp32"),
+    ([700, 1300, 50], 10, 2, 512, 256, 16, "fp8", 0, 3, "bf16"),
 ]
 
 
