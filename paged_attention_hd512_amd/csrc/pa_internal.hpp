@@ -62,7 +62,10 @@ struct DecodeSegment {  // 32 bytes
   int32_t slot;          // partial slot, or -1: write the final output directly
   int32_t page_base;     // kv_indptr[b]: the request's first entry in kv_indices
   int32_t more_begin;    // head segments: index of the wave's next segment
-  int32_t more_count;    // head segments: number of further segments of the wave
+  int32_t more_count;    // head segments, bits 0-15: number of further segments of the wave;
+                         // the wave's last segment, bits 16-23: size of the group of
+                         // neighbouring waves whose results it joins in LDS (0: none),
+                         // bits 24-31: that group's first wave within the workgroup
 };
 
 struct MergeItem {       // 16 bytes
