@@ -19,6 +19,9 @@ Decode rule (units of 16-token logical blocks, block j = tokens [16j, 16j+16)):
 * Pieces (one wave each) cut the flattened axis into P near-equal parts
   [U p // P, U (p+1) // P): with P0 = min(WAVE_SLOTS, ceil(U / MIN_PIECE_BLOCKS)) and the
   largest part size m = ceil(U / P0), P = ceil(U / m), the fewest parts of at most m units.
+  Pair-aligned instead, when S = 0 (no fixed split) and sum over (b, h) of
+  c_bh = ceil(n_b / m) is at most WAVE_SLOTS: each (b, h) range on its own in c_bh
+  near-equal parts [o_bh + n_b k // c_bh, o_bh + n_b (k+1) // c_bh), in (b, h) order.
 * A fixed split S > 0 (split-K S) cuts every (b, h) range into c = min(S, n_b) chunks
   [o_bh + n_b k // c, o_bh + n_b (k+1) // c); S = 0 adds no cuts.
 * A piece is cut at (b, h) boundaries and at chunk boundaries into segments, so every
@@ -88,7 +91,12 @@ def decode_partition_ref(kv_lens, window, num_splits, num_kv_heads, group_last=F
     p0 = min(WAVE_SLOTS, _ceil_div(total, MIN_PIECE_BLOCKS))
     m = _ceil_div(total, p0) if p0 > 0 else 0
     p = _ceil_div(total, m) if m > 0 else 0
-    pieces = [(total * k // p, total * (k + 1) // p) for k in range(p)]
+    per_pair = [_ceil_div(nblk[b], m) if m > 0 else 0 for b, _ in pairs]
+    if num_splits == 0 and m > 0 and sum(per_pair) <= WAVE_SLOTS:
+        pieces = [(origin[i] + nblk[b] * k // c, origin[i] + nblk[b] * (k + 1) // c)
+                  for i, ((b, _), c) in enumerate(zip(pairs, per_pair)) for k in range(c)]
+    else:
+        pieces = [(total * k // p, total * (k + 1) // p) for k in range(p)]
 
     def cuts_of(i):  # unit positions that end a segment inside pair i's range
         b = pairs[i][0]

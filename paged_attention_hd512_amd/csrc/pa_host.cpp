@@ -363,7 +363,20 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
     const int64_t np0 = std::min<int64_t>(kDecodeWaveSlots, (total + kMinPieceBlocks - 1) / kMinPieceBlocks);
     const int64_t per = np0 > 0 ? (total + np0 - 1) / np0 : 0;
     const int64_t np = per > 0 ? (total + per - 1) / per : 0;
-    for (int64_t k = 0; k < np; ++k) pieces.emplace_back(total * k / np, total * (k + 1) / np);
+    // Without a fixed split, when cutting each (b, h) on its own into near-equal pieces of
+    // at most that size takes no more waves than there are slots, no piece crosses a pair
+    // boundary: every wave then runs one segment, and none pays a second start.
+    int64_t aligned = 0;
+    for (int64_t i = 0; i < npairs; ++i) aligned += (origin[i + 1] - origin[i] + per - 1) / std::max<int64_t>(per, 1);
+    if (num_splits == 0 && per > 0 && aligned <= kDecodeWaveSlots) {
+      for (int64_t i = 0; i < npairs; ++i) {
+        const int64_t n = origin[i + 1] - origin[i];
+        const int64_t c = (n + per - 1) / per;
+        for (int64_t k = 0; k < c; ++k) pieces.emplace_back(origin[i] + n * k / c, origin[i] + n * (k + 1) / c);
+      }
+    } else {
+      for (int64_t k = 0; k < np; ++k) pieces.emplace_back(total * k / np, total * (k + 1) / np);
+    }
   }
   // End of the segment that starts at unit u of pair i: the pair's end, or with a fixed
   // split S the next of the S chunk boundaries of the pair, [o + n k / c) with c = min(S, n).

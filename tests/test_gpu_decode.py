@@ -138,11 +138,12 @@ def test_page_relabeling_gives_bit_identical_output_and_runs_are_deterministic()
 
 
 def test_waves_that_run_several_segments():
-    """Short requests: balanced pieces of 8 blocks span several (request, KV head) pairs,
-    so waves run several segments, some pairs are merged and some are written directly."""
+    """Many short requests: cutting each (request, KV head) on its own would take more
+    waves than there are slots, so balanced pieces of 8 blocks span several pairs; waves run
+    several segments, some pairs are merged and some are written directly."""
     say("waves with several segments")
-    lens = list(np.random.default_rng(11).integers(1, 70, size=40)) + [0, 700]
-    c = make_decode_case(lens, 12, 3, 512, 16, num_splits=0, out_dtype="fp32", seed=12,
+    lens = list(np.random.default_rng(11).integers(1, 40, size=2500)) + [0, 700]
+    c = make_decode_case(lens, 4, 1, 512, 16, num_splits=0, out_dtype="fp32", seed=12,
                          device=dev())
     runner, o, lse = gpu_decode(c)
     waves = pa.decode_waves(runner.plan, runner.plan_buf)

@@ -77,6 +77,8 @@ DECODE_CASES = [
     ([100, 5, 0], 3, 7, 3, 1),
     (list(np.random.default_rng(0).integers(1024, 8193, size=32)), 16, 0, 8, 4),
     (list(np.random.default_rng(1).integers(4096, 32769, size=64)), 64, 0, 0, 4),
+    # pair-aligned pieces of very different lengths (pairs of 3, 63, 1 and 2 blocks)
+    ([40, 1000, 3, 17], 16, 0, 0, 2),
 ]
 
 
@@ -158,8 +160,25 @@ def test_reference_partition_covers_visible_keys_exactly(lens, P, window, splits
                 assert len(segs) >= c
     blocks = [sum(-(-t1 // 16) - t0 // 16 for _, _, t0, t1, _ in w) for w in waves]
     assert blocks == sorted(blocks, reverse=True)  # longest first
+    # Balanced pieces of at most m blocks (m from the total and the 2048 wave slots); with
+    # no fixed split, pieces follow the pair boundaries whenever cutting each pair on its own
+    # into pieces of at most m blocks fits the slots: one segment per wave, a pair's pieces
+    # within one block of each other.  Otherwise the flattened axis in near-equal parts.
+    nblk = [0 if int(L) == 0 else -(-int(L) // 16) - (max(0, int(L) - window) if window > 0 else 0) // 16
+            for L in lens]
+    units = hkv * sum(nblk)
     if waves:
-        assert max(blocks) - min(blocks) <= 1 and len(waves) <= 2048
+        m = -(-units // min(2048, -(-units // 8)))
+        assert max(blocks) <= m and len(waves) <= 2048
+        aligned = splits == 0 and hkv * sum(-(-n // m) for n in nblk) <= 2048
+        if aligned:
+            assert all(len(w) == 1 for w in waves)
+            per_pair = {}
+            for w, nb in zip(waves, blocks):
+                per_pair.setdefault(tuple(w[0][:2]), []).append(nb)
+            assert all(max(v) - min(v) <= 1 for v in per_pair.values())
+        else:
+            assert max(blocks) - min(blocks) <= 1
     slots = sorted(s for w in waves for *_, s in w if s >= 0)
     assert slots == list(range(len(slots)))  # every slot written once
 
