@@ -1019,10 +1019,13 @@ struct PrefillMergeArgs {
 // rows (grid: merges x KV heads x tile_rows / 4).  The chunk outputs are weighted by
 // exp2(lse_bf(c) - max) / sum (chunks with no visible key have lse -inf and weight 0); the
 // lse is the log-sum-exp of the fp32 ones.  A row with no visible key at all gets a zero
-// output and lse -inf.  Lane l owns dims DVO/64 * l .. +DVO/64.
+// output and lse -inf.  Lane l owns dims DVO/64 * l .. +DVO/64.  The chunks' log-sum-exps
+// are read one per lane, 64 chunks a pass, and UN chunk rows are requested at once; every
+// row is added in chunk order.
 template <int DVO>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeArgs a) {
   constexpr int E = DVO / 64;
+  constexpr int UN = 8;  // chunk rows in flight
   const PrefillMerge m = a.merges[blockIdx.x];
   const int kvh = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -1033,32 +1036,61 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeArgs a) 
   const int64_t q_row = (int64_t)(m.q_begin + tok) * a.num_qo_heads + head;
   const int64_t row0 = ((int64_t)m.slot_begin * a.num_kv_heads + kvh) * kPrefillTileRows + rr;
   const int64_t step = (int64_t)a.num_kv_heads * kPrefillTileRows;  // rows between slots
+  const int n = m.num_slots;
+  auto lse_of = [&](int c) { return *(const f32x2_t*)(a.part_lse + 2 * (row0 + c * step)); };
   float mw = -INFINITY, mo = -INFINITY;
-  for (int c = 0; c < m.num_slots; ++c) {
-    const f32x2_t l = *(const f32x2_t*)(a.part_lse + 2 * (row0 + c * step));
-    mw = fmaxf(mw, l[0]);
-    mo = fmaxf(mo, l[1]);
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    if (c0 + lane < n) {
+      const f32x2_t l = lse_of(c0 + lane);
+      mw = fmaxf(mw, l[0]);
+      mo = fmaxf(mo, l[1]);
+    }
+  }
+  mw = max_xor16(max_xor32(mw));
+  mo = max_xor16(max_xor32(mo));
+#pragma unroll
+  for (int s = 8; s >= 1; s >>= 1) {
+    mw = fmaxf(mw, shfl_xor_f(mw, s));
+    mo = fmaxf(mo, shfl_xor_f(mo, s));
   }
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  float sw = 0.f, so = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < m.num_slots; ++c) {
-    const int64_t pr = row0 + c * step;
-    const f32x2_t l = *(const f32x2_t*)(a.part_lse + 2 * pr);
-    const float w = l[0] == -INFINITY ? 0.f : exp2f(l[0] - mw);
-    so += l[1] == -INFINITY ? 0.f : exp2f(l[1] - mo);
-    sw += w;
-    const float* src = a.part_o + pr * DVO + E * lane;
-#pragma unroll
-    for (int e = 0; e < E; e += 4) {
-      const f32x4_t v = *(const f32x4_t*)(src + e);
-      acc[e] = fmaf(w, v[0], acc[e]);
-      acc[e + 1] = fmaf(w, v[1], acc[e + 1]);
-      acc[e + 2] = fmaf(w, v[2], acc[e + 2]);
-      acc[e + 3] = fmaf(w, v[3], acc[e + 3]);
+  float sw = 0.f, so = 0.f;  // this lane's chunks
+  const float* src0 = a.part_o + row0 * DVO + E * lane;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int cn = min(64, n - c0);
+    float w = 0.f;
+    if (lane < cn) {
+      const f32x2_t l = lse_of(c0 + lane);
+      w = l[0] == -INFINITY ? 0.f : exp2f(l[0] - mw);
+      so += l[1] == -INFINITY ? 0.f : exp2f(l[1] - mo);
+      sw += w;
     }
+    for (int c = 0; c < cn; c += UN) {
+      f32x4_t x[UN][E / 4];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int cc = c0 + min(c + u, cn - 1);  // past the end: the last chunk, weight 0
+#pragma unroll
+        for (int e = 0; e < E / 4; ++e) x[u][e] = *(const f32x4_t*)(src0 + cc * step * DVO + 4 * e);
+      }
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c + u));
+#pragma unroll
+        for (int e = 0; e < E / 4; ++e)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[4 * e + v] = fmaf(wu, x[u][e][v], acc[4 * e + v]);
+      }
+    }
+  }
+  sw = sum_xor16(sum_xor32(sw));
+  so = sum_xor16(sum_xor32(so));
+#pragma unroll
+  for (int s = 8; s >= 1; s >>= 1) {
+    sw += shfl_xor_f(sw, s);
+    so += shfl_xor_f(so, s);
   }
   const float inv = sw > 0.f ? 1.f / sw : 0.f;
   const int64_t off = q_row * DVO + E * lane;
