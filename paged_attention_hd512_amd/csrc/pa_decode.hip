@@ -143,6 +143,12 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
   __shared__ __attribute__((aligned(16))) int progress[NWG];
   __shared__ __attribute__((aligned(16))) int grp_arrived[NWG];  // per group, at its first wave
   __shared__ __attribute__((aligned(16))) float park_all[DEFER ? NWG : 1][DEFER ? PARK : 4];
+  // The planner decides from decode_lds_bytes whether split results can wait in LDS: it
+  // must cover these buffers, and they must fit the CU.
+  constexpr int kLdsUsed = sizeof(q_all) + sizeof(p_all) + sizeof(alpha_all) + sizeof(progress) +
+                           sizeof(grp_arrived) + sizeof(park_all);
+  static_assert(kLdsUsed <= decode_lds_bytes(DQK, DVO, GMAX, PC) || !DEFER, "LDS budget");
+  static_assert(kLdsUsed <= kLdsBytesPerCu, "LDS of one CU");
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
