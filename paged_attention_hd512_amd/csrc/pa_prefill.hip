@@ -72,7 +72,9 @@ struct PrefillArgs {
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
   const PrefillItem* items;
-  void* out;                  // [total_q, Hq, DVO]
+  void* out;                  // [total_q, Hq, out_stride], this launch's DVO columns first
+  int32_t out_stride;         // elements between output rows (DVO, or the whole head_dim
+                              // when a launch computes one part of it)
   float* lse;                 // [total_q, Hq] or null
   float* part_o;              // split tiles: [slot][kv head][tile row][DVO] fp32
   float* part_lse;            // [slot][kv head][tile row][2] fp32, log2 domain
@@ -612,10 +614,9 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   // the issuing waves).  Other page sizes: every wave copies its own rows at the interval
   // start.
   constexpr bool SPREAD = PM == kPagesStage && !CONV;
-  // NVFP4 at 512/512: the first group loads the next stage's codes after its
-  // S^T (not before), and the second group stores them before its S^T, so the codes are
-  // never live beside the K operands of S^T, where the registers peak.
-  constexpr bool LATE = CONV && DQK == 512 && DVO == 512;
+  // NVFP4 holds a stage's codes in registers, which the 512/512 form has no room for: the
+  // host runs NVFP4 at 512/512 as two 512/256 launches, one per half of the value head_dim.
+  static_assert(!(CONV && DQK == 512 && DVO == 512), "NVFP4 at 512/512 runs as two 512/256 halves");
   // ---- S^T = K Q^T from K buffer kslot_c into s0 (keys 0..15) and s1 (keys 16..31); lane
   // holds keys 4*g4 + i.  With COPY the next stage's copies (K into the other buffer, V into
   // v_lds + vo_next) are issued among the steps.
@@ -889,9 +890,6 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
         softmax(st - 1);
         pv(vo_prev);
       }
-      if constexpr (LATE) {
-        if (has_next) conv_store(other_c, vo_next);
-      }
       qk(kslot_c, std::false_type{}, vo_next);
     } else {
       if constexpr (SPREAD) {
@@ -901,9 +899,6 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
         } else {
           qk(kslot_c, std::false_type{}, vo_next);
         }
-      } else if constexpr (LATE) {
-        qk(kslot_c, std::false_type{}, vo_next);
-        if (has_next) copy_stage(st + 1, other_c, vo_next);
       } else {
         if (has_next) copy_stage(st + 1, other_c, vo_next);
         qk(kslot_c, std::false_type{}, vo_next);
@@ -911,7 +906,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
       softmax(st);
       pv(vo_cur);
     }
-    if constexpr (CONV && !(LATE && decltype(second_c)::value)) {
+    if constexpr (CONV) {
       if (has_next) conv_store(other_c, vo_next);
     }
     const int t = vo_prev;
@@ -988,7 +983,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
     }
     return;
   }
-  const int64_t out_row = q_row * DVO;
+  const int64_t out_row = q_row * a.out_stride;
 #pragma unroll
   for (int t = 0; t < OT; ++t) {
     const int d = 16 * t + 4 * g4;
@@ -1008,6 +1003,7 @@ struct PrefillMergeArgs {
   const float* part_o;
   const float* part_lse;
   void* out;
+  int32_t out_stride;
   float* lse;
   int32_t num_qo_heads;
   int32_t num_kv_heads;
@@ -1093,7 +1089,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeArgs a) 
     so += shfl_xor_f(so, s);
   }
   const float inv = sw > 0.f ? 1.f / sw : 0.f;
-  const int64_t off = q_row * DVO + E * lane;
+  const int64_t off = q_row * a.out_stride + E * lane;
 #pragma unroll
   for (int e = 0; e < E; e += 4) {
     const f32x4_t v = {acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
@@ -1106,8 +1102,10 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeArgs a) 
 template <int DQK, int DVO, bool SHORT>
 static void launch_prefill(const PrefillArgs& a, int pm, int kv, int grid, hipStream_t s) {
   if (kv == kKvFp4) {
-    if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvFp4, SHORT><<<grid, 512, 0, s>>>(a);
-    else prefill_kernel<DQK, DVO, kPagesAny, kKvFp4, SHORT><<<grid, 512, 0, s>>>(a);
+    if constexpr (!(DQK == 512 && DVO == 512)) {  // 512/512 runs as two 512/256 halves
+      if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvFp4, SHORT><<<grid, 512, 0, s>>>(a);
+      else prefill_kernel<DQK, DVO, kPagesAny, kKvFp4, SHORT><<<grid, 512, 0, s>>>(a);
+    }
   } else if (kv == kKvFp8) {
     if (pm == kPagesStage) prefill_kernel<DQK, DVO, kPagesStage, kKvFp8, SHORT><<<grid, 512, 0, s>>>(a);
     else if (pm == kPagesPow2) prefill_kernel<DQK, DVO, kPagesPow2, kKvFp8, SHORT><<<grid, 512, 0, s>>>(a);
@@ -1191,29 +1189,47 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
                      ? kPagesStage
                      : ((P & (P - 1)) == 0 ? kPagesPow2 : kPagesAny);
   const bool short_tiles = plan->short_tiles != 0;
-  if (dqk == 512 && dvo == 512) launch_prefill<512, 512>(a, pm, kv, short_tiles, grid, s);
-  else if (dqk == 256 && dvo == 256) launch_prefill<256, 256>(a, pm, kv, short_tiles, grid, s);
-  else launch_prefill<512, 256>(a, pm, kv, short_tiles, grid, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
-  count_launches(1);
-  if (plan->num_merges > 0) {
-    PrefillMergeArgs m;
-    m.merges = (const PrefillMerge*)(ws + plan->merges_offset);
-    m.part_o = a.part_o;
-    m.part_lse = a.part_lse;
-    m.out = out;
-    m.lse = lse;
-    m.num_qo_heads = params->num_qo_heads;
-    m.num_kv_heads = cache->num_kv_heads;
-    m.group = a.group;
-    m.out_fp32 = a.out_fp32;
-    const dim3 mg(plan->num_merges, cache->num_kv_heads, kPrefillTileRows / 4);
-    if (dvo == 512) prefill_merge_kernel<512><<<mg, 256, 0, s>>>(m);
-    else prefill_merge_kernel<256><<<mg, 256, 0, s>>>(m);
-    e = hipGetLastError();
-    if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill merge launch: %s", hipGetErrorString(e));
+  // NVFP4 at 512/512 runs as two passes of the 512/256 kernel, one per half of the value
+  // head_dim (the scores are computed in both): the 512/512 form's registers spill.  Each
+  // pass reads its half of every V row and of its block scales, writes its half of each
+  // output row, and has its own half of the partial-output workspace.
+  const int parts = kv == kKvFp4 && dqk == 512 && dvo == 512 ? 2 : 1;
+  const int pdvo = dvo / parts;
+  const int64_t part_rows = (int64_t)plan->num_slots * cache->num_kv_heads * kPrefillTileRows;
+  float* part_o0 = a.part_o;
+  a.out_stride = dvo;
+  for (int h = 0; h < parts; ++h) {
+    if (h > 0) {
+      a.v += pdvo / 2;        // packed E2M1: two elements a byte
+      a.v_sf += pdvo / 16;    // one E4M3 scale per 16 elements
+      a.out = (char*)a.out + (size_t)pdvo * (a.out_fp32 ? 4 : 2);
+      a.part_o = part_o0 + part_rows * pdvo;
+    }
+    if (dqk == 512 && pdvo == 512) launch_prefill<512, 512>(a, pm, kv, short_tiles, grid, s);
+    else if (dqk == 256) launch_prefill<256, 256>(a, pm, kv, short_tiles, grid, s);
+    else launch_prefill<512, 256>(a, pm, kv, short_tiles, grid, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
     count_launches(1);
+    if (plan->num_merges > 0) {
+      PrefillMergeArgs m;
+      m.merges = (const PrefillMerge*)(ws + plan->merges_offset);
+      m.part_o = a.part_o;
+      m.part_lse = a.part_lse;
+      m.out = a.out;
+      m.out_stride = dvo;
+      m.lse = a.lse;
+      m.num_qo_heads = params->num_qo_heads;
+      m.num_kv_heads = cache->num_kv_heads;
+      m.group = a.group;
+      m.out_fp32 = a.out_fp32;
+      const dim3 mg(plan->num_merges, cache->num_kv_heads, kPrefillTileRows / 4);
+      if (pdvo == 512) prefill_merge_kernel<512><<<mg, 256, 0, s>>>(m);
+      else prefill_merge_kernel<256><<<mg, 256, 0, s>>>(m);
+      e = hipGetLastError();
+      if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill merge launch: %s", hipGetErrorString(e));
+      count_launches(1);
+    }
   }
   return PA_OK;
 }
