@@ -242,7 +242,6 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
   u32x4_t kbuf[NKL];
   vload_t vbuf[NVL];
   ksf_t ksf;            // NVFP4: this lane's K block scales of the block (E4M3 codes)
-  uint32_t vsf[NVL];    // V block scales (E4M3 codes), when V rows are read a row per lane set
   vq_t vq[8];           // NVFP4: TPD head_dim columns of eight V rows (see issue_v)
   uint32_t vsq[8];      // NVFP4: their block scales (E4M3 codes)
   float acc[GMAX][8];
@@ -304,18 +303,13 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerGroup, 2) void decode_partial_k
         }
       } else {
 #pragma unroll
-      for (int i = 0; i < NVL; ++i) {
-        const int src = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
-        int64_t off, soff = 0;
-        if constexpr (RPI == 1) {
-          off = readlane_i64(voff, src);
-          if constexpr (KV == kKvFp4) soff = readlane_i64(vsoff, src);
-        } else {
-          off = shfl_i64(voff, src);
-          if constexpr (KV == kKvFp4) soff = shfl_i64(vsoff, src);
+        for (int i = 0; i < NVL; ++i) {
+          const int src = RPI * i + (RPI == 2 ? (lane >> 5) : 0);
+          int64_t off;
+          if constexpr (RPI == 1) off = readlane_i64(voff, src);  // src is wave-uniform
+          else off = shfl_i64(voff, src);
+          vbuf[i] = __builtin_nontemporal_load((const vload_t*)(a.v + off + (lane % LPR) * VB8));
         }
-        vbuf[i] = __builtin_nontemporal_load((const vload_t*)(a.v + off + (lane % LPR) * VB8));
-      }
       }
     };
     // P V of one block: rescale the accumulators by the block's alpha, then add p * V with
