@@ -123,6 +123,11 @@ NVFP4_PREFILL_SWEEP = [
     ([3, 1, 16], [3000, 5000, 2100], 4, 2, 512, 256, 64, True, 0, "fp32"),
     ([16] * 4, [6000] * 4, 16, 8, 512, 256, 16, True, 0, "bf16"),
     ([8, 8], [9000, 9000], 4, 2, 512, 256, 32, True, 3000, "fp32"),
+    # 512/512 runs as two passes over the halves of the value head_dim: with the split-K
+    # merge, a window and bf16 output too
+    ([3, 1, 16], [3000, 5000, 2100], 4, 2, 512, 512, 64, True, 0, "fp32"),
+    ([8, 8], [9000, 9000], 4, 2, 512, 512, 16, True, 3000, "bf16"),
+    ([130, 64, 1], [300, 64, 1], 16, 8, 512, 512, 1, True, 0, "bf16"),
 ]
 
 
