@@ -38,8 +38,9 @@ SWEEP = [
     ([8, 8], [9000, 9000], 4, 2, 512, 512, 32, True, 3000, "fp32"),
     ([16] * 4, [6000] * 4, 16, 8, 512, 512, 64, True, 0, "bf16"),
     ([5, 2], [2500, 4000], 6, 2, 256, 256, 3, True, 0, "fp32"),
-    # groups of 5 and 7 query heads: tiles start and end inside a token's heads
+    # groups of 5, 6 and 7 query heads: tiles start and end inside a token's heads
     ([45, 9], [300, 9], 10, 2, 512, 512, 16, True, 0, "fp32"),
+    ([45, 9], [300, 9], 12, 2, 512, 256, 16, True, 0, "fp32"),
     ([33], [200], 7, 1, 512, 256, 64, True, 40, "bf16"),
 ]
 
