@@ -50,7 +50,11 @@ into c = ceil(S / C) chunks covering keys [max(kv_begin, 32 (s0 + S k // c)),
 min(kv_end, 32 (s0 + S (k+1) // c))), s0 = kv_begin // 32; chunks take consecutive
 partial slots in (b, tile, chunk) order and the tile a merge entry (b, row_begin, row_end,
 q_begin, first slot, c).  Items run by key count descending, ties in (b, tile, chunk)
-order.
+order; except, without split-K, when the K and V bytes the tiles read (per request, the keys
+from its tiles' smallest kv_begin to its largest kv_end, times H_kv times the bytes a key
+takes in one KV head) exceed LAST_LEVEL_CACHE_BYTES: then request by request (requests in
+the order of their longest tile in the first ordering, ties by b), key count descending
+within each, so the tiles running together read one request's keys.
 """
 
 BLOCK_TOKENS = 16
@@ -59,6 +63,7 @@ WAVES_PER_GROUP = 8
 MIN_PIECE_BLOCKS = 8
 MAX_SPLITS = 64
 PREFILL_STAGE = 32
+LAST_LEVEL_CACHE_BYTES = 256 << 20  # the GPU's last-level (memory-side) cache
 SPLIT_ITEMS = 512
 MIN_CHUNK_STAGES = 8
 
@@ -189,8 +194,10 @@ def decode_partition_ref(kv_lens, window, num_splits, num_kv_heads, group_last=F
     return waves, merges, groups
 
 
-def prefill_plan_ref(qo_lens, kv_lens, group, tile_rows, causal, window, num_kv_heads):
-    """Returns (items, merges).
+def prefill_plan_ref(qo_lens, kv_lens, group, tile_rows, causal, window, num_kv_heads,
+                     kv_bytes_per_key=0):
+    """Returns (items, merges).  kv_bytes_per_key: bytes of one key's K and V rows in one KV
+    head (0: never order request by request).
 
     items:  in execution order, each (b, row_begin, row_end, kv_begin, kv_end, slot), slot
             -1 for a tile computed whole.
@@ -231,4 +238,14 @@ def prefill_plan_ref(qo_lens, kv_lens, group, tile_rows, causal, window, num_kv_
                           min(ke, PREFILL_STAGE * (s0 + s * (k + 1) // c)), slots))
             slots += 1
     order = sorted(range(len(items)), key=lambda i: (-(items[i][4] - items[i][3]), i))
+    span = {}
+    for b, _, _, kb, ke, _ in items:
+        lo, hi = span.get(b, (kb, ke))
+        span[b] = (min(lo, kb), max(hi, ke))
+    kv_bytes = sum(hi - lo for lo, hi in span.values()) * num_kv_heads * kv_bytes_per_key
+    if chunk == 0 and kv_bytes > LAST_LEVEL_CACHE_BYTES:
+        first = {}
+        for i in order:
+            first.setdefault(items[i][0], len(first))
+        order = sorted(order, key=lambda i: first[items[i][0]])  # stable: lengths stay sorted
     return [items[i] for i in order], merges

@@ -658,6 +658,32 @@ pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache
   std::stable_sort(items.begin(), items.end(), [](const Tmp& a, const Tmp& b) {
     return (a.it.kv_end - a.it.kv_begin) > (b.it.kv_end - b.it.kv_begin);
   });
+  // Without split-K, when the K and V bytes the tiles read do not fit the last-level cache,
+  // the tiles run request by request (requests in the order of their longest tile, key
+  // count descending within each): the tiles running together then read one request's keys,
+  // which stay in that cache for the tiles that start later.
+  if (chunk == 0 && !items.empty()) {
+    const int64_t dk = cache->head_dim_qk + cache->head_dim_vo;
+    const int64_t per_key = cache->kv_dtype == PA_DTYPE_BF16 ? 2 * dk
+                            : cache->kv_dtype == PA_DTYPE_NVFP4 ? dk / 2 + dk / 16
+                                                                : dk;  // FP8
+    std::vector<int64_t> lo(batch, INT64_MAX), hi(batch, INT64_MIN);
+    for (const Tmp& t : items) {
+      lo[t.it.b] = std::min<int64_t>(lo[t.it.b], t.it.kv_begin);
+      hi[t.it.b] = std::max<int64_t>(hi[t.it.b], t.it.kv_end);
+    }
+    int64_t keys = 0;
+    for (int32_t b = 0; b < batch; ++b)
+      if (hi[b] > lo[b]) keys += hi[b] - lo[b];
+    if (keys * hkv * per_key > kLastLevelCacheBytes) {
+      std::vector<int32_t> rank(batch, -1);
+      int32_t next = 0;
+      for (const Tmp& t : items)
+        if (rank[t.it.b] < 0) rank[t.it.b] = next++;
+      std::stable_sort(items.begin(), items.end(),
+                       [&](const Tmp& a, const Tmp& b) { return rank[a.it.b] < rank[b.it.b]; });
+    }
+  }
   plan_header(plan, 2, params, cache, batch);
   plan->num_items = (int32_t)items.size();
   plan->num_merges = (int32_t)merges.size();

@@ -38,6 +38,7 @@ constexpr bool decode_parks(int dqk, int dvo, int gmax, bool fp4) {
 // Query heads the decode kernel computes for a group of `group` (its instantiations).
 constexpr int decode_gmax(int group) { return group <= 4 ? group : group <= 6 ? 6 : 8; }
 constexpr int kMaxPrefillGroup = 16;
+constexpr int64_t kLastLevelCacheBytes = int64_t(256) << 20;  // MI355X memory-side cache
 
 // Prefill: query rows per tile ((token, head) pairs of one head group), 16 per wave.
 constexpr int kPrefillTileRows = 128;

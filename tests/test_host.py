@@ -237,7 +237,8 @@ def test_prefill_plan_matches_reference_tiles(qo, kv, group, causal, window):
                                    cache, qo_indptr, indptr, last)
     items = pa.prefill_items(plan, buf)
     merges = pa.prefill_merges(plan, buf)
-    ref_items, ref_merges = prefill_plan_ref(qo, kv, group, plan.tile_rows, causal, window, hkv)
+    ref_items, ref_merges = prefill_plan_ref(qo, kv, group, plan.tile_rows, causal, window, hkv,
+                                             kv_bytes_per_key=2 * (512 + 512))
     assert [tuple(r[:5]) + (r[8],) for r in items.tolist()] == [tuple(r) for r in ref_items]
     assert [tuple(r) for r in merges.tolist()] == [tuple(r) for r in ref_merges]
     for r in items:
@@ -288,11 +289,33 @@ def test_random_plans_match_the_reference(seed):
     plan, buf = pa.pa_prefill_plan(params(hq=hkv * pgroup, window=window, causal=int(causal)),
                                    cache, qo_indptr, indptr, last)
     ref_items, ref_pmerges = prefill_plan_ref(qo, lens, pgroup, plan.tile_rows, causal, window,
-                                              hkv)
+                                              hkv, kv_bytes_per_key=2 * (512 + 512))
     items = pa.prefill_items(plan, buf)
     assert [tuple(r[:5]) + (r[8],) for r in items.tolist()] == [tuple(r) for r in ref_items]
     assert [tuple(r) for r in pa.prefill_merges(plan, buf).tolist()] == [tuple(r) for r in ref_pmerges]
     assert plan.short_tiles == short_tiles_rule(ref_items)
+
+
+def test_tiles_run_request_by_request_when_their_keys_exceed_the_last_level_cache():
+    """4 x 4096 new tokens (no split-K): over 20000-key requests the tiles read 328 MB of K
+    and V, more than the 256 MB last-level cache, so they run request by request (longest
+    first within each); over 5120-key requests (84 MB) the longest tiles of all requests run
+    first."""
+    def order(kv_len):
+        indptr, last = lens_to_table([kv_len] * 4, 16)
+        qo_indptr = np.arange(5, dtype=np.int32) * 4096
+        cache = pa.pa_kv_cache_hnd(0x10000, pa.PA_DTYPE_BF16, int(indptr[-1]) + 1, 2, 16, 512)
+        plan, buf = pa.pa_prefill_plan(params(hq=4), cache, qo_indptr, indptr, last)
+        assert plan.num_merges == 0
+        items = pa.prefill_items(plan, buf)
+        return items[:, 0].tolist(), (items[:, 4] - items[:, 3]).tolist()
+    reqs, lens = order(20000)
+    assert reqs == sorted(reqs) and len(set(reqs)) == 4
+    for b in range(4):
+        run = [n for r, n in zip(reqs, lens) if r == b]
+        assert run == sorted(run, reverse=True)
+    reqs, lens = order(5120)
+    assert lens == sorted(lens, reverse=True) and reqs[:4] == [0, 1, 2, 3]
 
 
 def test_short_tile_form_is_chosen_for_tiles_of_few_rows():
