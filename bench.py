@@ -163,6 +163,22 @@ def time_protocol(launch, stream, iters=50):
             "mean_ms": round(sum(t) / iters, 5)}
 
 
+def settle(launch, ms):
+    """Untimed steps for at least `ms` of host wall time; returns how many ran.  After an
+    idle gap (host work such as the oracle baseline) the GPU's clock takes tens of
+    milliseconds under load to return to its loaded level: causal prefill steps measured one
+    by one go from about 2.0 ms to 1.57 ms over their first 20 steps, so a line measured right
+    after host work without this would time part of that ramp."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            launch()
+        n += 4
+        torch.cuda.synchronize()
+    return n
+
+
 class Rotation:
     """Calls the launches of several copies of a workload in turn (one per call)."""
 
@@ -201,11 +217,12 @@ def pool_copy(case):
     return c2
 
 
-def time_decode(case, steps, warmup, copies=1, profile=False):
+def time_decode(case, steps, warmup, copies=1, profile=False, settle_ms=0.0):
     """Returns (ms_per_step, partial_kernel_ms, merge_ms, wall_ms, plan, protocol): the step
     time of back-to-back decode steps, then the two kernels' durations from events around
     each, then the 50-iteration protocol.  With copies = 2 every loop alternates between
-    two copies of the pool.  With profile, only warmup + steps decode steps run."""
+    two copies of the pool.  With profile, only warmup + steps decode steps run.  With
+    settle_ms, untimed steps run for that long after the warmup ones."""
     import torch
     import paged_attention_hd512_amd.pa as pa
 
@@ -229,6 +246,7 @@ def time_decode(case, steps, warmup, copies=1, profile=False):
             step_fn()
         torch.cuda.synchronize()
         return None, None, None, None, runners[0][0].plan, None
+    settled = settle(step_fn, settle_ms)
     step, wall = time_steps(step_fn, stream, steps)
     # The merge alone, back to back (it is idempotent: it re-reads the partials); consecutive
     # launches abut, so this average carries none of the few microseconds that an event
@@ -239,6 +257,8 @@ def time_decode(case, steps, warmup, copies=1, profile=False):
                           stream, steps) if runners[0][0].plan.num_merges > 0 else (0.0, 0.0)
     part = step - merge
     proto = time_protocol(step_fn, stream)
+    if settle_ms > 0:
+        proto.update(settle_ms=settle_ms, settle_steps=settled)
     return max(step, 1e-9), part, merge, wall, runners[0][0].plan, proto
 
 
@@ -275,10 +295,11 @@ def time_decode_graph(case, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def time_prefill(case, steps, warmup, profile=False):
+def time_prefill(case, steps, warmup, profile=False, settle_ms=0.0):
     """Returns (ms_per_step, kernel_ms, wall_ms, plan, protocol): back-to-back prefill steps,
     then the duration of one step's launch(es) from events around it, then the 50-iteration
-    protocol.  With profile, only warmup + steps prefill steps run."""
+    protocol.  With profile, only warmup + steps prefill steps run.  With settle_ms, untimed
+    steps run for that long after the warmup ones."""
     import torch
     from paged_attention_hd512_amd import PagedPrefill
     import paged_attention_hd512_amd.pa as pa
@@ -301,11 +322,14 @@ def time_prefill(case, steps, warmup, profile=False):
             pa.pa_paged_prefill(*args)
         torch.cuda.synchronize()
         return None, None, None, run.plan, None
+    settled = settle(lambda: pa.pa_paged_prefill(*args), settle_ms)
     step, wall = time_steps(lambda: pa.pa_paged_prefill(*args), stream, steps)
     # A prefill step is its kernel launch(es): back-to-back steps abut, so the step average
     # is the launch duration (events between launches would add a few microseconds each).
     kern = step
     proto = time_protocol(lambda: pa.pa_paged_prefill(*args), stream)
+    if settle_ms > 0:
+        proto.update(settle_ms=settle_ms, settle_steps=settled)
     return step, kern, wall, run.plan, proto
 
 
@@ -499,7 +523,7 @@ def decode_config(case):
             "kv_len_mean": float(case.kv_lens.mean()), "out_dtype": case.out_dtype}
 
 
-def measure_decode(name, steps, warmup, variant=None, profile=False):
+def measure_decode(name, steps, warmup, variant=None, profile=False, settle_ms=0.0):
     import torch
     from synth import decode_workload
     case = decode_workload(name, device="cuda", variant=variant)
@@ -511,7 +535,7 @@ def measure_decode(name, steps, warmup, variant=None, profile=False):
     # last-level cache, so the timed loops alternate between two copies of the pool.
     copies = 2 if name == "window_decode" and case.head_dim_qk == 256 else 1
     step_ms, part_ms, merge_ms, wall_ms, plan, proto = time_decode(case, steps, warmup, copies,
-                                                                   profile)
+                                                                   profile, settle_ms)
     if profile:
         return {"case": case, "profiled_calls": warmup + steps, "pool_copies": copies}
     nbytes = decode_algorithmic_bytes(case)
@@ -533,11 +557,12 @@ def measure_decode(name, steps, warmup, variant=None, profile=False):
     return res
 
 
-def measure_prefill(name, steps, warmup, head_dim_vo, profile=False):
+def measure_prefill(name, steps, warmup, head_dim_vo, profile=False, settle_ms=0.0):
     from synth import prefill_workload
     case = prefill_workload(name, device="cuda", head_dim_vo=head_dim_vo)
     case.name = f"{name}_qk512_vo{head_dim_vo}"
-    step_ms, kern_ms, wall_ms, plan, proto = time_prefill(case, steps, warmup, profile)
+    step_ms, kern_ms, wall_ms, plan, proto = time_prefill(case, steps, warmup, profile,
+                                                          settle_ms)
     if profile:
         return {"case": case, "profiled_calls": warmup + steps}
     flops = prefill_algorithmic_flops(case)
@@ -554,12 +579,13 @@ def measure_prefill(name, steps, warmup, head_dim_vo, profile=False):
     }
 
 
-def measure_extend(name, steps, warmup, profile=False):
+def measure_extend(name, steps, warmup, profile=False, settle_ms=0.0):
     """Short-query extend: the whole call (prefill kernel over key chunks + merge) against
     the algorithmic HBM bytes."""
     from synth import prefill_workload
     case = prefill_workload(name, device="cuda", head_dim_vo=512)
-    step_ms, kern_ms, wall_ms, plan, proto = time_prefill(case, steps, warmup, profile)
+    step_ms, kern_ms, wall_ms, plan, proto = time_prefill(case, steps, warmup, profile,
+                                                          settle_ms)
     if profile:
         return {"case": case, "profiled_calls": warmup + steps, "kind": "extend"}
     nbytes = extend_algorithmic_bytes(case)
@@ -606,6 +632,8 @@ def main():
     ap.add_argument("--baseline-seconds", type=float, default=10.0,
                     help="oracle time for the headline's cpu_baseline (secondaries: a quarter)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="secondary lines: untimed steps for this long after the warmup steps")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -620,24 +648,24 @@ def main():
         copy_calibration()
         return
 
-    def run_named(wl, profile=False):
-        st, wu = args.steps, args.warmup
+    def run_named(wl, profile=False, settle_ms=0.0):
+        st, wu, sm = args.steps, args.warmup, settle_ms
         if wl.startswith("window_decode_d"):
             d, p = wl[len("window_decode_d"):].split("_p")
-            return measure_decode("window_decode", st, wu, (int(d), int(p)), profile)
+            return measure_decode("window_decode", st, wu, (int(d), int(p)), profile, sm)
         if wl.startswith("causal_prefill_vo"):
             return measure_prefill("causal_prefill", st, wu, int(wl[len("causal_prefill_vo"):]),
-                                   profile)
+                                   profile, sm)
         if wl.startswith("fp8_prefill_vo"):
             return measure_prefill("fp8_prefill", st, wu, int(wl[len("fp8_prefill_vo"):]),
-                                   profile)
+                                   profile, sm)
         if wl == "extend_prefill":
-            return measure_extend(wl, st, wu, profile)
+            return measure_extend(wl, st, wu, profile, sm)
         if wl == "nvfp4_prefill":
-            return measure_prefill(wl, st, wu, 256, profile)
+            return measure_prefill(wl, st, wu, 256, profile, sm)
         if wl.startswith("gqa_decode_splitk"):
-            return measure_decode("gqa_decode", st, wu, wl[len("gqa_decode_"):], profile)
-        return measure_decode(wl, st, wu, None, profile)
+            return measure_decode("gqa_decode", st, wu, wl[len("gqa_decode_"):], profile, sm)
+        return measure_decode(wl, st, wu, None, profile, sm)
 
     if args.profile:
         r = run_named(args.workload, profile=True)
@@ -692,7 +720,9 @@ def main():
             if wl == args.workload:
                 continue
             try:
-                r = run_named(wl)
+                # Each secondary follows the previous line's oracle baseline (host work, GPU
+                # idle), so its timed steps start once the clock has settled under load.
+                r = run_named(wl, settle_ms=args.settle_ms)
                 unit = "TFLOP/s" if "flops" in r else "GB/s"
                 sec[wl] = {"value": round(r["value"], 3), "unit": unit,
                            "ms_per_step": round(r["step_ms"], 5), "roofline": r["roofline"],
