@@ -221,8 +221,8 @@ def time_decode(case, steps, warmup, copies=1, profile=False, settle_ms=0.0):
     """Returns (ms_per_step, partial_kernel_ms, merge_ms, wall_ms, plan, protocol): the step
     time of back-to-back decode steps, then the two kernels' durations from events around
     each, then the 50-iteration protocol.  With copies = 2 every loop alternates between
-    two copies of the pool.  With profile, only warmup + steps decode steps run.  With
-    settle_ms, untimed steps run for that long after the warmup ones."""
+    two copies of the pool.  With settle_ms, untimed steps run for that long after the warmup
+    ones.  With profile, only the warmup steps, the settle steps and `steps` more run."""
     import torch
     import paged_attention_hd512_amd.pa as pa
 
@@ -242,10 +242,11 @@ def time_decode(case, steps, warmup, copies=1, profile=False, settle_ms=0.0):
     for _ in range(warmup):
         step_fn()
     if profile:
+        settled = settle(step_fn, settle_ms)
         for _ in range(steps):
             step_fn()
         torch.cuda.synchronize()
-        return None, None, None, None, runners[0][0].plan, None
+        return None, None, None, None, runners[0][0].plan, {"settle_calls": settled}
     settled = settle(step_fn, settle_ms)
     step, wall = time_steps(step_fn, stream, steps)
     # The merge alone, back to back (it is idempotent: it re-reads the partials); consecutive
@@ -298,8 +299,8 @@ def time_decode_graph(case, steps, warmup):
 def time_prefill(case, steps, warmup, profile=False, settle_ms=0.0):
     """Returns (ms_per_step, kernel_ms, wall_ms, plan, protocol): back-to-back prefill steps,
     then the duration of one step's launch(es) from events around it, then the 50-iteration
-    protocol.  With profile, only warmup + steps prefill steps run.  With settle_ms, untimed
-    steps run for that long after the warmup ones."""
+    protocol.  With settle_ms, untimed steps run for that long after the warmup ones.  With
+    profile, only the warmup steps, the settle steps and `steps` more run."""
     import torch
     from paged_attention_hd512_amd import PagedPrefill
     import paged_attention_hd512_amd.pa as pa
@@ -318,10 +319,11 @@ def time_prefill(case, steps, warmup, profile=False, settle_ms=0.0):
     for _ in range(warmup):
         pa.pa_paged_prefill(*args)
     if profile:
+        settled = settle(lambda: pa.pa_paged_prefill(*args), settle_ms)
         for _ in range(steps):
             pa.pa_paged_prefill(*args)
         torch.cuda.synchronize()
-        return None, None, None, run.plan, None
+        return None, None, None, run.plan, {"settle_calls": settled}
     settled = settle(lambda: pa.pa_paged_prefill(*args), settle_ms)
     step, wall = time_steps(lambda: pa.pa_paged_prefill(*args), stream, steps)
     # A prefill step is its kernel launch(es): back-to-back steps abut, so the step average
@@ -537,7 +539,8 @@ def measure_decode(name, steps, warmup, variant=None, profile=False, settle_ms=0
     step_ms, part_ms, merge_ms, wall_ms, plan, proto = time_decode(case, steps, warmup, copies,
                                                                    profile, settle_ms)
     if profile:
-        return {"case": case, "profiled_calls": warmup + steps, "pool_copies": copies}
+        return {"case": case, "profiled_calls": warmup + proto["settle_calls"] + steps,
+                "settle_calls": proto["settle_calls"], "pool_copies": copies}
     nbytes = decode_algorithmic_bytes(case)
     achieved = nbytes / (part_ms * 1e-3) / 1e9
     res = {
@@ -564,7 +567,8 @@ def measure_prefill(name, steps, warmup, head_dim_vo, profile=False, settle_ms=0
     step_ms, kern_ms, wall_ms, plan, proto = time_prefill(case, steps, warmup, profile,
                                                           settle_ms)
     if profile:
-        return {"case": case, "profiled_calls": warmup + steps}
+        return {"case": case, "profiled_calls": warmup + proto["settle_calls"] + steps,
+                "settle_calls": proto["settle_calls"]}
     flops = prefill_algorithmic_flops(case)
     achieved = flops / (kern_ms * 1e-3) / 1e12
     return {
@@ -587,7 +591,8 @@ def measure_extend(name, steps, warmup, profile=False, settle_ms=0.0):
     step_ms, kern_ms, wall_ms, plan, proto = time_prefill(case, steps, warmup, profile,
                                                           settle_ms)
     if profile:
-        return {"case": case, "profiled_calls": warmup + steps, "kind": "extend"}
+        return {"case": case, "profiled_calls": warmup + proto["settle_calls"] + steps,
+                "settle_calls": proto["settle_calls"], "kind": "extend"}
     nbytes = extend_algorithmic_bytes(case)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     return {
@@ -628,7 +633,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
-                    help="run only warmup + steps launches of the workload (for rocprofv3)")
+                    help="run only the warmup launches, the --settle-ms launches and then "
+                         "`steps` launches of the workload (for rocprofv3)")
     ap.add_argument("--baseline-seconds", type=float, default=10.0,
                     help="oracle time for the headline's cpu_baseline (secondaries: a quarter)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -668,9 +674,12 @@ def main():
         return measure_decode(wl, st, wu, None, profile, sm)
 
     if args.profile:
-        r = run_named(args.workload, profile=True)
+        # Untimed calls for --settle-ms come before the last `steps` calls, so those run at
+        # the settled clock, as a secondary line's timed steps do.
+        r = run_named(args.workload, profile=True, settle_ms=args.settle_ms)
         print(json.dumps({"profile": args.workload, "workload": r["case"].name,
                           "calls": r["profiled_calls"], "warmup": args.warmup,
+                          "settle_ms": args.settle_ms, "settle_calls": r["settle_calls"],
                           "steps": args.steps,
                           "kernel_source_hash": {f: kernel_source_hash(f)
                                                  for f in KERNEL_SOURCES}}), flush=True)
