@@ -256,8 +256,11 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
  * / 512)), is cut into ceil(stages / C) near-equal runs of whole stages; each such chunk
  * writes a partial (normalised output and log-sum-exps) to its own workspace slot and a
  * merge combines them (plan->num_merges split tiles, plan->num_slots slots,
- * plan->chunk_blocks = C, 0 without splitting).  Items run by key count, longest first.
- * The result does not depend on the split.  Same two-call sizing as pa_decode_plan.
+ * plan->chunk_blocks = C, 0 without splitting).  Items run by key count, longest first;
+ * without split-K, when the K and V bytes of the requests' key ranges (all KV heads) exceed
+ * 256 MiB, the GPU's memory-side last-level cache, they run request by request instead
+ * (requests in the order of their longest tile, longest first within each request).
+ * The result does not depend on the split or the order.  Same two-call sizing as pa_decode_plan.
  * Supported: head dims (512,512), (256,256), (512,256); kv bf16, FP8 E4M3FN or NVFP4; q bf16;
  * out fp32 or bf16; num_qo_heads / num_kv_heads <= 16.  Never calls HIP. */
 pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache,
