@@ -92,3 +92,10 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_settle_runs_nothing_when_its_time_is_zero():
+    """The headline line (and --settle-ms 0) must run exactly the requested warmup steps."""
+    calls = []
+    assert bench.settle(lambda: calls.append(1), 0.0) == 0
+    assert calls == []
