@@ -215,6 +215,28 @@ def test_full_size_causal_prefill_on_256_rows_per_request(name, dvo):
 
 
 @pytest.mark.slow
+def test_ragged_prefill_whose_keys_exceed_the_last_level_cache():
+    """Three requests of different lengths (600, 1500 and 2500 new tokens over 9000, 6000 and
+    2500 keys; 16/8 heads, 512/512 bf16, page 64): 273 MiB of K and V, above the 256 MiB
+    last-level cache, so the tiles run request by request (the plan is checked), and 96
+    tokens of every request (all heads) match the oracle."""
+    say("ragged prefill above the last-level cache")
+    c = make_prefill_case([600, 1500, 2500], [9000, 6000, 2500], 16, 8, 512, 64,
+                          head_dim_vo=512, causal=True, out_dtype="bf16", seed=77, device=dev())
+    runner, o, lse = gpu_prefill(c)
+    assert runner.plan.num_merges == 0
+    reqs = pa.prefill_items(runner.plan, runner.plan_buf)[:, 0].tolist()
+    runs = [b for i, b in enumerate(reqs) if i == 0 or reqs[i - 1] != b]
+    assert sorted(runs) == [0, 1, 2], runs  # each request's tiles are contiguous
+    toks = full_size_rows(c, 96, 77)
+    ref, ref_lse = oracle_prefill(c, tokens=toks)
+    idx = torch.as_tensor(toks).to(o.device)
+    compare(f"ragged prefill {len(toks)} rows", out_to_np(o.index_select(0, idx)), ref,
+            lse.index_select(0, idx).cpu().numpy(), ref_lse, out_dtype=c.out_dtype)
+    assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.slow
 def test_full_size_extend_prefill_is_split_and_matches():
     """The short-query extend workload (8 requests x 16 new tokens over 16368 cached keys,
     16/8 heads, page 64) in its launch configuration: the plan cuts every tile into key
