@@ -170,6 +170,9 @@ typedef struct pa_plan {
                                       kv head) are combined in LDS into one slot (the
                                       planner sets it where the kernel can hold a split
                                       result per wave in LDS); changes rounding order only */
+  int32_t staged_pages;            /* prefill, NVFP4 KV: page-table entries whose K and V
+                                      pages the run first widens to bf16 in the workspace
+                                      (0: none); the result is the same                  */
   int64_t plan_bytes;              /* bytes of the host plan buffer in use              */
   int64_t items_offset;            /* byte offset of the item array in the plan buffer  */
   int64_t merges_offset;           /* byte offset of the merge array in the plan buffer */
@@ -178,6 +181,9 @@ typedef struct pa_plan {
   int64_t partial_o_offset;        /* byte offset of partial outputs in the workspace   */
   int64_t partial_lse_offset;      /* byte offset of partial lse in the workspace       */
   int64_t workspace_bytes;         /* device workspace the run call needs               */
+  int64_t staged_offset;           /* prefill: byte offset of the widened pages in the
+                                      workspace (bf16 K, then bf16 V, [entry][kv head]
+                                      [slot][head_dim], then one int32 per entry)        */
 } pa_plan;
 
 /* Fills *out for the combined HND cache [num_pages, 2, num_kv_heads, page_size, head_dim]
@@ -260,7 +266,12 @@ pa_status pa_decode_plan(const pa_attn_params* params, const pa_kv_cache* cache,
  * without split-K, when the K and V bytes of the requests' key ranges (all KV heads) exceed
  * 256 MiB, the GPU's memory-side last-level cache, they run request by request instead
  * (requests in the order of their longest tile, longest first within each request).
- * The result does not depend on the split or the order.  Same two-call sizing as pa_decode_plan.
+ * NVFP4 without split-K, when the tiles read each key of the table at least four times
+ * on average: the run first widens every K and V page the table lists into bf16 pages
+ * in the workspace (exact: each E2M1 value times its E4M3 block scale) and runs the bf16
+ * kernel over them (plan->staged_pages, plan->staged_offset; the workspace grows by
+ * 2 (head_dim_qk + head_dim_vo) bytes per (entry, kv head, slot)).
+ * The result does not depend on the split, the order or the widening.  Same two-call sizing as pa_decode_plan.
  * Supported: head dims (512,512), (256,256), (512,256); kv bf16, FP8 E4M3FN or NVFP4; q bf16;
  * out fp32 or bf16; num_qo_heads / num_kv_heads <= 16.  Never calls HIP. */
 pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache,

@@ -658,13 +658,23 @@ pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache
   std::stable_sort(items.begin(), items.end(), [](const Tmp& a, const Tmp& b) {
     return (a.it.kv_end - a.it.kv_begin) > (b.it.kv_end - b.it.kv_begin);
   });
+  // NVFP4 without split-K: when the tiles read every key several times, widening each page
+  // once per call (to bf16, in the workspace) costs less than widening each key in every
+  // tile that reads it; the bf16 kernel then runs over the widened pages.
+  int64_t staged_pages = 0;
+  if (cache->kv_dtype == PA_DTYPE_NVFP4 && chunk == 0 && !items.empty() && batch > 0) {
+    int64_t reads = 0;
+    for (const Tmp& t : items) reads += t.it.kv_end - t.it.kv_begin;
+    const int64_t entries = kv_indptr_host[batch];
+    if (entries > 0 && reads >= kStageMinReads * entries * cache->page_size) staged_pages = entries;
+  }
   // Without split-K, when the K and V bytes the tiles read do not fit the last-level cache,
   // the tiles run request by request (requests in the order of their longest tile, key
   // count descending within each): the tiles running together then read one request's keys,
   // which stay in that cache for the tiles that start later.
   if (chunk == 0 && !items.empty()) {
     const int64_t dk = cache->head_dim_qk + cache->head_dim_vo;
-    const int64_t per_key = cache->kv_dtype == PA_DTYPE_BF16 ? 2 * dk
+    const int64_t per_key = cache->kv_dtype == PA_DTYPE_BF16 || staged_pages > 0 ? 2 * dk
                             : cache->kv_dtype == PA_DTYPE_NVFP4 ? dk / 2 + dk / 16
                                                                 : dk;  // FP8
     std::vector<int64_t> lo(batch, INT64_MAX), hi(batch, INT64_MIN);
@@ -712,6 +722,14 @@ pa_status pa_prefill_plan(const pa_attn_params* params, const pa_kv_cache* cache
   const int64_t part_rows = num_slots * hkv * kPrefillTileRows;
   plan->partial_lse_offset = align_up(plan->partial_o_offset + part_rows * cache->head_dim_vo * 4, 256);
   plan->workspace_bytes = align_up(plan->partial_lse_offset + part_rows * 2 * 4, 256);
+  plan->staged_pages = (int32_t)staged_pages;
+  plan->staged_offset = 0;
+  if (staged_pages > 0) {
+    plan->staged_offset = plan->workspace_bytes;
+    const int64_t rows = staged_pages * hkv * cache->page_size;
+    plan->workspace_bytes = align_up(
+        plan->staged_offset + rows * (cache->head_dim_qk + cache->head_dim_vo) * 2 + staged_pages * 4, 256);
+  }
   if (!plan_buf_host) return PA_OK;
   if ((int64_t)plan_buf_bytes < plan->plan_bytes)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "plan buffer has %zu bytes, plan needs %lld",

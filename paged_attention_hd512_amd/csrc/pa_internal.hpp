@@ -39,6 +39,9 @@ constexpr bool decode_parks(int dqk, int dvo, int gmax, bool fp4) {
 constexpr int decode_gmax(int group) { return group <= 4 ? group : group <= 6 ? 6 : 8; }
 constexpr int kMaxPrefillGroup = 16;
 constexpr int64_t kLastLevelCacheBytes = int64_t(256) << 20;  // MI355X memory-side cache
+// NVFP4 prefill widens the table's pages to bf16 once per call when the tiles read each
+// key at least this many times on average.
+constexpr int64_t kStageMinReads = 4;
 
 // Prefill: query rows per tile ((token, head) pairs of one head group), 16 per wave.
 constexpr int kPrefillTileRows = 128;

@@ -968,7 +968,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   const float l_bf_tot = sum_xor32(sum_xor16(l_bf));
   if (!row_valid) return;
   float inv = l_bf_tot > 0.f ? 1.f / l_bf_tot : 0.f;
-  if constexpr (KV != kKvBf16) inv *= a.v_scale;
+  inv *= a.v_scale;  // 1 for a bf16 cache
   if (it.slot >= 0) {
     // One key chunk of a split tile: its normalised output and two log-sum-exps, over the
     // bf16-rounded weights (the merge weights, so the merged output is normalised by the
@@ -996,6 +996,61 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(PrefillArgs a) {
   }
   if (a.lse && g4 == 0)
     a.lse[q_row] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+// Widening of NVFP4 pages for prefill (the NVFP4 page's block format: E2M1 pairs, one E4M3
+// scale per 16 elements): page-table entry j's K and V rows become bf16 rows of staged page
+// j (each value times its block scale, exact in bf16), and entry j of `ident` becomes j, so
+// the bf16 kernel reads staged page j where the table lists page kv_indices[j].
+struct StageArgs {
+  const char* k;
+  const char* v;
+  const char* k_sf;
+  const char* v_sf;
+  int64_t k_sp, k_sh, k_st, v_sp, v_sh, v_st;        // data strides, bytes
+  int64_t ks_sp, ks_sh, ks_st, vs_sp, vs_sh, vs_st;  // block-scale strides, bytes
+  const int32_t* kv_indices;
+  uint16_t* k_out;  // [entry][kv head][slot][head_dim_qk] bf16
+  uint16_t* v_out;  // [entry][kv head][slot][head_dim_vo] bf16
+  int32_t* ident;
+  int32_t num_kv_heads, page_size, dqk, dvo;
+};
+
+// One page of one head: `rows` rows of D elements; each thread widens 8 elements (one
+// 4-byte word of codes) at a time.
+__device__ __forceinline__ void stage_rows(const char* src, int64_t st, const char* sf,
+                                           int64_t sst, uint16_t* dst, int D, int rows) {
+  const int words = D / 8;
+  for (int i = threadIdx.x; i < rows * words; i += blockDim.x) {
+    const int r = i / words, w = i - r * words;
+    const uint32_t codes = *(const uint32_t*)(src + r * st + 4 * w);
+    const uint32_t sbyte = *(const uint8_t*)(sf + r * sst + (w >> 1));
+    float scale[4];
+    fp8x4_to_f32(sbyte, scale);
+    float f[8];
+    fp4x8_to_f32(codes, f);
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // products of a 2-bit and a 4-bit significand: exact in bf16, so truncation is exact
+      const uint32_t lo = __float_as_uint(f[2 * e] * scale[0]) >> 16;
+      const uint32_t hi = __float_as_uint(f[2 * e + 1] * scale[0]) >> 16;
+      o[e] = lo | (hi << 16);
+    }
+    *(u32x4_t*)(dst + (int64_t)r * D + 8 * w) = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void nvfp4_stage_kernel(StageArgs a) {
+  const int64_t j = blockIdx.x;
+  const int h = blockIdx.y;
+  const int64_t page = a.kv_indices[j];
+  if (h == 0 && threadIdx.x == 0) a.ident[j] = (int32_t)j;
+  const int64_t slab = (j * a.num_kv_heads + h) * a.page_size;
+  stage_rows(a.k + page * a.k_sp + h * a.k_sh, a.k_st, a.k_sf + page * a.ks_sp + h * a.ks_sh,
+             a.ks_st, a.k_out + slab * a.dqk, a.dqk, a.page_size);
+  stage_rows(a.v + page * a.v_sp + h * a.v_sh, a.v_st, a.v_sf + page * a.vs_sp + h * a.vs_sh,
+             a.vs_st, a.v_out + slab * a.dvo, a.dvo, a.page_size);
 }
 
 struct PrefillMergeArgs {
@@ -1131,9 +1186,9 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
                                       void* workspace, size_t workspace_bytes, void* stream) {
   pa_status st = check_cache(cache, true);
   if (st != PA_OK) return st;
-  const int kv = cache->kv_dtype == PA_DTYPE_NVFP4        ? kKvFp4
-                 : cache->kv_dtype == PA_DTYPE_FP8_E4M3FN ? kKvFp8
-                                                          : kKvBf16;
+  int kv = cache->kv_dtype == PA_DTYPE_NVFP4        ? kKvFp4
+           : cache->kv_dtype == PA_DTYPE_FP8_E4M3FN ? kKvFp8
+                                                    : kKvBf16;
   if ((st = check_params(params, cache, kMaxPrefillGroup)) != PA_OK) return st;
   if ((st = check_plan_matches(plan, 2, params, cache, table, workspace_bytes)) != PA_OK) return st;
   if (plan->num_items == 0) return PA_OK;
@@ -1180,6 +1235,37 @@ extern "C" pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const 
   hipStream_t s = (hipStream_t)stream;
   const int dqk = cache->head_dim_qk, dvo = cache->head_dim_vo;
   const int P = cache->page_size;
+  if (plan->staged_pages > 0) {
+    // Widen the table's NVFP4 pages into bf16 pages in the workspace, then run the bf16
+    // kernel over them through an identity page list (k_scale is in scale_log2 and
+    // v_scale in a.v_scale as before).
+    const int64_t n = plan->staged_pages, H = cache->num_kv_heads;
+    if (kv != kKvFp4 || plan->staged_offset < plan->partial_lse_offset ||
+        plan->staged_offset + n * H * P * (dqk + dvo) * 2 + n * 4 > plan->workspace_bytes)
+      return fail(PA_ERR_INVALID_ARG, "plan's widened-page region does not fit this cache");
+    StageArgs g;
+    g.k = a.k; g.v = a.v; g.k_sf = a.k_sf; g.v_sf = a.v_sf;
+    g.k_sp = a.k_sp; g.k_sh = a.k_sh; g.k_st = a.k_st;
+    g.v_sp = a.v_sp; g.v_sh = a.v_sh; g.v_st = a.v_st;
+    g.ks_sp = a.ks_sp; g.ks_sh = a.ks_sh; g.ks_st = a.ks_st;
+    g.vs_sp = a.vs_sp; g.vs_sh = a.vs_sh; g.vs_st = a.vs_st;
+    g.kv_indices = a.kv_indices;
+    g.k_out = (uint16_t*)(ws + plan->staged_offset);
+    g.v_out = g.k_out + n * H * P * dqk;
+    g.ident = (int32_t*)(g.v_out + n * H * P * dvo);
+    g.num_kv_heads = (int32_t)H; g.page_size = P; g.dqk = dqk; g.dvo = dvo;
+    nvfp4_stage_kernel<<<dim3((unsigned)n, (unsigned)H), 256, 0, s>>>(g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "nvfp4 widening launch: %s", hipGetErrorString(e));
+    count_launches(1);
+    kv = kKvBf16;
+    a.k = (const char*)g.k_out;
+    a.v = (const char*)g.v_out;
+    a.k_sp = 2 * H * P * dqk; a.k_sh = 2 * (int64_t)P * dqk; a.k_st = 2 * dqk;
+    a.v_sp = 2 * H * P * dvo; a.v_sh = 2 * (int64_t)P * dvo; a.v_st = 2 * dvo;
+    a.k_sf = a.v_sf = nullptr;
+    a.kv_indices = g.ident;
+  }
   // The one-lookup-per-stage path forms byte offsets inside a page, and page strides, in
   // 32 bits.
   const bool page_fits_u32 = (int64_t)P * a.k_st + 2 * dqk < (int64_t(1) << 32) &&

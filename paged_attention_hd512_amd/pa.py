@@ -69,11 +69,12 @@ class pa_plan(Structure):
                 ("num_splits", c_int32), ("tile_rows", c_int32), ("total_q", c_int32),
                 ("max_kv_len", c_int32), ("num_workers", c_int32),
                 ("deferred_partials", c_int32), ("short_tiles", c_int32),
-                ("grouped_partials", c_int32), ("plan_bytes", c_int64),
+                ("grouped_partials", c_int32), ("staged_pages", c_int32),
+                ("plan_bytes", c_int64),
                 ("items_offset", c_int64), ("merges_offset", c_int64),
                 ("workers_offset", c_int64),
                 ("partial_o_offset", c_int64), ("partial_lse_offset", c_int64),
-                ("workspace_bytes", c_int64)]
+                ("workspace_bytes", c_int64), ("staged_offset", c_int64)]
 
 
 # Every symbol include/pa.h declares, with (restype, argtypes).

@@ -240,3 +240,38 @@ def test_nvfp4_decode_replays_from_a_graph():
         out_e, lse_e = run.run(q)
         torch.cuda.synchronize()
         assert torch.equal(out_g, out_e) and torch.equal(lse_g, lse_e), f"replay {i}"
+
+
+WIDENED_PREFILL = [
+    # qo_lens, kv_lens, hq, hkv, dqk, dvo, page, window, out, padded pools
+    ([2048, 2048], [2600, 2200], 16, 8, 512, 512, 16, 0, "bf16", False),
+    ([2048, 2048], [2600, 2200], 16, 8, 512, 512, 16, 0, "fp32", True),
+    ([2048, 2048], [2100, 3000], 16, 8, 512, 256, 1, 700, "fp32", False),
+    ([8192], [8300], 8, 8, 256, 256, 64, 0, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("qo,kv,hq,hkv,dqk,dvo,page,window,out,padded", WIDENED_PREFILL)
+def test_nvfp4_prefill_over_widened_pages(qo, kv, hq, hkv, dqk, dvo, page, window, out, padded):
+    """Causal prefills whose tiles read every key several times: the run widens the table's
+    NVFP4 pages to bf16 once and runs the bf16 kernel over them (the plan says so); 64
+    tokens of every request (all heads) match the oracle on the stored codes, also with K,
+    V and their scales in separately padded allocations."""
+    from test_gpu_prefill import full_size_rows
+    name = f"nvfp4 widened prefill kv={kv} dims={dqk}/{dvo} page={page} window={window} {out}"
+    say(name)
+    c = make_prefill_case(qo, kv, hq, hkv, dqk, page, head_dim_vo=dvo, causal=True,
+                          window=window, out_dtype=out, kv_dtype="nvfp4", seed=sum(kv) + page,
+                          device=dev())
+    if padded:
+        c.k_pool, c.v_pool = repad(c.k_pool, 16), repad(c.v_pool, 48)
+        c.k_sf, c.v_sf = repad(c.k_sf, 16), repad(c.v_sf, 32)
+        c.cache = c.sf_cache = None
+    runner, o, lse = gpu_prefill(c)
+    assert runner.plan.staged_pages == int(c.kv_indptr[-1]) and runner.plan.num_merges == 0
+    toks = full_size_rows(c, 64, 5)
+    ref, ref_lse = oracle_prefill(c, tokens=toks)
+    idx = torch.as_tensor(toks).to(o.device)
+    compare(name, out_to_np(o.index_select(0, idx)), ref, lse.index_select(0, idx).cpu().numpy(),
+            ref_lse, out_dtype=out)
+    assert torch.isfinite(o.float()).all()
