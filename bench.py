@@ -577,7 +577,9 @@ def measure_prefill(name, steps, warmup, head_dim_vo, profile=False, settle_ms=0
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": traffic_for(case.name), "kernel": "prefill_kernel",
+                     "traffic": traffic_for(case.name),
+                     "kernel": ("nvfp4_stage_kernel + prefill_kernel" if plan.staged_pages > 0
+                                else "prefill_kernel"),
                      "algorithmic_flops_per_launch": flops, "kernel_avg_ms": round(kern_ms, 5)},
         "protocol": proto,
     }
