@@ -338,7 +338,10 @@ pa_status pa_paged_decode_merge(const pa_plan* plan, const void* q, const pa_kv_
  * num_qo_heads, head_dim_vo] in params->out_dtype and optional lse [total_q, num_qo_heads]
  * fp32 (NULL: not written).  qo_indptr is the device copy of the array
  * given to pa_prefill_plan.  One kernel launch, or two when the plan splits tiles (the
- * chunk partials go to the workspace, then a merge kernel writes their rows). */
+ * chunk partials go to the workspace, then a merge kernel writes their rows), or, when
+ * the plan widens NVFP4 pages (plan->staged_pages > 0), the widening kernel first and
+ * then the bf16 prefill kernel over the widened pages.  NVFP4 at 512/512 without widening
+ * runs the 512/256 form twice, once per half of head_dim_vo. */
 pa_status pa_paged_prefill(const pa_plan* plan, const void* q, const int32_t* qo_indptr,
                            const pa_kv_cache* cache, const pa_page_table* table,
                            const pa_attn_params* params, void* out, float* lse,
