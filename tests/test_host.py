@@ -511,3 +511,39 @@ def test_run_calls_refuse_a_plan_made_for_other_sizes():
     with pytest.raises(pa.PaError) as e:
         pa.pa_paged_decode(plan, 0x4001, c, table, p, 0x5000, None, 0x6000, 1 << 20)
     assert e.value.status == pa.PA_ERR_UNSUPPORTED  # misaligned q
+
+
+def test_nvfp4_prefill_widens_pages_only_when_tiles_re_read_keys():
+    """NVFP4 prefill plans reserve bf16 pages for every page-table entry (2 (D_qk + D_vo)
+    bytes per entry, KV head and slot, plus one int32 per entry) exactly when the plan does
+    not split keys and its tiles read each key at least four times on average; bf16 and
+    FP8 plans never do."""
+    def plan_for(qo, kv, dtype, hq=16, hkv=8, P=16, dvo=512):
+        indptr, last = lens_to_table(kv, P)
+        qo_indptr = np.zeros(len(qo) + 1, np.int32)
+        qo_indptr[1:] = np.cumsum(qo)
+        pages = int(indptr[-1]) + 1
+        if dtype == pa.PA_DTYPE_NVFP4:
+            cache = pa.pa_kv_cache_nvfp4_hnd(0x10000, 0x20000, pages, hkv, P, 512)
+        else:
+            cache = pa.pa_kv_cache_hnd(0x10000, dtype, pages, hkv, P, 512)
+        plan, _ = pa.pa_prefill_plan(params(hq=hq), cache, qo_indptr, indptr, last)
+        return plan, int(indptr[-1])
+
+    # 2 x 2048 new tokens (16/8 heads: 64 tiles of 128 rows per KV head), no split-K, each
+    # key read by many tiles: widened.
+    plan, entries = plan_for([2048, 2048], [2600, 2200], pa.PA_DTYPE_NVFP4)
+    assert plan.num_merges == 0 and plan.staged_pages == entries
+    assert plan.staged_offset >= plan.partial_lse_offset and plan.staged_offset % 256 == 0
+    need = entries * 8 * 16 * (512 + 512) * 2 + entries * 4
+    assert plan.staged_offset + need <= plan.workspace_bytes < plan.staged_offset + need + 256
+    # The same shapes over bf16 and FP8 caches: never.
+    for dt in (pa.PA_DTYPE_BF16, pa.PA_DTYPE_FP8_E4M3FN):
+        assert plan_for([2048, 2048], [2600, 2200], dt)[0].staged_pages == 0
+    # A few new tokens over long KV: the plan splits keys, so no widening.
+    plan, _ = plan_for([16] * 4, [6000] * 4, pa.PA_DTYPE_NVFP4)
+    assert plan.num_merges > 0 and plan.staged_pages == 0 and plan.staged_offset == 0
+    # No split, but each key read by fewer than four tiles on average (one 128-row tile per
+    # 16 tokens at group 8, keys mostly behind a long prefix read by one tile each).
+    plan, _ = plan_for([16] * 512, [4000] * 512, pa.PA_DTYPE_NVFP4, hq=64, hkv=8)
+    assert plan.num_merges == 0 and plan.staged_pages == 0
